@@ -1,0 +1,219 @@
+"""Float64 CPU oracle for the chunked GRPO policy loss.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and the
+benchmark's CPU-baseline leg may import or call this module.  The product path
+(the HIP library and its Python binding) never does, and this module imports
+nothing from it.
+
+It is the plain definition of what the fused GPU path computes, written out in
+float64 NumPy with the full logits materialised one block of rows at a time:
+no online log-sum-exp, no vocabulary splits, no stored-dZ slabs, no fusion.
+
+Sources (pages as extracted):
+  [P-blog]  Unsloth "Long-context GRPO" blog, Chinese translation at
+            zjt100.com; sections "Unsloth efficient GRPO algorithm" and
+            "GRPO maths and the problems found".
+  [P-docs]  Unsloth docs "GRPO with 7x longer context" (French edition);
+            sections "Flattened sequence length chunking", "Hidden states
+            chunking" and "Offloading activations for log softmax".
+  [P-aibit] aibit.im "Mastering GRPO" (French); section "From RLHF and PPO to
+            the efficiency of GRPO".
+
+The loss and KL formula images were lost from the pages; what they state in
+prose fixes the pieces used here:
+  * the policy term multiplies exp(lp - stopgrad(lp)), whose value is 1 and
+    whose gradient is that of lp, by the per-sequence advantage broadcast
+    over the sequence's tokens [P-blog, GRPO maths];
+  * the KL is the reverse KL between the trained policy Q and the frozen
+    reference P, estimated without an extra factor of Q, scaled by beta = 0.04
+    [P-blog, GRPO maths].  The estimator with that property named there
+    (Schulman's) is k3: exp(x) - x - 1 with x = ref_lp - lp;
+  * log-probabilities come from float32-or-better logits with the max-shifted
+    log-sum-exp [P-docs, flattened chunking, note 2; P-blog, GRPO maths];
+  * the advantage is derived per prompt group from the group's rewards
+    [P-aibit, From RLHF and PPO]; here (r - mean) / (std + eps), sample std.
+Readings where the pages are silent (aggregation, std estimator, masked-token
+outputs, empty mask) are listed in the module-level notes of each function.
+
+Parity unpinned: nothing.  Every function is pinned by the CPU tests against
+closed forms, invariants, library routines (scipy log_softmax, numpy std,
+torch float64 autograd of the literal policy-term expression) and central
+finite differences of the stop-gradient surrogate.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+ROW_BLOCK = 256
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# advantages
+# ---------------------------------------------------------------------------
+def group_advantages(rewards, group_size, eps=1e-4):
+    """A_b = (r_b - mean_g) / (std_g + eps) within each group of `group_size`.
+
+    [P-aibit, From RLHF and PPO]: GRPO samples several answers per prompt,
+    scores each, and turns the scores into an advantage statistically, in
+    place of a value model.  Groups are consecutive runs of `group_size`
+    rewards.  std is the sample standard deviation (divide by n - 1); a group
+    of one has std := 0, so its advantage is 0.  NaN rewards propagate.
+    """
+    r = _f64(rewards).reshape(-1, group_size)
+    n = r.shape[1]
+    mean = r.sum(axis=1, keepdims=True) / n
+    dev = r - mean
+    if n > 1:
+        std = np.sqrt((dev * dev).sum(axis=1, keepdims=True) / (n - 1))
+    else:
+        std = np.zeros_like(mean)
+    return (dev / (std + eps)).reshape(-1)
+
+
+# ---------------------------------------------------------------------------
+# log-probabilities
+# ---------------------------------------------------------------------------
+def logits(H_rows, W):
+    """z = H W^T for a block of rows: [b, d] x [V, d] -> [b, V], float64.
+
+    [P-docs, Offloading activations]: the logits of a batch slice are the
+    hidden states times the LM head.
+    """
+    return _f64(H_rows) @ _f64(W).T
+
+
+def lse_and_target(Z, y_rows):
+    """Max-shifted log-sum-exp of each row of Z and the target log-prob.
+
+    [P-blog, GRPO maths]: the logsumexp trick; lse = M + log sum exp(z - M)
+    with M the row max.  lp = z[y] - lse.
+    """
+    M = Z.max(axis=1)
+    lse = M + np.log(np.exp(Z - M[:, None]).sum(axis=1))
+    lp = Z[np.arange(Z.shape[0]), np.asarray(y_rows, dtype=np.int64)] - lse
+    return lp, lse
+
+
+def token_logprobs(H, W, y, rows=None, block=ROW_BLOCK):
+    """(lp, lse) for every token (or for the listed `rows`), float64.
+
+    [P-docs, Flattened sequence length chunking]: the selective log-softmax
+    of the hidden states through the LM head, gathered at the completion ids.
+    The logits of `block` rows are formed in full, then reduced.
+    """
+    H = np.asarray(H)
+    y = np.asarray(y)
+    idx = np.arange(H.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    lp = np.empty(len(idx))
+    lse = np.empty(len(idx))
+    for b0 in range(0, len(idx), block):
+        sel = idx[b0:b0 + block]
+        lp[b0:b0 + block], lse[b0:b0 + block] = lse_and_target(logits(H[sel], W), y[sel])
+    return lp, lse
+
+
+# ---------------------------------------------------------------------------
+# per-token KL and loss
+# ---------------------------------------------------------------------------
+def reverse_kl_k3(ref_lp, lp):
+    """kl = exp(x) - x - 1 with x = ref_lp - lp (unscaled, every token).
+
+    [P-blog, GRPO maths]: reverse KL with Q the trained policy and P the
+    reference, estimated without an extra factor of Q.
+    """
+    x = _f64(ref_lp) - _f64(lp)
+    return np.exp(x) - x - 1.0
+
+
+def token_advantages(adv, seq_len):
+    """A per flattened token: sequence b's advantage on its seq_len tokens.
+
+    [P-blog, GRPO maths]: the advantages are unsqueezed along the sequence
+    axis, so one value covers all tokens of a completion.
+    """
+    return np.repeat(_f64(adv), seq_len)
+
+
+def loss_forward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04):
+    """Masked token-mean GRPO loss plus the per-token outputs.
+
+    l_t = -(R_t * A_t - beta * kl_t), with R_t = exp(lp_t - stopgrad(lp_t)),
+    whose value is exactly 1 [P-blog, GRPO maths].
+    loss = sum_t m_t l_t / max(sum_t m_t, 1): one mean over all unmasked
+    flattened tokens (an empty mask gives 0).
+    lp, kl and lse are reported for every token, masked or not.
+    """
+    lp, lse = token_logprobs(H, W, y)
+    kl = reverse_kl_k3(ref_lp, lp)
+    A_t = token_advantages(adv, seq_len)
+    R = 1.0
+    ell = -(R * A_t - beta * kl)
+    m = _f64(mask)
+    loss = (m * ell).sum() / max(m.sum(), 1.0)
+    return dict(loss=float(loss), lp=lp, kl=kl, lse=lse, ell=ell)
+
+
+def loss_coefficients(mask, adv, ref_lp, lp, seq_len, beta=0.04, grad_loss=1.0):
+    """c_t = d loss / d lp_t.
+
+    From l_t = -(R_t A_t - beta kl_t): dR/dlp = R = 1 and
+    dkl/dlp = 1 - exp(x), so dl_t/dlp_t = -A_t + beta (1 - exp(x_t)).
+    The mean contributes m_t / max(sum m, 1); grad_loss is the upstream scalar.
+    """
+    m = _f64(mask)
+    A_t = token_advantages(adv, seq_len)
+    x = _f64(ref_lp) - _f64(lp)
+    return grad_loss * m / max(m.sum(), 1.0) * (-A_t + beta * (1.0 - np.exp(x)))
+
+
+def loss_backward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04, grad_loss=1.0,
+                  dh_rows=None, want_dW=True, block=ROW_BLOCK):
+    """Gradients of the loss w.r.t. H and W, float64.
+
+    [P-docs, Offloading activations]: the backward recomputes the logits of
+    each slice instead of keeping them from the forward.  Per token:
+      p_t = softmax(z_t);  dZ_t = c_t (onehot(y_t) - p_t)
+      dH_t = dZ_t W;       dW = sum_t dZ_t^T h_t
+    Returns (dH, dW).  dH has one row per entry of `dh_rows` (all tokens if
+    None).  dW is the value the GPU adds to its accumulator (None when
+    want_dW is False).  Only unmasked tokens contribute to dW (c_t = 0
+    elsewhere), so only they and the requested dH rows are visited.
+    """
+    H = np.asarray(H)
+    y = np.asarray(y)
+    N = H.shape[0]
+    Wf = _f64(W)
+    mask = np.asarray(mask)
+    lp_all = np.zeros(N)
+    active = np.nonzero(mask)[0]
+    rows = np.arange(N) if dh_rows is None else np.asarray(dh_rows, dtype=np.int64)
+    need = np.union1d(active, rows) if want_dW else np.unique(rows)
+    # per-token coefficient needs lp of the token: recompute from full logits
+    lp_need, _ = token_logprobs(H, W, y, rows=need, block=block)
+    lp_all[need] = lp_need
+    c = loss_coefficients(mask, adv, ref_lp, lp_all, seq_len, beta, grad_loss)
+    dW = np.zeros_like(Wf)
+    dH = np.zeros((len(rows), Wf.shape[1]))
+    pos = {int(t): i for i, t in enumerate(rows)}
+    for b0 in range(0, len(need), block):
+        sel = need[b0:b0 + block]
+        Hs = _f64(H[sel])
+        Z = Hs @ Wf.T
+        M = Z.max(axis=1, keepdims=True)
+        P = np.exp(Z - M)
+        P /= P.sum(axis=1, keepdims=True)
+        dZ = -P
+        dZ[np.arange(len(sel)), y[sel].astype(np.int64)] += 1.0
+        dZ *= c[sel][:, None]
+        if want_dW:
+            dW += dZ.T @ Hs
+        g = dZ @ Wf
+        for i, t in enumerate(sel):
+            j = pos.get(int(t))
+            if j is not None:
+                dH[j] = g[i]
+    return dH, (dW if want_dW else None)

@@ -1,0 +1,298 @@
+"""Pins for the float64 oracle: closed forms, invariants, library routines,
+brute force and finite differences.  Each test is chosen so a plausible slip
+in the oracle (a dropped term, a wrong sign or index, a transposed operand,
+the wrong std estimator) fails at least one of them.  CPU only."""
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from workloads import BY_NAME
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+BETA = 0.04
+
+
+def _table(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _problem(seed=0, P=2, G=3, L=5, d=7, V=11, ref_sigma=0.05, lo=2, hi=5):
+    rng = np.random.default_rng(seed)
+    B = P * G
+    N = B * L
+    H = rng.standard_normal((N, d))
+    W = 0.3 * rng.standard_normal((V, d))
+    H_ref = H + ref_sigma * rng.standard_normal((N, d))
+    y = rng.integers(0, V, N)
+    r = rng.integers(0, 4, B).astype(np.float64)
+    lengths = rng.integers(lo, hi + 1, B)
+    mask = (np.arange(L)[None, :] < lengths[:, None]).astype(np.uint8).reshape(-1)
+    adv = oracle.group_advantages(r, G)
+    ref_lp, _ = oracle.token_logprobs(H_ref, W, y)
+    return dict(H=H, W=W, H_ref=H_ref, y=y, r=r, mask=mask, adv=adv, ref_lp=ref_lp,
+                L=L, G=G, N=N, V=V, d=d)
+
+
+# --------------------------------------------------------------------------- advantages
+def test_advantages_closed_form_golden():
+    rows = _table("advantages_closed_form.txt")
+    r = np.array([float(a) for a, _ in rows])
+    want = np.array([float(b) for _, b in rows])
+    got = oracle.group_advantages(r, 4, eps=1e-4)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-15)
+
+
+def test_advantages_match_numpy_std_ddof1():
+    rng = np.random.default_rng(3)
+    r = rng.integers(0, 4, (6, 8)).astype(np.float64)
+    want = (r - r.mean(axis=1, keepdims=True)) / (np.std(r, axis=1, ddof=1, keepdims=True) + 1e-4)
+    np.testing.assert_allclose(oracle.group_advantages(r.reshape(-1), 8), want.reshape(-1),
+                               rtol=1e-14, atol=1e-14)
+
+
+def test_advantages_group_sums_vanish():
+    rng = np.random.default_rng(4)
+    r = rng.standard_normal(40)
+    A = oracle.group_advantages(r, 5).reshape(8, 5)
+    assert np.abs(A.sum(axis=1)).max() < 1e-12
+
+
+def test_advantages_degenerate_groups():
+    assert np.all(oracle.group_advantages(np.full(8, 2.0), 4) == 0.0)
+    assert np.all(oracle.group_advantages(np.array([0.0, 3.0, 1.0]), 1) == 0.0)
+    A = oracle.group_advantages(np.array([1.0, np.nan, 2.0, 3.0, 0.0, 1.0, 2.0, 3.0]), 4)
+    assert np.all(np.isnan(A[:4])) and np.all(np.isfinite(A[4:]))
+
+
+# --------------------------------------------------------------------------- log-probs
+def test_logprobs_match_scipy_log_softmax():
+    p = _problem(1)
+    lp, lse = oracle.token_logprobs(p["H"], p["W"], p["y"])
+    Z = p["H"] @ p["W"].T
+    want = scipy.special.log_softmax(Z, axis=1)[np.arange(p["N"]), p["y"]]
+    np.testing.assert_allclose(lp, want, rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(Z, axis=1), rtol=1e-13)
+    assert np.all(lp <= 0) and np.all(lse >= Z.max(axis=1))
+
+
+def test_logprobs_brute_force_python_loops():
+    rng = np.random.default_rng(2)
+    H = rng.standard_normal((3, 4))
+    W = rng.standard_normal((5, 4))
+    y = [4, 0, 2]
+    lp, _ = oracle.token_logprobs(H, W, y)
+    for t in range(3):
+        z = [sum(H[t][k] * W[v][k] for k in range(4)) for v in range(5)]
+        want = z[y[t]] - math.log(sum(math.exp(zv) for zv in z))
+        assert abs(lp[t] - want) < 1e-13
+
+
+def test_logprobs_closed_forms():
+    # W = 0: every logit is 0, so lp = -log V and lse = log V.
+    H = np.ones((4, 3))
+    lp, lse = oracle.token_logprobs(H, np.zeros((7, 3)), [0, 3, 6, 2])
+    np.testing.assert_allclose(lp, -math.log(7), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse, math.log(7), rtol=0, atol=1e-15)
+    # V = 2, logits (a, b): lp of target 0 is -log(1 + exp(b - a)).
+    H = np.array([[1.0, 0.0], [0.0, 1.0]])
+    W = np.array([[0.7, -0.2], [-1.3, 2.5]])       # z_0 = (0.7, -1.3), z_1 = (-0.2, 2.5)
+    lp, _ = oracle.token_logprobs(H, W, [0, 0])
+    np.testing.assert_allclose(lp, [-math.log1p(math.exp(-2.0)), -math.log1p(math.exp(2.7))],
+                               rtol=1e-15)
+
+
+def test_logprobs_large_logits_stay_finite():
+    # max shift: logits near 1e3 must not overflow
+    H = np.array([[1000.0], [-1000.0]])
+    W = np.array([[1.0], [0.999]])
+    lp, _ = oracle.token_logprobs(H, W, [0, 1])
+    np.testing.assert_allclose(lp, [-math.log1p(math.exp(-1.0)), -math.log1p(math.exp(-1.0))],
+                               rtol=1e-12)
+
+
+def test_logprobs_block_size_and_row_subset_invariance():
+    p = _problem(5, P=3, G=4, L=9)
+    a, _ = oracle.token_logprobs(p["H"], p["W"], p["y"], block=256)
+    b, _ = oracle.token_logprobs(p["H"], p["W"], p["y"], block=7)
+    rows = np.array([5, 0, 17, 100])
+    c, _ = oracle.token_logprobs(p["H"], p["W"], p["y"], rows=rows, block=3)
+    np.testing.assert_array_equal(a, b)
+    np.testing.assert_array_equal(a[rows], c)
+
+
+# --------------------------------------------------------------------------- KL
+def test_kl_closed_form_golden():
+    for x, want in _table("kl_closed_form.txt"):
+        x, want = float(x), float(want)
+        # x = ref_lp - lp: put ref_lp = x + lp for a non-trivial lp
+        got = oracle.reverse_kl_k3(np.array([x - 2.5]), np.array([-2.5]))[0]
+        assert abs(got - want) < 1e-15, (x, got, want)
+
+
+def test_kl_nonnegative_and_zero_only_at_equality():
+    rng = np.random.default_rng(6)
+    ref = -rng.random(1000) * 10
+    lp = -rng.random(1000) * 10
+    kl = oracle.reverse_kl_k3(ref, lp)
+    assert np.all(kl >= 0) and np.all(kl > 0)
+    assert np.all(oracle.reverse_kl_k3(lp, lp) == 0.0)
+
+
+# --------------------------------------------------------------------------- loss
+def test_policy_equals_reference_gives_zero_kl_and_minus_mean_advantage():
+    p = _problem(7)
+    ref_lp, _ = oracle.token_logprobs(p["H"], p["W"], p["y"])      # H_ref = H
+    out = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], p["adv"], ref_lp, p["L"], BETA)
+    assert np.all(out["kl"] == 0.0)
+    A_t = np.repeat(p["adv"], p["L"])
+    m = p["mask"].astype(np.float64)
+    assert out["loss"] == pytest.approx(-(m * A_t).sum() / m.sum(), rel=1e-15, abs=1e-15)
+
+
+def test_loss_special_cases():
+    p = _problem(8)
+    m = p["mask"].astype(np.float64)
+    A_t = np.repeat(p["adv"], p["L"])
+    # beta = 0: the KL drops out, independent of H and W
+    out0 = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"], 0.0)
+    assert out0["loss"] == pytest.approx(-(m * A_t).sum() / m.sum(), rel=1e-14)
+    # A = 0: loss is beta times the masked mean KL
+    zeros = np.zeros_like(p["adv"])
+    outa = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], zeros, p["ref_lp"], p["L"], BETA)
+    assert outa["loss"] == pytest.approx(BETA * (m * outa["kl"]).sum() / m.sum(), rel=1e-14)
+    assert outa["loss"] > 0
+    # empty mask: loss 0
+    oute = oracle.loss_forward(p["H"], p["W"], p["y"], np.zeros_like(p["mask"]), p["adv"],
+                               p["ref_lp"], p["L"], BETA)
+    assert oute["loss"] == 0.0
+
+
+def _torch_autograd_loss(p, H, W, beta=BETA):
+    """Independent reference: torch float64 autograd of the stop-gradient ratio
+    exp(lp - sg(lp)) times the per-sequence advantage, plus beta times the k3
+    KL, masked token mean."""
+    B, L = len(p["adv"]), p["L"]
+    logp = torch.log_softmax(H @ W.T, dim=1)
+    lp = logp[torch.arange(logp.shape[0]), torch.as_tensor(p["y"]).long()].reshape(B, L)
+    ratio = (lp - lp.detach()).exp()
+    A_tok = torch.as_tensor(p["adv"]).reshape(B, 1).expand(B, L)
+    x = torch.as_tensor(p["ref_lp"]).reshape(B, L) - lp
+    k3 = x.exp() - x - 1.0
+    m = torch.as_tensor(p["mask"]).double().reshape(B, L)
+    per_token = beta * k3 - ratio * A_tok
+    return (per_token * m).sum() / torch.clamp(m.sum(), min=1.0)
+
+
+def test_gradients_match_torch_autograd():
+    p = _problem(9)
+    H = torch.tensor(p["H"], requires_grad=True)
+    W = torch.tensor(p["W"], requires_grad=True)
+    loss = _torch_autograd_loss(p, H, W)
+    loss.backward()
+    out = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"], BETA)
+    assert out["loss"] == pytest.approx(loss.item(), rel=1e-13)
+    dH, dW = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                  p["L"], BETA)
+    np.testing.assert_allclose(dH, H.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
+def _surrogate(p, H, W, lp0, beta=BETA):
+    """J = sum m [-(exp(lp - lp0) A - beta kl)] / sum m, lp0 frozen: value equals the
+    loss at lp = lp0 and its gradient equals the loss gradient."""
+    lp, _ = oracle.token_logprobs(H, W, p["y"])
+    A_t = np.repeat(p["adv"], p["L"])
+    x = p["ref_lp"] - lp
+    ell = -(np.exp(lp - lp0) * A_t - beta * (np.exp(x) - x - 1))
+    m = p["mask"].astype(np.float64)
+    return (m * ell).sum() / max(m.sum(), 1.0)
+
+
+@pytest.mark.parametrize("beta,zero_adv", [(BETA, False), (BETA, True), (0.0, False)])
+def test_gradients_match_central_differences_of_surrogate(beta, zero_adv):
+    p = _problem(10, ref_sigma=0.7)
+    if zero_adv:
+        p["adv"] = np.zeros_like(p["adv"])          # pure KL path
+    lp0, _ = oracle.token_logprobs(p["H"], p["W"], p["y"])
+    dH, dW = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                  p["L"], beta)
+    rng = np.random.default_rng(11)
+    h = 1e-6
+    for _ in range(12):
+        t, k = rng.integers(0, p["N"]), rng.integers(0, p["d"])
+        Hp, Hm = p["H"].copy(), p["H"].copy()
+        Hp[t, k] += h
+        Hm[t, k] -= h
+        fd = (_surrogate(p, Hp, p["W"], lp0, beta) - _surrogate(p, Hm, p["W"], lp0, beta)) / (2 * h)
+        assert abs(fd - dH[t, k]) < 1e-8 + 1e-6 * abs(fd), (t, k, fd, dH[t, k])
+        v, k = rng.integers(0, p["V"]), rng.integers(0, p["d"])
+        Wp, Wm = p["W"].copy(), p["W"].copy()
+        Wp[v, k] += h
+        Wm[v, k] -= h
+        fd = (_surrogate(p, p["H"], Wp, lp0, beta) - _surrogate(p, p["H"], Wm, lp0, beta)) / (2 * h)
+        assert abs(fd - dW[v, k]) < 1e-8 + 1e-6 * abs(fd), (v, k, fd, dW[v, k])
+
+
+def test_gradient_invariants():
+    p = _problem(12)
+    dH, dW = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                  p["L"], BETA)
+    # each dZ row sums to zero, so the vocab-sum of dW vanishes
+    assert np.abs(dW.sum(axis=0)).max() < 1e-15 * max(1.0, np.abs(dW).max()) + 1e-16
+    # masked tokens get no gradient
+    assert np.all(dH[p["mask"] == 0] == 0.0)
+    assert np.abs(dH[p["mask"] == 1]).max() > 0
+    # requested rows only / no dW
+    rows = np.array([3, 0, 11])
+    dHr, none = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                     p["L"], BETA, dh_rows=rows, want_dW=False)
+    assert none is None
+    np.testing.assert_allclose(dHr, dH[rows], rtol=1e-13, atol=1e-18)
+
+
+def test_policy_equals_reference_gradient_is_weighted_cross_entropy():
+    p = _problem(13)
+    p["ref_lp"], _ = oracle.token_logprobs(p["H"], p["W"], p["y"])    # H_ref = H
+    dH, dW = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                  p["L"], BETA)
+    H = torch.tensor(p["H"], requires_grad=True)
+    W = torch.tensor(p["W"], requires_grad=True)
+    ce = torch.nn.functional.cross_entropy(H @ W.T, torch.as_tensor(p["y"]).long(), reduction="none")
+    m = torch.as_tensor(p["mask"]).double()
+    w = m * torch.as_tensor(np.repeat(p["adv"], p["L"])) / m.sum()
+    (w * ce).sum().backward()
+    np.testing.assert_allclose(dH, H.grad.numpy(), rtol=1e-10, atol=1e-16)
+    np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-10, atol=1e-16)
+
+
+def test_grad_loss_scales_linearly():
+    p = _problem(14)
+    a = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"], BETA)
+    b = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"], BETA,
+                             grad_loss=-2.5)
+    for got, base in ((b[0], a[0]), (b[1], a[1])):
+        np.testing.assert_allclose(got, -2.5 * base, rtol=1e-13, atol=1e-14 * np.abs(base).max())
+
+
+# --------------------------------------------------------------------------- workload shapes
+def test_long_context_workload_reproduces_pages_logit_memory():
+    """8 x 20480 tokens x 128256 vocab x 4 B is the pages' 78.3 GB of logits;
+    one generation at a time is 9.8 GB; the difference is the 68.5 GB saved."""
+    w = BY_NAME["llama3.1-8b-20k-bf16"]
+    figs = {k: float(v) for k, v in _table("logit_memory_figures.txt")}
+    full = w.N * w.V * 4 / 2**30
+    one = w.L * w.V * 4 / 2**30
+    assert round(full, 1) == figs["full_fp32_logits"]
+    assert round(one, 1) == figs["one_generation_fp32_logits"]
+    assert round(full - one, 1) == figs["saved"]
