@@ -1,0 +1,212 @@
+"""Benchmark: one step = one pass of the whole fused GRPO loss hot path over
+one batch of synthetic inputs on one GPU:
+
+    advantages -> reference log-probs (no grad) -> loss forward -> loss backward
+
+Prints ONE JSON line.  `value` is flattened tokens per second of the whole
+step (inputs resident in HBM before the timed region).  Also reported: the
+forward+backward-only rate and its fraction of dense bf16 MFMA peak, peak HBM
+allocated, a roofline entry for the dominant kernel timed with HIP events on
+its own stream, and the float64 oracle timed on the host cores on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "flattened tokens/s GRPO loss fwd+bwd (1 GPU) + % bf16 MFMA peak + peak HBM"
+PEAK_FLOPS = {"bf16": 2.5e15, "f32": 157.3e12}   # MI355X dense MFMA peaks
+DEFAULT_WORKLOAD = "qwen2.5-1.5b-bf16"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_flops(kind, d, V, N, N_act):
+    """Algorithmic MFMA flops of one step's launches of a kernel kind."""
+    if kind == "lse_partials":          # reference pass + loss forward: 2 d V per token each
+        return 2 * (2.0 * d * V * N)
+    if kind in ("dz", "dh_gemm", "dw_gemm"):   # backward, active tokens only
+        return 2.0 * d * V * N_act
+    return None
+
+
+def cpu_baseline(w, inp, seconds=15.0):
+    """The float64 oracle, as it stands, on a bounded sample: the first n
+    flattened tokens of the batch, run through reference log-probs, loss forward
+    and loss backward, on all host threads BLAS uses."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+
+    H = inp["H"].detach().cpu()
+    H_ref = inp["H_ref"].detach().cpu()
+    W64 = inp["W"].detach().to("cpu").double().numpy()
+    y = inp["y"].cpu().numpy().astype(np.int64)
+    mask = inp["mask"].cpu().numpy()
+    r = inp["rewards"].cpu().numpy()
+
+    def run(n):
+        Hs = H[:n].double().numpy()
+        Hr = H_ref[:n].double().numpy()
+        ys, ms = y[:n], mask[:n]
+        adv = oracle.group_advantages(r, w.G)[:1]
+        t0 = time.perf_counter()
+        ref, _ = oracle.token_logprobs(Hr, W64, ys)
+        oracle.loss_forward(Hs, W64, ys, ms, adv, ref, n, 0.04)
+        oracle.loss_backward(Hs, W64, ys, ms, adv, ref, n, 0.04)
+        return time.perf_counter() - t0
+
+    n = min(16, w.L)
+    t = run(n)
+    n2 = int(max(16, min(w.L, 4096, n * seconds / max(t, 1e-3))))
+    t2 = run(n2)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    return {"value": n2 / t2, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n2} flattened tokens of sequence 0 (ref + fwd + bwd, float64 "
+                      f"NumPy, full V={w.V}, d={w.d}); {t2:.1f} s on "
+                      f"{len(os.sched_getaffinity(0))} visible host CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import grpo_policy_loss_amd as gp
+    import workloads
+
+    w = workloads.BY_NAME[args.workload]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {w.name}: N={w.N} d={w.d} V={w.V} {w.dtype} chunk={w.chunk}")
+    t0 = time.time()
+    inp = workloads.generate(w, seed=args.seed, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+    N, d, V, B, L = w.N, w.d, w.V, w.B, w.L
+    N_act = int(inp["mask"].sum().item())
+    dt = gp.GRPO_BF16 if w.dtype == "bf16" else gp.GRPO_F32
+    ws_f = torch.empty(gp.grpo_workspace_bytes(gp.GRPO_OP_FWD, N, d, V, dt, w.chunk),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(gp.grpo_workspace_bytes(gp.GRPO_OP_BWD, N, d, V, dt, w.chunk),
+                       dtype=torch.uint8, device=dev)
+    dW = torch.zeros(V, d, dtype=torch.float32, device=dev)
+    dH = torch.empty_like(inp["H"])
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        adv = gp.grpo_advantages(inp["rewards"], w.G, workloads.EPS)
+        ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, workspace=ws_f)
+        if ev is not None:
+            ev[1].record(stream)
+        loss, lp, kl, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref,
+                                             B, L, workloads.BETA, w.chunk, workspace=ws_f)
+        if ev is not None:
+            ev[2].record(stream)
+        dW.zero_()
+        gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp, lse, B, L,
+                         workloads.BETA, 1.0, w.chunk, dW=dW, dH=dH, workspace=ws_b)
+        if ev is not None:
+            ev[3].record(stream)
+        return loss
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup {i + 1}/{args.warmup} done")
+
+    torch.cuda.reset_peak_memory_stats(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    gp.grpo_timing_begin()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    kernels = gp.grpo_timing_end()
+    peak_bytes = torch.cuda.max_memory_allocated(dev)
+    log(f"[bench] {args.steps} timed steps in {t_total:.3f}s")
+
+    ms_ref = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    ms_fwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ms_bwd = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
+    ms_step = t_total * 1e3 / args.steps
+    fb_flops = 2.0 * d * V * N + 6.0 * d * V * N_act
+    peak = PEAK_FLOPS[w.dtype]
+
+    # roofline of the dominant kernel: algorithmic flops / its measured time
+    dom = max(kernels.items(), key=lambda kv: kv[1][1])
+    dom_name, (dom_launches, dom_ms) = dom
+    dom_flops = alg_flops(dom_name, d, V, N, N_act)
+    roof = None
+    if dom_flops is not None:
+        achieved = dom_flops * args.steps / (dom_ms * 1e-3) / 1e12
+        roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved * 1e12 / peak, 4),
+                "traffic": None, "launches": dom_launches,
+                "avg_launch_ms": round(dom_ms / dom_launches, 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the float64 oracle on the host ...")
+        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value']:.2f} tokens/s")
+
+    out = {
+        "metric": METRIC,
+        "value": round(N / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "tokens": N, "active_tokens": N_act, "d": d, "V": V,
+                   "chunk": w.chunk, "beta": workloads.BETA,
+                   "step": "advantages + reference log-probs + loss fwd + loss bwd"},
+        "fwd_bwd_tokens_per_s": round(N / ((ms_fwd + ms_bwd) * 1e-3), 1),
+        "fwd_bwd_mfma_frac": round(fb_flops / ((ms_fwd + ms_bwd) * 1e-3) / peak, 4),
+        "ms": {"advantages+ref": round(ms_ref, 3), "fwd": round(ms_fwd, 3),
+               "bwd": round(ms_bwd, 3)},
+        "peak_hbm_gb": round(peak_bytes / 1e9, 3),
+        "full_fp32_logits_gb": round(N * V * 4 / 1e9, 2),
+        "kernels_ms_per_step": {k: round(v[1] / args.steps, 3) for k, v in kernels.items()},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,22 @@
+"""MI355X-native fused, chunked GRPO policy loss.
+
+The loss runs in libgrpo.so (hand-written HIP kernels for gfx950) behind the C
+ABI declared in include/grpo.h; this package is its thin Python binding.
+"""
+from ._lib import (  # noqa: F401
+    GRPO_BF16,
+    GRPO_F32,
+    GRPO_OP_BWD,
+    GRPO_OP_FWD,
+    GRPO_OP_REF,
+    GrpoError,
+    grpo_advantages,
+    grpo_gemm_nt,
+    grpo_loss_bwd,
+    grpo_loss_fwd,
+    grpo_ref_logprobs,
+    grpo_timing_begin,
+    grpo_timing_end,
+    grpo_workspace_bytes,
+    lib,
+)

@@ -1,0 +1,212 @@
+"""ctypes binding of libgrpo.so (include/grpo.h).
+
+Argument marshalling only: every step of the loss runs in the HIP library.
+torch supplies device memory (outputs and workspace) and the current stream.
+There is no CPU fallback: without the built library or a GPU every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrpo.so")
+
+GRPO_F32, GRPO_BF16 = 0, 1
+GRPO_OP_REF, GRPO_OP_FWD, GRPO_OP_BWD = 0, 1, 2
+STATUS = {0: "GRPO_OK", -1: "GRPO_ERR_INVALID_ARG", -2: "GRPO_ERR_WORKSPACE",
+          -3: "GRPO_ERR_UNSUPPORTED", -4: "GRPO_ERR_HIP"}
+
+_i64, _f32, _vp, _sz, _int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+
+# name -> (restype, argtypes); mirrors include/grpo.h
+SIGNATURES = {
+    "grpo_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _int, _i64]),
+    "grpo_advantages": (_int, [_vp, _i64, _i64, _f32, _vp, _vp]),
+    "grpo_ref_logprobs": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _i64, _vp, _vp, _sz, _vp]),
+    "grpo_loss_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _f32,
+                             _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "grpo_loss_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
+                             _f32, _f32, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "grpo_gemm_nt": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
+    "grpo_timing_begin": (_int, []),
+    "grpo_timing_end": (_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_int),
+                               ctypes.POINTER(ctypes.c_double), _int]),
+    "grpo_strerror": (ctypes.c_char_p, [_int]),
+    "grpo_last_error": (ctypes.c_char_p, []),
+}
+
+
+class GrpoError(RuntimeError):
+    def __init__(self, fn: str, code: int, detail: str):
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}: {detail}")
+        self.code = code
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libgrpo.so (built in-tree by grpo_policy_loss_amd.build)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with grpo_policy_loss_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise GrpoError(fn, code, lib().grpo_last_error().decode(errors="replace"))
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return GRPO_F32
+    if t.dtype == torch.bfloat16:
+        return GRPO_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _want(t: torch.Tensor, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def grpo_workspace_bytes(op: int, N: int, d: int, V: int, dtype: int, chunk: int) -> int:
+    return int(lib().grpo_workspace_bytes(op, N, d, V, dtype, chunk))
+
+
+def _workspace(op, N, d, V, dt, chunk, device, workspace):
+    need = grpo_workspace_bytes(op, N, d, V, dt, chunk)
+    if need == 0:
+        _check("grpo_workspace_bytes", -1)
+    if workspace is not None and workspace.numel() * workspace.element_size() >= need:
+        return workspace
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+def grpo_advantages(rewards: torch.Tensor, group_size: int, eps: float = 1e-4, out=None):
+    _dev(rewards)
+    _want(rewards, torch.float32, "rewards")
+    if rewards.numel() % group_size:
+        raise ValueError("rewards length must be a multiple of group_size")
+    out = torch.empty_like(rewards) if out is None else out
+    _check("grpo_advantages", lib().grpo_advantages(
+        _ptr(rewards), rewards.numel() // group_size, group_size, eps, _ptr(out), _stream()))
+    return out
+
+
+def grpo_ref_logprobs(H_ref, W, y, chunk: int = 4096, out=None, workspace=None):
+    _dev(H_ref, W, y)
+    _want(y, torch.int32, "y")
+    N, d = H_ref.shape
+    V = W.shape[0]
+    dt = _dt(H_ref)
+    if W.dtype != H_ref.dtype or W.shape[1] != d or y.numel() != N:
+        raise ValueError("shape/dtype mismatch between H_ref, W, y")
+    out = torch.empty(N, dtype=torch.float32, device=H_ref.device) if out is None else out
+    ws = _workspace(GRPO_OP_REF, N, d, V, dt, chunk, H_ref.device, workspace)
+    _check("grpo_ref_logprobs", lib().grpo_ref_logprobs(
+        _ptr(H_ref), _ptr(W), _ptr(y), N, d, V, dt, chunk, _ptr(out), _ptr(ws),
+        ws.numel(), _stream()))
+    return out
+
+
+def grpo_loss_fwd(H, W, y, mask, adv, ref_lp, B: int, L: int, beta: float = 0.04,
+                  chunk: int = 4096, workspace=None):
+    """Returns (loss[1], lp[N], kl[N], lse[N]), all float32 on the GPU."""
+    _dev(H, W, y, mask, adv, ref_lp)
+    _want(y, torch.int32, "y")
+    _want(mask, torch.uint8, "mask")
+    _want(adv, torch.float32, "adv")
+    _want(ref_lp, torch.float32, "ref_lp")
+    N, d = H.shape
+    V = W.shape[0]
+    dt = _dt(H)
+    if W.dtype != H.dtype or W.shape[1] != d or N != B * L or y.numel() != N \
+            or mask.numel() != N or ref_lp.numel() != N or adv.numel() != B:
+        raise ValueError("shape/dtype mismatch")
+    dev = H.device
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lp = torch.empty(N, dtype=torch.float32, device=dev)
+    kl = torch.empty(N, dtype=torch.float32, device=dev)
+    lse = torch.empty(N, dtype=torch.float32, device=dev)
+    ws = _workspace(GRPO_OP_FWD, N, d, V, dt, chunk, dev, workspace)
+    _check("grpo_loss_fwd", lib().grpo_loss_fwd(
+        _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(adv), _ptr(ref_lp), B, L, d, V, dt, beta,
+        chunk, _ptr(loss), _ptr(lp), _ptr(kl), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return loss, lp, kl, lse
+
+
+def grpo_loss_bwd(H, W, y, mask, adv, ref_lp, lp, lse, B: int, L: int, beta: float = 0.04,
+                  grad_loss: float = 1.0, chunk: int = 4096, dW=None, dH=None, workspace=None):
+    """Returns (dH[N, d] in H's dtype, dW[V, d] float32).  dW is accumulated into
+    when given (zeros are allocated otherwise)."""
+    _dev(H, W, y, mask, adv, ref_lp, lp, lse)
+    N, d = H.shape
+    V = W.shape[0]
+    dt = _dt(H)
+    if W.dtype != H.dtype or N != B * L:
+        raise ValueError("shape/dtype mismatch")
+    dev = H.device
+    dH = torch.empty_like(H) if dH is None else dH
+    dW = torch.zeros(V, d, dtype=torch.float32, device=dev) if dW is None else dW
+    _dev(dH, dW)
+    _want(dW, torch.float32, "dW")
+    ws = _workspace(GRPO_OP_BWD, N, d, V, dt, chunk, dev, workspace)
+    _check("grpo_loss_bwd", lib().grpo_loss_bwd(
+        _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(adv), _ptr(ref_lp), _ptr(lp), _ptr(lse),
+        B, L, d, V, dt, beta, grad_loss, chunk, _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
+        _stream()))
+    return dH, dW
+
+
+def grpo_timing_begin():
+    """Start per-kernel HIP-event timing of this thread's library launches."""
+    lib().grpo_timing_begin()
+
+
+def grpo_timing_end(max_entries: int = 32):
+    """Stop timing; {kernel name: (launches, total milliseconds)}."""
+    names = (ctypes.c_char_p * max_entries)()
+    launches = (_int * max_entries)()
+    ms = (ctypes.c_double * max_entries)()
+    n = lib().grpo_timing_end(names, launches, ms, max_entries)
+    return {names[i].decode(): (launches[i], ms[i]) for i in range(min(n, max_entries))}
+
+
+def grpo_gemm_nt(A, B):
+    """C = A @ B.T in float32 through the library's MFMA tile main loop."""
+    _dev(A, B)
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or A.dtype != B.dtype:
+        raise ValueError("shape/dtype mismatch")
+    C = torch.empty(M, N, dtype=torch.float32, device=A.device)
+    _check("grpo_gemm_nt", lib().grpo_gemm_nt(_ptr(A), _ptr(B), M, N, K, _dt(A), _ptr(C), _stream()))
+    return C

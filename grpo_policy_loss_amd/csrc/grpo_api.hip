@@ -1,0 +1,381 @@
+// grpo_api.hip -- the C ABI (include/grpo.h): argument checks, workspace
+// planning and the launch sequence of each call.  No allocation, no host
+// synchronisation: every call enqueues on the caller's stream and returns.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "../../include/grpo.h"
+#include "kernels.hpp"
+#include "tile_mma.hpp"
+#include "timing.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(GRPO_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+inline size_t esize(int dtype) { return dtype == GRPO_F32 ? 4 : 2; }
+
+// Bump allocator over the caller's workspace.
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+// Forward / reference workspace: per-(vocab tile, token) partial pairs of
+// one chunk, the chunk's target logits, and the per-block loss sums.
+struct FwdPlan {
+  int64_t C, cpad, S, nchunks, parts_per_chunk;
+  size_t o_pm, o_ps, o_zy, o_lpart, o_cpart, total;
+};
+
+FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
+  FwdPlan p{};
+  p.C = std::min<int64_t>(chunk, N);
+  p.cpad = round_up(p.C, grpo::kBN);
+  p.S = (V + grpo::kBM - 1) / grpo::kBM;
+  p.nchunks = (N + p.C - 1) / p.C;
+  p.parts_per_chunk = p.cpad / 256;
+  Carve c;
+  p.o_pm = c.take((size_t)(p.S * p.cpad) * 4);
+  p.o_ps = c.take((size_t)(p.S * p.cpad) * 4);
+  p.o_zy = c.take((size_t)p.cpad * 4);
+  p.o_lpart = c.take((size_t)(p.nchunks * p.parts_per_chunk) * 8);
+  p.o_cpart = c.take((size_t)(p.nchunks * p.parts_per_chunk) * 4);
+  p.total = c.off;
+  return p;
+}
+
+// Backward workspace.  The dZ slab (and its transpose) covers `vs`
+// vocabulary rows of one chunk; vs is chosen so each is at most 256 MiB.
+constexpr int64_t kSlabBytes = 256ll << 20;
+
+struct BwdPlan {
+  int64_t C, cpad, vpad, vs, nslabs, nchunks;
+  size_t o_idx, o_cnt, o_wt, o_hact, o_ht, o_coef, o_lse, o_y, o_dz, o_dzt, o_dhacc, total;
+};
+
+BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
+  BwdPlan p{};
+  const size_t es = esize(dtype);
+  p.C = std::min<int64_t>(chunk, N);
+  p.cpad = round_up(p.C, grpo::kBN);
+  p.vpad = round_up(V, grpo::kBM);
+  int64_t vs = kSlabBytes / (p.cpad * (int64_t)es);
+  vs = std::max<int64_t>(grpo::kBM, vs / grpo::kBM * grpo::kBM);
+  p.vs = std::min<int64_t>(vs, p.vpad);
+  p.nslabs = (V + p.vs - 1) / p.vs;
+  p.nchunks = (N + p.C - 1) / p.C;
+  Carve c;
+  p.o_idx = c.take((size_t)N * 4);
+  p.o_cnt = c.take(4);
+  p.o_wt = c.take((size_t)(d * p.vpad) * es);
+  p.o_hact = c.take((size_t)(p.cpad * d) * es);
+  p.o_ht = c.take((size_t)(d * p.cpad) * es);
+  p.o_coef = c.take((size_t)p.cpad * 4);
+  p.o_lse = c.take((size_t)p.cpad * 4);
+  p.o_y = c.take((size_t)p.cpad * 4);
+  p.o_dz = c.take((size_t)(p.cpad * p.vs) * es);
+  p.o_dzt = c.take((size_t)(p.vs * p.cpad) * es);
+  p.o_dhacc = c.take((size_t)(p.cpad * d) * 4);
+  p.total = c.off;
+  return p;
+}
+
+// Shape checks shared by all calls.  Operands are addressed per 256-row tile
+// with 32-bit offsets, so one tile's rows must span < 2 GiB.
+int check_shape(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
+  if (N <= 0 || d <= 0 || V <= 0 || chunk <= 0)
+    return fail(GRPO_ERR_INVALID_ARG, "sizes must be positive (N=%lld d=%lld V=%lld chunk=%lld)",
+                (long long)N, (long long)d, (long long)V, (long long)chunk);
+  if (dtype != GRPO_F32 && dtype != GRPO_BF16)
+    return fail(GRPO_ERR_INVALID_ARG, "dtype %d is neither GRPO_F32 nor GRPO_BF16", dtype);
+  const int64_t vec = 16 / (int64_t)esize(dtype);
+  if (d % vec != 0)
+    return fail(GRPO_ERR_UNSUPPORTED, "d=%lld must be a multiple of %lld for this dtype",
+                (long long)d, (long long)vec);
+  if (N > INT32_MAX || V > INT32_MAX || chunk > (1 << 24))
+    return fail(GRPO_ERR_UNSUPPORTED, "N, V must fit int32 and chunk <= 2^24");
+  const int64_t cpad = round_up(std::min(chunk, N), grpo::kBN);
+  const int64_t row_span = 256 * std::max<int64_t>(std::max(d, round_up(V, 256)), cpad) * 4;
+  if (row_span >= (1ll << 31))
+    return fail(GRPO_ERR_UNSUPPORTED, "a 256-row tile would span >= 2 GiB (d=%lld V=%lld)",
+                (long long)d, (long long)V);
+  return GRPO_OK;
+}
+
+#define GRPO_CHECK_PTR(p)                                                          \
+  do {                                                                             \
+    if ((p) == nullptr) return fail(GRPO_ERR_INVALID_ARG, "null pointer: %s", #p); \
+  } while (0)
+
+#define GRPO_HIP(call)                                    \
+  do {                                                    \
+    hipError_t e_ = (call);                               \
+    if (e_ != hipSuccess) return hip_fail(e_, #call);     \
+  } while (0)
+
+template <typename T>
+int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* mask,
+             const float* adv, const float* ref_lp, int64_t N, int64_t L, int64_t d, int64_t V,
+             float beta, int64_t chunk, float* loss, float* out_lp, float* out_kl,
+             float* out_lse, char* ws, hipStream_t s) {
+  const FwdPlan p = plan_fwd(N, V, chunk);
+  float* pm = (float*)(ws + p.o_pm);
+  float* ps = (float*)(ws + p.o_ps);
+  float* zy = (float*)(ws + p.o_zy);
+  double* lpart = (double*)(ws + p.o_lpart);
+  int* cpart = (int*)(ws + p.o_cpart);
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    const int64_t c0 = c * p.C;
+    const int n_tok = (int)std::min<int64_t>(p.C, N - c0);
+    GRPO_HIP(grpo::launch_lse_partials<T>(W, H + c0 * d, y + c0, V, d, n_tok, (int)p.cpad, pm, ps,
+                                          zy, s));
+    GRPO_HIP(grpo::launch_lse_merge(mode, pm, ps, zy, (int)p.S, (int)p.cpad, n_tok, c0, y, V,
+                                    out_lp, out_lse, out_kl, ref_lp, mask, adv, L, beta, lpart,
+                                    cpart, (int)(c * p.parts_per_chunk), s));
+  }
+  if (mode == 1) {
+    // every full chunk writes all cpad/256 of its slots; a short last chunk
+    // writes only its first blocks, and the final sum reads exactly those
+    const int64_t last_c0 = (p.nchunks - 1) * p.C;
+    const int64_t last_blocks = (std::min<int64_t>(p.C, N - last_c0) + 255) / 256;
+    const int64_t nparts = (p.nchunks - 1) * p.parts_per_chunk + last_blocks;
+    GRPO_HIP(grpo::launch_loss_final(lpart, cpart, (int)nparts, loss, s));
+  }
+  return GRPO_OK;
+}
+
+template <typename T>
+int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, const float* adv,
+             const float* ref_lp, const float* lp, const float* lse, int64_t N, int64_t L,
+             int64_t d, int64_t V, float beta, float grad_loss, int64_t chunk, T* dH, float* dW,
+             char* ws, int dtype, hipStream_t s) {
+  const BwdPlan p = plan_bwd(N, d, V, dtype, chunk);
+  int32_t* idx = (int32_t*)(ws + p.o_idx);
+  int32_t* cnt = (int32_t*)(ws + p.o_cnt);
+  T* WT = (T*)(ws + p.o_wt);
+  T* H_act = (T*)(ws + p.o_hact);
+  T* HT = (T*)(ws + p.o_ht);
+  float* coef = (float*)(ws + p.o_coef);
+  float* lse_c = (float*)(ws + p.o_lse);
+  int32_t* y_c = (int32_t*)(ws + p.o_y);
+  T* dZ = (T*)(ws + p.o_dz);
+  T* dZT = (T*)(ws + p.o_dzt);
+  float* dH_acc = (float*)(ws + p.o_dhacc);
+
+  GRPO_HIP(grpo::launch_zero(dH, (size_t)(N * d) * sizeof(T), s));
+  GRPO_HIP(grpo::launch_active_scan(mask, N, idx, cnt, s));
+  GRPO_HIP(grpo::launch_transpose<T>(W, V, d, WT, p.vpad, s));
+  // Chunks are planned for the worst case (every token active); chunks past
+  // the device-side active count exit at once, so no host sync is needed.
+  for (int64_t c = 0; c < p.nchunks; ++c) {
+    const int64_t c0 = c * p.C;
+    const int C = (int)p.C;
+    GRPO_HIP(grpo::launch_bwd_prep<T>(H, d, idx, cnt, c0, C, (int)p.cpad, y, mask, adv, ref_lp, lp,
+                                      lse, L, beta, grad_loss, H_act, coef, lse_c, y_c, s));
+    GRPO_HIP(grpo::launch_transpose<T>(H_act, p.cpad, d, HT, p.cpad, s));
+    for (int64_t sl = 0; sl < p.nslabs; ++sl) {
+      const int64_t v0 = sl * p.vs;
+      const int vs_valid = (int)std::min<int64_t>(p.vs, V - v0);
+      GRPO_HIP(grpo::launch_dz<T>(W, H_act, d, V, v0, vs_valid, (int)p.vs, cnt, c0, C,
+                                  (int)p.cpad, coef, lse_c, y_c, dZ, dZT, s));
+      GRPO_HIP(grpo::launch_dh_gemm<T>(WT, p.vpad, v0, vs_valid, dZ, (int)p.vs, d, cnt, c0, C,
+                                       (int)p.cpad, sl == 0 ? 1 : 0, dH_acc, s));
+      GRPO_HIP(grpo::launch_dw_gemm<T>(HT, (int)p.cpad, dZT, d, V, v0, vs_valid, cnt, c0, C, dW,
+                                       s));
+    }
+    GRPO_HIP(grpo::launch_dh_scatter<T>(dH_acc, d, idx, cnt, c0, C, dH, s));
+  }
+  return GRPO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* grpo_strerror(int code) {
+  switch (code) {
+    case GRPO_OK: return "success";
+    case GRPO_ERR_INVALID_ARG: return "invalid argument";
+    case GRPO_ERR_WORKSPACE: return "workspace missing or too small";
+    case GRPO_ERR_UNSUPPORTED: return "unsupported shape";
+    case GRPO_ERR_HIP: return "HIP runtime error";
+    default: return "unknown grpo status";
+  }
+}
+
+const char* grpo_last_error(void) { return g_last_error; }
+
+size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
+  if (check_shape(N, d, V, dtype, chunk) != GRPO_OK) return 0;
+  switch (op) {
+    case GRPO_OP_REF:
+    case GRPO_OP_FWD: return plan_fwd(N, V, chunk).total;
+    case GRPO_OP_BWD: return plan_bwd(N, d, V, dtype, chunk).total;
+    default: fail(GRPO_ERR_INVALID_ARG, "unknown op %d", op); return 0;
+  }
+}
+
+int grpo_advantages(const float* rewards, int64_t num_groups, int64_t group_size, float eps,
+                    float* adv, void* stream) {
+  g_last_error[0] = 0;
+  GRPO_CHECK_PTR(rewards);
+  GRPO_CHECK_PTR(adv);
+  if (num_groups <= 0 || group_size <= 0)
+    return fail(GRPO_ERR_INVALID_ARG, "num_groups and group_size must be positive");
+  if (num_groups > INT32_MAX) return fail(GRPO_ERR_UNSUPPORTED, "num_groups exceeds int32");
+  if (!isfinite(eps) || eps < 0.f) return fail(GRPO_ERR_INVALID_ARG, "eps must be finite, >= 0");
+  GRPO_HIP(grpo::launch_advantages(rewards, num_groups, group_size, eps, adv,
+                                   (hipStream_t)stream));
+  return GRPO_OK;
+}
+
+int grpo_ref_logprobs(const void* H_ref, const void* W, const int32_t* y, int64_t N, int64_t d,
+                      int64_t V, int dtype, int64_t chunk, float* ref_lp, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  GRPO_CHECK_PTR(H_ref);
+  GRPO_CHECK_PTR(W);
+  GRPO_CHECK_PTR(y);
+  GRPO_CHECK_PTR(ref_lp);
+  int st = check_shape(N, d, V, dtype, chunk);
+  if (st != GRPO_OK) return st;
+  const size_t need = plan_fwd(N, V, chunk).total;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GRPO_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GRPO_BF16)
+    return lse_pass<__bf16>(0, (const __bf16*)H_ref, (const __bf16*)W, y, nullptr, nullptr,
+                            nullptr, N, 1, d, V, 0.f, chunk, nullptr, ref_lp, nullptr, nullptr,
+                            (char*)workspace, s);
+  return lse_pass<float>(0, (const float*)H_ref, (const float*)W, y, nullptr, nullptr, nullptr, N,
+                         1, d, V, 0.f, chunk, nullptr, ref_lp, nullptr, nullptr,
+                         (char*)workspace, s);
+}
+
+int grpo_loss_fwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                  const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
+                  int64_t V, int dtype, float beta, int64_t chunk, float* loss, float* lp,
+                  float* kl, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  GRPO_CHECK_PTR(H);
+  GRPO_CHECK_PTR(W);
+  GRPO_CHECK_PTR(y);
+  GRPO_CHECK_PTR(mask);
+  GRPO_CHECK_PTR(adv);
+  GRPO_CHECK_PTR(ref_lp);
+  GRPO_CHECK_PTR(loss);
+  GRPO_CHECK_PTR(lp);
+  GRPO_CHECK_PTR(kl);
+  GRPO_CHECK_PTR(lse);
+  if (B <= 0 || L <= 0) return fail(GRPO_ERR_INVALID_ARG, "B and L must be positive");
+  if (B > INT32_MAX / L) return fail(GRPO_ERR_UNSUPPORTED, "B*L exceeds int32");
+  const int64_t N = B * L;
+  int st = check_shape(N, d, V, dtype, chunk);
+  if (st != GRPO_OK) return st;
+  if (!isfinite(beta)) return fail(GRPO_ERR_INVALID_ARG, "beta must be finite");
+  const size_t need = plan_fwd(N, V, chunk).total;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GRPO_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GRPO_BF16)
+    return lse_pass<__bf16>(1, (const __bf16*)H, (const __bf16*)W, y, mask, adv, ref_lp, N, L, d,
+                            V, beta, chunk, loss, lp, kl, lse, (char*)workspace, s);
+  return lse_pass<float>(1, (const float*)H, (const float*)W, y, mask, adv, ref_lp, N, L, d, V,
+                         beta, chunk, loss, lp, kl, lse, (char*)workspace, s);
+}
+
+int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                  const float* adv, const float* ref_lp, const float* lp, const float* lse,
+                  int64_t B, int64_t L, int64_t d, int64_t V, int dtype, float beta,
+                  float grad_loss, int64_t chunk, void* dH, float* dW, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  GRPO_CHECK_PTR(H);
+  GRPO_CHECK_PTR(W);
+  GRPO_CHECK_PTR(y);
+  GRPO_CHECK_PTR(mask);
+  GRPO_CHECK_PTR(adv);
+  GRPO_CHECK_PTR(ref_lp);
+  GRPO_CHECK_PTR(lp);
+  GRPO_CHECK_PTR(lse);
+  GRPO_CHECK_PTR(dH);
+  GRPO_CHECK_PTR(dW);
+  if (B <= 0 || L <= 0) return fail(GRPO_ERR_INVALID_ARG, "B and L must be positive");
+  if (B > INT32_MAX / L) return fail(GRPO_ERR_UNSUPPORTED, "B*L exceeds int32");
+  const int64_t N = B * L;
+  int st = check_shape(N, d, V, dtype, chunk);
+  if (st != GRPO_OK) return st;
+  if (!isfinite(beta)) return fail(GRPO_ERR_INVALID_ARG, "beta must be finite");
+  if (!isfinite(grad_loss)) return fail(GRPO_ERR_INVALID_ARG, "grad_loss must be finite");
+  const size_t need = plan_bwd(N, d, V, dtype, chunk).total;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GRPO_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GRPO_BF16)
+    return bwd_pass<__bf16>((const __bf16*)H, (const __bf16*)W, y, mask, adv, ref_lp, lp, lse, N,
+                            L, d, V, beta, grad_loss, chunk, (__bf16*)dH, dW, (char*)workspace,
+                            dtype, s);
+  return bwd_pass<float>((const float*)H, (const float*)W, y, mask, adv, ref_lp, lp, lse, N, L, d,
+                         V, beta, grad_loss, chunk, (float*)dH, dW, (char*)workspace, dtype, s);
+}
+
+int grpo_gemm_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int dtype,
+                 float* C, void* stream) {
+  g_last_error[0] = 0;
+  GRPO_CHECK_PTR(A);
+  GRPO_CHECK_PTR(B);
+  GRPO_CHECK_PTR(C);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(GRPO_ERR_INVALID_ARG, "M, N, K must be positive");
+  if (dtype != GRPO_F32 && dtype != GRPO_BF16)
+    return fail(GRPO_ERR_INVALID_ARG, "dtype %d is neither GRPO_F32 nor GRPO_BF16", dtype);
+  if ((K * (int64_t)esize(dtype)) % 16 != 0)
+    return fail(GRPO_ERR_UNSUPPORTED, "K * element size must be a multiple of 16 bytes");
+  if (256 * K * (int64_t)esize(dtype) >= (1ll << 31) || M > INT32_MAX || N > INT32_MAX)
+    return fail(GRPO_ERR_UNSUPPORTED, "shape too large");
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GRPO_BF16)
+    GRPO_HIP(grpo::launch_gemm_nt<__bf16>((const __bf16*)A, (const __bf16*)B, M, N, K, C, s));
+  else
+    GRPO_HIP(grpo::launch_gemm_nt<float>((const float*)A, (const float*)B, M, N, K, C, s));
+  return GRPO_OK;
+}
+
+int grpo_timing_begin(void) {
+  grpo::timing_begin();
+  return GRPO_OK;
+}
+
+int grpo_timing_end(const char** names, int* launches, double* total_ms, int max_entries) {
+  return grpo::timing_end(names, launches, total_ms, max_entries);
+}
+
+}  // extern "C"

@@ -1,0 +1,717 @@
+// kernels.hip -- HIP kernels of the fused chunked GRPO loss for gfx950.
+//
+// Forward (per chunk of flattened tokens):
+//   k_lse_partials: MFMA tile z^T = W_tile . H_tile^T (vocab rows x token
+//     columns), folded in registers into a (max, sum-exp) pair per token for
+//     that 256-row vocabulary tile, plus the target logit z[y] when the
+//     target falls in the tile.  Logits never leave registers.
+//   k_lse_merge: fixed-order merge of the per-tile pairs into lse and lp; in
+//     loss mode also kl and the masked per-block loss sums.
+//   k_loss_final: fixed-order sum of the block sums -> loss.
+// Backward (per chunk of ACTIVE tokens, per vocabulary slab):
+//   k_dz: the same tile recomputed; the epilogue forms
+//     dZ = c_t (onehot(y_t) - exp(z - lse_t)) in registers and stores it in
+//     H's dtype into a bounded [chunk x slab] buffer and its transpose.
+//   k_dh_gemm: dH_acc[t][:] (+)= sum_v dZ[t][v] W[v][:]   (MFMA, fp32 acc)
+//   k_dw_gemm: dW[v][:]     +=  sum_t dZ[t][v] h_t[:]     (MFMA, fp32 RMW)
+// Every reduction runs in a fixed order, so results are bitwise reproducible.
+#include <math.h>
+
+#include "kernels.hpp"
+#include "tile_mma.hpp"
+#include "timing.hpp"
+
+namespace grpo {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Online log-sum-exp pair combination in base e, carried as (max, sum of
+// exp(z - max)).  An empty side has max = -inf and sum = 0.
+__device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == kNegInf) {
+    s = 0.f;
+    m = M;
+    return;
+  }
+  s = s * ex2((m - M) * kLog2e) + s2 * ex2((m2 - M) * kLog2e);
+  m = M;
+}
+
+// Hardware dispatches workgroup b to XCD b % 8.  Remap so that XCD x
+// receives a contiguous range of logical tile ids, then order the logical
+// ids in groups of 4 M-tiles (M fastest), so the ~32 workgroups resident on
+// one XCD share 4 A-panels and ~8 B-panels in that XCD's L2.
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tm, int tn, int& mt,
+                                            int& nt) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int p = xcd * q + (xcd < r ? xcd : r) + slot;
+  constexpr int GM = 4;
+  const int per_group = GM * tn;
+  const int g = p / per_group;
+  const int first = g * GM;
+  const int gm = (tm - first) < GM ? (tm - first) : GM;
+  const int rem = p - g * per_group;
+  mt = first + rem % gm;
+  nt = rem / gm;
+}
+
+template <typename T>
+__device__ __forceinline__ T to_elem(float x);
+template <>
+__device__ __forceinline__ float to_elem<float>(float x) {
+  return x;
+}
+template <>
+__device__ __forceinline__ __bf16 to_elem<__bf16>(float x) {
+  return (__bf16)x;
+}
+
+// Store 4 consecutive values (16 B for f32, 8 B for bf16).
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  *(f32x4_t*)p = f32x4_t{a, b, c, d};
+}
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+  *(bf16x4_t*)p = bf16x4_t{(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------- advantages
+// One wave64 per group; sums in double, fixed order.
+__global__ void __launch_bounds__(64) k_advantages(const float* __restrict__ r, int64_t G,
+                                                   float eps, float* __restrict__ adv) {
+  const int64_t base = (int64_t)blockIdx.x * G;
+  const int lane = threadIdx.x;
+  double s = 0.0;
+  for (int64_t i = lane; i < G; i += 64) s += (double)r[base + i];
+  const double mean = wave_sum(s) / (double)G;
+  double q = 0.0;
+  for (int64_t i = lane; i < G; i += 64) {
+    const double dv = (double)r[base + i] - mean;
+    q += dv * dv;
+  }
+  q = wave_sum(q);
+  const double sd = G > 1 ? sqrt(q / (double)(G - 1)) : 0.0;
+  for (int64_t i = lane; i < G; i += 64)
+    adv[base + i] = (float)(((double)r[base + i] - mean) / (sd + (double)eps));
+}
+
+// ---------------------------------------------------------------- forward tile
+template <typename T>
+__global__ void __launch_bounds__(kThreads, 1)
+    k_lse_partials(const T* __restrict__ W, const T* __restrict__ H, const int32_t* __restrict__ y,
+                   int64_t V, int64_t d, int n_tok, int cpad, int tm, int tn,
+                   float* __restrict__ part_m, float* __restrict__ part_s,
+                   float* __restrict__ zy) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  char GRPO_LDS* lds = (char GRPO_LDS*)smem;
+  int mt, nt;
+  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  const int64_t m0 = (int64_t)mt * kBM;  // first vocab row
+  const int n0 = nt * kBN;               // first token (chunk-local)
+  const uint32_t rowb = (uint32_t)(d * (int64_t)sizeof(T));
+  const int mvalid = (int)((V - m0) < kBM ? (V - m0) : kBM);
+  const Operand A{(const char*)(W + m0 * d), rowb, mvalid, rowb};
+  const Operand B{(const char*)(H + (int64_t)n0 * d), rowb, n_tok - n0, rowb};
+
+  f32x16_t acc[4][4];
+  tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm0 = (wave >> 1) * 128;
+  const bool full = mvalid >= wm0 + 128;
+
+  float mx[4], sm[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (full || acc_row(wave, lane, i, e) < mvalid) m = fmaxf(m, acc[i][j][e]);
+    const float mb = m * kLog2e;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (full || acc_row(wave, lane, i, e) < mvalid) s += ex2(fmaf(acc[i][j][e], kLog2e, -mb));
+    mx[j] = m;
+    sm[j] = s;
+  }
+  // lanes l and l ^ 32 hold the same token column
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float om = __shfl_xor(mx[j], 32, 64);
+    const float os = __shfl_xor(sm[j], 32, 64);
+    lse_combine(mx[j], sm[j], om, os);
+  }
+
+  // target logit: exactly one lane of the grid holds z[t][y_t]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = n0 + acc_col(wave, lane, j);
+    if (t < n_tok) {
+      const int r = y[t] - (int)(m0 + wm0);
+      if (r >= 0 && r < 128 && r < mvalid - wm0 && ((r >> 2) & 1) == (lane >> 5)) {
+        const int ti = r >> 5, te = ((r >> 3) & 3) * 4 + (r & 3);
+        float v = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (i == ti && e == te) v = acc[i][j][e];
+        zy[t] = v;
+      }
+    }
+  }
+
+  // combine the two waves that share token columns, through LDS
+  __syncthreads();
+  float* red = (float*)smem;  // [2 column halves][128] max, then sums
+  if ((wave >> 1) == 1 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      red[(wave & 1) * 128 + 32 * j + lane] = mx[j];
+      red[256 + (wave & 1) * 128 + 32 * j + lane] = sm[j];
+    }
+  }
+  __syncthreads();
+  if ((wave >> 1) == 0 && lane < 32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = (wave & 1) * 128 + 32 * j + lane;
+      float m = mx[j], s = sm[j];
+      lse_combine(m, s, red[c], red[256 + c]);
+      const int t = n0 + c;
+      if (t < n_tok) {
+        part_m[(int64_t)mt * cpad + t] = m;
+        part_s[(int64_t)mt * cpad + t] = s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- forward merge
+__global__ void __launch_bounds__(256)
+    k_lse_merge(int mode, const float* __restrict__ part_m, const float* __restrict__ part_s,
+                const float* __restrict__ zy, int S, int cpad, int n_tok, int64_t c0,
+                const int32_t* __restrict__ y, int64_t V, float* __restrict__ out_lp,
+                float* __restrict__ out_lse, float* __restrict__ out_kl,
+                const float* __restrict__ ref_lp, const uint8_t* __restrict__ mask,
+                const float* __restrict__ adv, int64_t L, float beta, double* loss_part,
+                int* cnt_part, int part0) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  double ml = 0.0;
+  int cnt = 0;
+  if (t < n_tok) {
+    float M = kNegInf, Ssum = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float m = part_m[(int64_t)s * cpad + t];
+      const float v = part_s[(int64_t)s * cpad + t];
+      if (m > M) {
+        Ssum = Ssum * exp2f((M - m) * kLog2e) + v;
+        M = m;
+      } else {
+        Ssum += v * exp2f((m - M) * kLog2e);
+      }
+    }
+    const float lse = M + logf(Ssum);
+    const int64_t tg = c0 + t;
+    const int32_t yt = y[tg];
+    const float lp = (yt >= 0 && yt < V) ? zy[t] - lse : __builtin_nanf("");
+    out_lp[tg] = lp;
+    if (mode == 1) {
+      out_lse[tg] = lse;
+      const float x = ref_lp[tg] - lp;
+      const float kl = expm1f(x) - x;
+      out_kl[tg] = kl;
+      if (mask[tg] != 0) {
+        const float ell = -(adv[tg / L] - beta * kl);
+        ml = (double)ell;
+        cnt = 1;
+      }
+    }
+  }
+  if (mode == 1) {
+    __shared__ double sml[4];
+    __shared__ int scnt[4];
+    ml = wave_sum(ml);
+    cnt = wave_sum(cnt);
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+      sml[wave] = ml;
+      scnt[wave] = cnt;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      loss_part[part0 + blockIdx.x] = ((sml[0] + sml[1]) + sml[2]) + sml[3];
+      cnt_part[part0 + blockIdx.x] = scnt[0] + scnt[1] + scnt[2] + scnt[3];
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256)
+    k_loss_final(const double* __restrict__ loss_part, const int* __restrict__ cnt_part,
+                 int nparts, float* __restrict__ loss) {
+  double s = 0.0;
+  long long c = 0;
+  for (int i = threadIdx.x; i < nparts; i += 256) {
+    s += loss_part[i];
+    c += cnt_part[i];
+  }
+  __shared__ double ss[256];
+  __shared__ long long sc[256];
+  ss[threadIdx.x] = s;
+  sc[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = 128; w >= 1; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      ss[threadIdx.x] += ss[threadIdx.x + w];
+      sc[threadIdx.x] += sc[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) loss[0] = (float)(ss[0] / (double)(sc[0] > 0 ? sc[0] : 1));
+}
+
+// ---------------------------------------------------------------- backward helpers
+// Indices of the unmasked tokens in increasing order, and their count.
+__global__ void __launch_bounds__(1024)
+    k_active_scan(const uint8_t* __restrict__ mask, int64_t N, int32_t* __restrict__ idx,
+                  int32_t* __restrict__ count) {
+  __shared__ int sc[1024];
+  const int tid = threadIdx.x;
+  const int64_t seg = (N + 1023) / 1024;
+  const int64_t b = tid * seg;
+  const int64_t e = (b + seg) < N ? (b + seg) : N;
+  int c = 0;
+  for (int64_t i = b; i < e; ++i) c += mask[i] != 0;
+  sc[tid] = c;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive Hillis-Steele scan
+    const int v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  int off = sc[tid] - c;
+  for (int64_t i = b; i < e; ++i)
+    if (mask[i] != 0) idx[off++] = (int32_t)i;
+  if (tid == 1023) count[0] = sc[1023];
+}
+
+// out[c][r] = in[r][c] for r < R; out[c][r] = 0 for R <= r < Rpad.
+template <typename T>
+__global__ void __launch_bounds__(256)
+    k_transpose(const T* __restrict__ in, int64_t R, int64_t Cc, T* __restrict__ out,
+                int64_t Rpad) {
+  __shared__ T tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t rr = r0 + r, cc = c0 + tx;
+    tile[r][tx] = (rr < R && cc < Cc) ? in[rr * Cc + cc] : to_elem<T>(0.f);
+  }
+  __syncthreads();
+  for (int c = ty; c < 64; c += 4) {
+    const int64_t cc = c0 + c, rr = r0 + tx;
+    if (cc < Cc && rr < Rpad) out[cc * Rpad + rr] = tile[tx][c];
+  }
+}
+
+// Gather the hidden states of chunk c's active tokens into H_act and form
+// the per-token backward coefficient c_t, lse and target; padding rows are 0.
+template <typename T>
+__global__ void __launch_bounds__(256)
+    k_bwd_prep(const T* __restrict__ H, int64_t d, const int32_t* __restrict__ idx,
+               const int32_t* __restrict__ count, int64_t c0, int C,
+               const int32_t* __restrict__ y, const float* __restrict__ adv,
+               const float* __restrict__ ref_lp, const float* __restrict__ lp,
+               const float* __restrict__ lse, int64_t L, float beta, float grad_loss,
+               T* __restrict__ H_act, float* __restrict__ coef, float* __restrict__ lse_c,
+               int32_t* __restrict__ y_c) {
+  const int cnt = count[0];
+  if (c0 >= cnt) return;
+  const int j = blockIdx.x;
+  const bool valid = j < C && c0 + j < cnt;
+  const int64_t t = valid ? idx[c0 + j] : 0;
+  const int nvec = (int)(d * (int64_t)sizeof(T) / 16);
+  const int4* src = (const int4*)(H + t * d);
+  int4* dst = (int4*)(H_act + (int64_t)j * d);
+  for (int v = threadIdx.x; v < nvec; v += 256) dst[v] = valid ? src[v] : int4{0, 0, 0, 0};
+  if (threadIdx.x == 0) {
+    if (valid) {
+      const float x = ref_lp[t] - lp[t];
+      const float scale = grad_loss / (float)(cnt > 0 ? cnt : 1);
+      coef[j] = scale * (-adv[t / L] - beta * expm1f(x));
+      lse_c[j] = lse[t];
+      y_c[j] = y[t];
+    } else {
+      coef[j] = 0.f;
+      lse_c[j] = 0.f;
+      y_c[j] = -1;
+    }
+  }
+}
+
+// ---------------------------------------------------------------- backward tiles
+template <typename T>
+__global__ void __launch_bounds__(kThreads, 1)
+    k_dz(const T* __restrict__ W, const T* __restrict__ H_act, int64_t d, int64_t v0,
+         int vs_valid, int vs, const int32_t* __restrict__ count, int64_t c0, int C, int cpad,
+         int tm, int tn, const float* __restrict__ coef, const float* __restrict__ lse_c,
+         const int32_t* __restrict__ y_c, T* __restrict__ dZ, T* __restrict__ dZT) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  char GRPO_LDS* lds = (char GRPO_LDS*)smem;
+  int n_act = count[0] - (int)c0;
+  n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
+  int mt, nt;
+  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  const int n0 = nt * kBN;
+  if (n0 >= n_act) return;
+  const int m0 = mt * kBM;
+  const uint32_t rowb = (uint32_t)(d * (int64_t)sizeof(T));
+  const Operand A{(const char*)(W + (v0 + m0) * d), rowb, vs_valid - m0, rowb};
+  const Operand B{(const char*)(H_act + (int64_t)n0 * d), rowb, n_act - n0, rowb};
+  f32x16_t acc[4][4];
+  tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = n0 + acc_col(wave, lane, j);
+    const float ct = coef[t];
+    const float lb = lse_c[t] * kLog2e;
+    const int64_t yl = (int64_t)y_c[t] - v0;  // target relative to the slab
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int v = m0 + acc_row(wave, lane, i, 4 * g);
+        float q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float p = ex2(fmaf(acc[i][j][4 * g + u], kLog2e, -lb));
+          const float onehot = (v + u) == yl ? 1.f : 0.f;
+          q[u] = (v + u) < vs_valid ? ct * (onehot - p) : 0.f;
+        }
+        store4(dZ + (int64_t)t * vs + v, q[0], q[1], q[2], q[3]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) dZT[(int64_t)(v + u) * cpad + t] = to_elem<T>(q[u]);
+      }
+    }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads, 1)
+    k_dh_gemm(const T* __restrict__ WT, int64_t vpad, int64_t v0, int vs_valid,
+              const T* __restrict__ dZ, int vs, int64_t d, const int32_t* __restrict__ count,
+              int64_t c0, int C, int tm, int tn, int first, float* __restrict__ dH_acc) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  char GRPO_LDS* lds = (char GRPO_LDS*)smem;
+  int n_act = count[0] - (int)c0;
+  n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
+  int mt, nt;
+  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  const int n0 = nt * kBN;
+  if (n0 >= n_act) return;
+  const int64_t m0 = (int64_t)mt * kBM;
+  const uint32_t kb = (uint32_t)(((int64_t)vs_valid * (int64_t)sizeof(T) + 15) & ~(int64_t)15);
+  const Operand A{(const char*)(WT + m0 * vpad + v0), (uint32_t)(vpad * (int64_t)sizeof(T)),
+                  (int)((d - m0) < kBM ? (d - m0) : kBM), kb};
+  const Operand B{(const char*)(dZ + (int64_t)n0 * vs), (uint32_t)(vs * (int64_t)sizeof(T)),
+                  n_act - n0, kb};
+  f32x16_t acc[4][4];
+  tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = n0 + acc_col(wave, lane, j);
+    if (t >= n_act) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t nd = m0 + acc_row(wave, lane, i, 4 * g);
+        if (nd >= d) continue;
+        f32x4_t* p = (f32x4_t*)(dH_acc + (int64_t)t * d + nd);
+        f32x4_t v{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                  acc[i][j][4 * g + 3]};
+        if (!first) v += *p;
+        *p = v;
+      }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads, 1)
+    k_dw_gemm(const T* __restrict__ HT, int cpad, const T* __restrict__ dZT, int64_t d,
+              int64_t v0, int vs_valid, const int32_t* __restrict__ count, int64_t c0, int C,
+              int tm, int tn, float* __restrict__ dW) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  char GRPO_LDS* lds = (char GRPO_LDS*)smem;
+  int n_act = count[0] - (int)c0;
+  n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
+  if (n_act <= 0) return;
+  int mt, nt;
+  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  const int64_t m0 = (int64_t)mt * kBM;
+  const int n0 = nt * kBN;
+  const uint32_t kb = (uint32_t)(((int64_t)n_act * (int64_t)sizeof(T) + 15) & ~(int64_t)15);
+  const uint32_t ldb = (uint32_t)(cpad * (int64_t)sizeof(T));
+  const Operand A{(const char*)(HT + m0 * cpad), ldb, (int)((d - m0) < kBM ? (d - m0) : kBM), kb};
+  const Operand B{(const char*)(dZT + (int64_t)n0 * cpad), ldb, vs_valid - n0, kb};
+  f32x16_t acc[4][4];
+  tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int v = n0 + acc_col(wave, lane, j);
+    if (v >= vs_valid) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int64_t nd = m0 + acc_row(wave, lane, i, 4 * g);
+        if (nd >= d) continue;
+        f32x4_t* p = (f32x4_t*)(dW + (v0 + v) * d + nd);
+        *p += f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                      acc[i][j][4 * g + 3]};
+      }
+  }
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+    k_dh_scatter(const float* __restrict__ dH_acc, int64_t d, const int32_t* __restrict__ idx,
+                 const int32_t* __restrict__ count, int64_t c0, int C, T* __restrict__ dH) {
+  int n_act = count[0] - (int)c0;
+  n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
+  const int j = blockIdx.x;
+  if (j >= n_act) return;
+  const int64_t t = idx[c0 + j];
+  for (int64_t k = threadIdx.x * 4; k < d; k += 1024) {
+    const f32x4_t v = *(const f32x4_t*)(dH_acc + (int64_t)j * d + k);
+    store4(dH + t * d + k, v[0], v[1], v[2], v[3]);
+  }
+}
+
+__global__ void __launch_bounds__(256) k_zero(int4* __restrict__ p, int64_t n16, char* tail,
+                                              int ntail) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride)
+    p[i] = int4{0, 0, 0, 0};
+  if (blockIdx.x == 0 && (int)threadIdx.x < ntail) tail[threadIdx.x] = 0;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads, 1)
+    k_gemm_nt(const T* __restrict__ A, const T* __restrict__ B, int64_t M, int64_t N, int64_t K,
+              int tm, int tn, float* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  char GRPO_LDS* lds = (char GRPO_LDS*)smem;
+  int mt, nt;
+  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  const int64_t m0 = (int64_t)mt * kBM, n0 = (int64_t)nt * kBN;
+  const uint32_t rowb = (uint32_t)(K * (int64_t)sizeof(T));
+  const Operand Ao{(const char*)(A + m0 * K), rowb, (int)((M - m0) < kBM ? (M - m0) : kBM), rowb};
+  const Operand Bo{(const char*)(B + n0 * K), rowb, (int)((N - n0) < kBN ? (N - n0) : kBN), rowb};
+  f32x16_t acc[4][4];
+  tile_mainloop<T>(acc, Ao, Bo, (int)((rowb + kBKB - 1) / kBKB), lds);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + acc_row(wave, lane, i, e), n = n0 + acc_col(wave, lane, j);
+        if (m < M && n < N) C[m * N + n] = acc[i][j][e];
+      }
+}
+
+inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_advantages(const float* rewards, int64_t groups, int64_t G, float eps,
+                             float* adv, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_ADVANTAGES, s);
+  hipLaunchKernelGGL(k_advantages, dim3((unsigned)groups), dim3(64), 0, s, rewards, G, eps, adv);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_lse_partials(const T* W, const T* H, const int32_t* y, int64_t V, int64_t d,
+                               int n_tok, int cpad, float* part_m, float* part_s, float* zy,
+                               hipStream_t s) {
+  ScopedKernelTimer timer_(KK_LSE_PARTIALS, s);
+  const int tm = cdiv(V, kBM), tn = cdiv(n_tok, kBN);
+  hipLaunchKernelGGL(k_lse_partials<T>, dim3(tm * tn), dim3(kThreads), 0, s, W, H, y, V, d, n_tok,
+                     cpad, tm, tn, part_m, part_s, zy);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_merge(int mode, const float* part_m, const float* part_s, const float* zy,
+                            int S, int cpad, int n_tok, int64_t c0, const int32_t* y, int64_t V,
+                            float* out_lp, float* out_lse, float* out_kl, const float* ref_lp,
+                            const uint8_t* mask, const float* adv, int64_t L, float beta,
+                            double* loss_part, int* cnt_part, int part0, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_LSE_MERGE, s);
+  hipLaunchKernelGGL(k_lse_merge, dim3(cdiv(n_tok, 256)), dim3(256), 0, s, mode, part_m, part_s,
+                     zy, S, cpad, n_tok, c0, y, V, out_lp, out_lse, out_kl, ref_lp, mask, adv, L,
+                     beta, loss_part, cnt_part, part0);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_final(const double* loss_part, const int* cnt_part, int nparts, float* loss,
+                             hipStream_t s) {
+  ScopedKernelTimer timer_(KK_LOSS_FINAL, s);
+  hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, s, loss_part, cnt_part, nparts, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_active_scan(const uint8_t* mask, int64_t N, int32_t* idx, int32_t* count,
+                              hipStream_t s) {
+  ScopedKernelTimer timer_(KK_ACTIVE_SCAN, s);
+  hipLaunchKernelGGL(k_active_scan, dim3(1), dim3(1024), 0, s, mask, N, idx, count);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_transpose(const T* in, int64_t R, int64_t Cc, T* out, int64_t Rpad,
+                            hipStream_t s) {
+  ScopedKernelTimer timer_(KK_TRANSPOSE, s);
+  hipLaunchKernelGGL(k_transpose<T>, dim3(cdiv(Rpad, 64), cdiv(Cc, 64)), dim3(256), 0, s, in, R,
+                     Cc, out, Rpad);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int32_t* count,
+                           int64_t c0, int C, int cpad, const int32_t* y, const uint8_t* mask,
+                           const float* adv, const float* ref_lp, const float* lp,
+                           const float* lse, int64_t L, float beta, float grad_loss, T* H_act,
+                           float* coef, float* lse_c, int32_t* y_c, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_BWD_PREP, s);
+  (void)mask;
+  hipLaunchKernelGGL(k_bwd_prep<T>, dim3(cpad), dim3(256), 0, s, H, d, idx, count, c0, C, y, adv,
+                     ref_lp, lp, lse, L, beta, grad_loss, H_act, coef, lse_c, y_c);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,
+                     int vs, const int32_t* count, int64_t c0, int C, int cpad, const float* coef,
+                     const float* lse_c, const int32_t* y_c, T* dZ, T* dZT, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_DZ, s);
+  (void)V;
+  const int tm = cdiv(vs_valid, kBM), tn = cdiv(C, kBN);
+  hipLaunchKernelGGL(k_dz<T>, dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0, vs_valid, vs,
+                     count, c0, C, cpad, tm, tn, coef, lse_c, y_c, dZ, dZT);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dh_gemm(const T* WT, int64_t vpad, int64_t v0, int vs_valid, const T* dZ, int vs,
+                          int64_t d, const int32_t* count, int64_t c0, int C, int cpad,
+                          int first, float* dH_acc, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_DH_GEMM, s);
+  (void)cpad;
+  const int tm = cdiv(d, kBM), tn = cdiv(C, kBN);
+  hipLaunchKernelGGL(k_dh_gemm<T>, dim3(tm * tn), dim3(kThreads), 0, s, WT, vpad, v0, vs_valid, dZ,
+                     vs, d, count, c0, C, tm, tn, first, dH_acc);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZT, int64_t d, int64_t V, int64_t v0,
+                          int vs_valid, const int32_t* count, int64_t c0, int C, float* dW,
+                          hipStream_t s) {
+  ScopedKernelTimer timer_(KK_DW_GEMM, s);
+  (void)V;
+  const int tm = cdiv(d, kBM), tn = cdiv(vs_valid, kBN);
+  hipLaunchKernelGGL(k_dw_gemm<T>, dim3(tm * tn), dim3(kThreads), 0, s, HT, cpad, dZT, d, v0,
+                     vs_valid, count, c0, C, tm, tn, dW);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dh_scatter(const float* dH_acc, int64_t d, const int32_t* idx,
+                             const int32_t* count, int64_t c0, int C, T* dH, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_DH_SCATTER, s);
+  hipLaunchKernelGGL(k_dh_scatter<T>, dim3(C), dim3(256), 0, s, dH_acc, d, idx, count, c0, C, dH);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_ZERO, s);
+  if (bytes == 0) return hipSuccess;
+  const int64_t n16 = (int64_t)(bytes / 16);
+  const int ntail = (int)(bytes % 16);
+  int blocks = (int)((n16 + 255) / 256);
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_zero, dim3(blocks), dim3(256), 0, s, (int4*)p, n16,
+                     (char*)p + n16 * 16, ntail);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t K, float* C,
+                          hipStream_t s) {
+  ScopedKernelTimer timer_(KK_GEMM_NT, s);
+  const int tm = cdiv(M, kBM), tn = cdiv(N, kBN);
+  hipLaunchKernelGGL(k_gemm_nt<T>, dim3(tm * tn), dim3(kThreads), 0, s, A, B, M, N, K, tm, tn, C);
+  return hipGetLastError();
+}
+
+#define GRPO_INSTANTIATE(T)                                                                       \
+  template hipError_t launch_lse_partials<T>(const T*, const T*, const int32_t*, int64_t,         \
+                                             int64_t, int, int, float*, float*, float*,           \
+                                             hipStream_t);                                        \
+  template hipError_t launch_transpose<T>(const T*, int64_t, int64_t, T*, int64_t, hipStream_t);  \
+  template hipError_t launch_bwd_prep<T>(const T*, int64_t, const int32_t*, const int32_t*,       \
+                                         int64_t, int, int, const int32_t*, const uint8_t*,        \
+                                         const float*, const float*, const float*, const float*,  \
+                                         int64_t, float, float, T*, float*, float*, int32_t*,      \
+                                         hipStream_t);                                            \
+  template hipError_t launch_dz<T>(const T*, const T*, int64_t, int64_t, int64_t, int, int,       \
+                                   const int32_t*, int64_t, int, int, const float*, const float*, \
+                                   const int32_t*, T*, T*, hipStream_t);                          \
+  template hipError_t launch_dh_gemm<T>(const T*, int64_t, int64_t, int, const T*, int, int64_t,  \
+                                        const int32_t*, int64_t, int, int, int, float*,           \
+                                        hipStream_t);                                             \
+  template hipError_t launch_dw_gemm<T>(const T*, int, const T*, int64_t, int64_t, int64_t, int,  \
+                                        const int32_t*, int64_t, int, float*, hipStream_t);       \
+  template hipError_t launch_dh_scatter<T>(const float*, int64_t, const int32_t*, const int32_t*, \
+                                           int64_t, int, T*, hipStream_t);                        \
+  template hipError_t launch_gemm_nt<T>(const T*, const T*, int64_t, int64_t, int64_t, float*,    \
+                                        hipStream_t);
+
+GRPO_INSTANTIATE(float)
+GRPO_INSTANTIATE(__bf16)
+
+}  // namespace grpo

@@ -1,0 +1,77 @@
+// kernels.hpp -- host-side launchers of the HIP kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace grpo {
+
+// Logical tile grid of one GEMM-shaped launch.
+struct Grid2 {
+  int tm;  // tiles along M (A rows)
+  int tn;  // tiles along N (B rows)
+};
+
+hipError_t launch_advantages(const float* rewards, int64_t groups, int64_t G, float eps,
+                             float* adv, hipStream_t s);
+
+// Forward: per-(vocab tile, token) online-LSE partials and the target logit
+// for the tokens [0, n_tok) of one chunk whose hidden states start at H.
+template <typename T>
+hipError_t launch_lse_partials(const T* W, const T* H, const int32_t* y, int64_t V, int64_t d,
+                               int n_tok, int cpad, float* part_m, float* part_s, float* zy,
+                               hipStream_t s);
+
+// Merge the partials of one chunk (tokens c0 .. c0 + n_tok - 1).
+// mode 0: reference log-probs -> out_lp.  mode 1: loss forward.
+hipError_t launch_lse_merge(int mode, const float* part_m, const float* part_s, const float* zy,
+                            int S, int cpad, int n_tok, int64_t c0, const int32_t* y, int64_t V,
+                            float* out_lp, float* out_lse, float* out_kl, const float* ref_lp,
+                            const uint8_t* mask, const float* adv, int64_t L, float beta,
+                            double* loss_part, int* cnt_part, int part0, hipStream_t s);
+
+hipError_t launch_loss_final(const double* loss_part, const int* cnt_part, int nparts, float* loss,
+                             hipStream_t s);
+
+// Backward helpers.
+hipError_t launch_active_scan(const uint8_t* mask, int64_t N, int32_t* idx, int32_t* count,
+                              hipStream_t s);
+
+template <typename T>
+hipError_t launch_transpose(const T* in, int64_t R, int64_t Cc, T* out, int64_t Rpad,
+                            hipStream_t s);
+
+template <typename T>
+hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int32_t* count,
+                           int64_t c0, int C, int cpad, const int32_t* y, const uint8_t* mask,
+                           const float* adv, const float* ref_lp, const float* lp,
+                           const float* lse, int64_t L, float beta, float grad_loss, T* H_act,
+                           float* coef, float* lse_c, int32_t* y_c, hipStream_t s);
+
+template <typename T>
+hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,
+                     int vs, const int32_t* count, int64_t c0, int C, int cpad, const float* coef,
+                     const float* lse_c, const int32_t* y_c, T* dZ, T* dZT, hipStream_t s);
+
+template <typename T>
+hipError_t launch_dh_gemm(const T* WT, int64_t vpad, int64_t v0, int vs_valid, const T* dZ, int vs,
+                          int64_t d, const int32_t* count, int64_t c0, int C, int cpad,
+                          int first, float* dH_acc, hipStream_t s);
+
+template <typename T>
+hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZT, int64_t d, int64_t V, int64_t v0,
+                          int vs_valid, const int32_t* count, int64_t c0, int C, float* dW,
+                          hipStream_t s);
+
+template <typename T>
+hipError_t launch_dh_scatter(const float* dH_acc, int64_t d, const int32_t* idx,
+                             const int32_t* count, int64_t c0, int C, T* dH, hipStream_t s);
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+// Plain tile GEMM C[m][n] = sum_k A[m][k] B[n][k] into float32 C (diagnostic).
+template <typename T>
+hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t K, float* C,
+                          hipStream_t s);
+
+}  // namespace grpo

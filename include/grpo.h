@@ -1,0 +1,176 @@
+/*
+ * grpo.h -- C ABI of the fused, chunked GRPO policy loss for AMD MI355X (gfx950).
+ *
+ * What it computes (sources: Unsloth "Long-context GRPO" blog, Chinese
+ * translation at zjt100.com, section on the GRPO maths; Unsloth docs "GRPO
+ * with 7x longer context", sections "Flattened sequence length chunking" and
+ * "Offloading activations for log softmax"; aibit.im "Mastering GRPO",
+ * section "From RLHF and PPO to the efficiency of GRPO"):
+ *
+ *   tokens   t = b*L + j over B sequences of padded length L (N = B*L)
+ *   logits   z_t = W h_t              W: [V, d] LM head, h_t: row t of H [N, d]
+ *   lse_t    = log sum_v exp(z_tv)     (max-shifted, float32 or better)
+ *   lp_t     = z_{t, y_t} - lse_t      selective log-softmax at the target id
+ *   x_t      = ref_lp_t - lp_t
+ *   kl_t     = exp(x_t) - x_t - 1      reverse KL, no extra policy factor
+ *   l_t      = -(exp(lp_t - stopgrad(lp_t)) * A_{b(t)} - beta * kl_t)
+ *              (the ratio's value is 1; its gradient is that of lp_t)
+ *   loss     = sum_t m_t l_t / max(sum_t m_t, 1)   masked token mean
+ *
+ * and the backward of that loss, which recomputes every logit tile instead
+ * of keeping a (tokens x vocab) tensor:
+ *   c_t  = g * m_t / max(sum m, 1) * (-A_{b(t)} + beta * (1 - exp(x_t)))
+ *   dZ_t = c_t * (onehot(y_t) - softmax(z_t))
+ *   dH_t = dZ_t W            dW += sum_t dZ_t^T h_t
+ *
+ * Conventions shared by every call:
+ *  - Every pointer argument is a DEVICE pointer unless stated otherwise, to a
+ *    dense row-major array owned by the caller.  The library allocates no
+ *    memory and keeps no state between calls beyond its loaded code objects.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work and return; nothing is synchronised on the host.
+ *  - `dtype` (grpo_dtype) gives the element type of H, H_ref, W and dH
+ *    together: GRPO_F32 (float) or GRPO_BF16 (bfloat16).  Logits, log-sum-exp
+ *    and every per-token output are float32; dW is always float32.
+ *  - Return value: GRPO_OK or a negative grpo_status.  Argument errors are
+ *    detected on the host before anything is enqueued; no output is touched
+ *    then.  GRPO_ERR_HIP means a launch failed and the outputs are undefined.
+ *    grpo_last_error() returns a thread-local text describing the last
+ *    failure.
+ *  - Device-side preconditions not checked on the host: targets y in
+ *    [0, V) (an out-of-range target gives lp = NaN in the forward and an
+ *    undefined gradient), mask values in {0, 1}, and no aliasing between
+ *    inputs and outputs.
+ *  - Shape limits: d must be a multiple of 8 (bf16) or 4 (f32) so that rows
+ *    load as 16-byte vectors; N, d, V, chunk >= 1.
+ */
+#ifndef GRPO_H
+#define GRPO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GRPO_F32 = 0, GRPO_BF16 = 1 } grpo_dtype;
+
+typedef enum {
+  GRPO_OK = 0,
+  GRPO_ERR_INVALID_ARG = -1, /* null pointer, size <= 0, N != B*L, bad dtype, non-finite beta */
+  GRPO_ERR_WORKSPACE = -2,   /* workspace pointer null or smaller than grpo_workspace_bytes() */
+  GRPO_ERR_UNSUPPORTED = -3, /* shape outside the limits above */
+  GRPO_ERR_HIP = -4          /* a HIP launch or runtime call failed */
+} grpo_status;
+
+typedef enum { GRPO_OP_REF = 0, GRPO_OP_FWD = 1, GRPO_OP_BWD = 2 } grpo_op;
+
+/*
+ * Workspace bytes that grpo_ref_logprobs (op = GRPO_OP_REF), grpo_loss_fwd
+ * (GRPO_OP_FWD) or grpo_loss_bwd (GRPO_OP_BWD) needs for these sizes.  The
+ * workspace is caller-owned device memory with 256-byte alignment; its
+ * contents on entry do not matter and are clobbered.  Returns 0 for invalid
+ * arguments.  It never scales with N*V: the forward keeps only per-token
+ * split partials of one chunk, the backward one bounded [chunk x V_s] slab
+ * of dZ (and its transpose), a transposed copy of W and one chunk of hidden
+ * states.
+ */
+size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk);
+
+/*
+ * Group-relative advantages (aibit.im "Mastering GRPO", section "From RLHF
+ * and PPO to the efficiency of GRPO": several completions per prompt are
+ * scored and the advantage is derived from the group's rewards).
+ *   rewards [num_groups * group_size] float32, group-major (group p holds
+ *           entries p*group_size .. p*group_size + group_size - 1)
+ *   adv     [num_groups * group_size] float32, written:
+ *           adv = (r - mean_p) / (std_p + eps), std with divisor n - 1;
+ *           a group of one has std 0 (so adv = 0).  NaN rewards propagate
+ *           to their own group only.
+ */
+int grpo_advantages(const float* rewards, int64_t num_groups, int64_t group_size, float eps,
+                    float* adv, void* stream);
+
+/*
+ * Reference-policy log-probabilities, no gradient (Unsloth blog, GRPO maths:
+ * P is the frozen reference model in the reverse-KL term).
+ *   H_ref [N, d] dtype; W [V, d] dtype; y [N] int32 target ids.
+ *   ref_lp [N] float32, written: log softmax(W h_t)[y_t] for every token.
+ *   chunk: flattened tokens per launch (>= 1); the result does not depend on it.
+ * Uses exactly the same kernels as grpo_loss_fwd, so H_ref == H gives
+ * ref_lp bitwise equal to lp, hence kl == 0 exactly.
+ */
+int grpo_ref_logprobs(const void* H_ref, const void* W, const int32_t* y, int64_t N, int64_t d,
+                      int64_t V, int dtype, int64_t chunk, float* ref_lp, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/*
+ * Forward of the masked token-mean GRPO loss over N = B*L flattened tokens
+ * (Unsloth docs, "Flattened sequence length chunking": the (batch x context)
+ * axis is flattened and processed `chunk` tokens at a time; no logits are
+ * ever written to memory, each vocabulary tile is folded into an online
+ * log-sum-exp in registers).
+ *   H [N, d] dtype; W [V, d] dtype; y [N] int32; mask [N] uint8 (0/1);
+ *   adv [B] float32 (one advantage per sequence); ref_lp [N] float32.
+ *   beta: KL weight (0.04 in the pages' setting), finite.
+ *   loss [1] float32, written.
+ *   lp, kl, lse [N] float32, written for every token, masked or not
+ *   (kl unscaled by beta; lse is what grpo_loss_bwd needs back).
+ */
+int grpo_loss_fwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                  const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
+                  int64_t V, int dtype, float beta, int64_t chunk, float* loss, float* lp,
+                  float* kl, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of grpo_loss_fwd's loss with upstream gradient grad_loss (Unsloth
+ * docs, "Offloading activations for log softmax": the backward recomputes
+ * the chunk's logits rather than keeping them from the forward).  Only
+ * unmasked tokens are visited (masked tokens have zero gradient).
+ *   H, W, y, mask, adv, ref_lp as in grpo_loss_fwd; lp and lse [N] float32
+ *   are the forward's outputs for the same inputs.
+ *   dH [N, d] dtype, OVERWRITTEN (rows of masked tokens become 0).
+ *   dW [V, d] float32, ACCUMULATED (+=): the caller zeroes it first for a
+ *   plain gradient.
+ */
+int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                  const float* adv, const float* ref_lp, const float* lp, const float* lse,
+                  int64_t B, int64_t L, int64_t d, int64_t V, int dtype, float beta,
+                  float grad_loss, int64_t chunk, void* dH, float* dW, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * Diagnostic: C[M, N] (float32, row-major, written) = A[M, K] . B[N, K]^T,
+ * through the same MFMA tile main loop the loss kernels use (A, B dtype
+ * elements, both rows contiguous along K).  K times the element size must be
+ * a multiple of 16 bytes.  Used by the parity tests to check that loop on
+ * its own; not part of the loss itself.
+ */
+int grpo_gemm_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int dtype,
+                 float* C, void* stream);
+
+/*
+ * Diagnostics: per-kernel timing with HIP events, off by default.  After
+ * grpo_timing_begin(), every kernel launch that this thread's library calls
+ * enqueue is bracketed by two HIP events recorded on the launch's own stream.
+ * grpo_timing_end() waits for those events and writes, for each kernel that
+ * ran, its name (static string), launch count and summed elapsed time in
+ * milliseconds into the caller's HOST arrays of max_entries; it returns the
+ * number of kernels that ran (entries past max_entries are dropped) and
+ * switches timing off.  Used by the benchmark for its roofline figure.
+ */
+int grpo_timing_begin(void);
+int grpo_timing_end(const char** names, int* launches, double* total_ms, int max_entries);
+
+/* Static text for a grpo_status code. */
+const char* grpo_strerror(int code);
+
+/* Thread-local text describing the most recent failure on this thread ("" if none). */
+const char* grpo_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GRPO_H */

@@ -1,0 +1,122 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/grpo.h declares, sizes workspaces sanely, and rejects bad
+arguments on the host before anything is enqueued (no compute call is made
+with valid arguments here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "grpo.h")
+
+gp = pytest.importorskip("grpo_policy_loss_amd")
+from grpo_policy_loss_amd import _lib  # noqa: E402
+
+if not os.path.exists(_lib.LIB_PATH):
+    pytest.skip("libgrpo.so not built", allow_module_level=True)
+
+L = _lib.lib()
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(grpo_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = declared_functions()
+    for n in ["grpo_advantages", "grpo_ref_logprobs", "grpo_loss_fwd", "grpo_loss_bwd",
+              "grpo_workspace_bytes", "grpo_strerror", "grpo_last_error", "grpo_gemm_nt"]:
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    for n in declared_functions():
+        assert hasattr(L, n), n
+        assert n in _lib.SIGNATURES, f"binding lacks a signature for {n}"
+
+
+def test_strerror_texts():
+    for code in [0, -1, -2, -3, -4, 7]:
+        assert L.grpo_strerror(code)
+
+
+@pytest.mark.parametrize("op", [0, 1, 2])
+def test_workspace_bytes_bounded_and_independent_of_N_times_V(op):
+    # long-context shape: 163840 tokens, V 128256, d 4096, chunk 8192
+    N, d, V, chunk = 163840, 4096, 128256, 8192
+    ws = L.grpo_workspace_bytes(op, N, d, V, 1, chunk)
+    assert ws > 0
+    assert ws < N * V * 2 / 10           # far below one bf16 (tokens x vocab) tensor
+    if op == 2:
+        # grows with N only through the active-index list (4 B per token)
+        ws2 = L.grpo_workspace_bytes(op, 2 * N, d, V, 1, chunk)
+        assert ws2 - ws <= 4 * N + 512
+
+
+def test_workspace_bytes_rejects_bad_shapes():
+    assert L.grpo_workspace_bytes(1, 0, 256, 1024, 0, 128) == 0
+    assert L.grpo_workspace_bytes(1, 512, 255, 1024, 0, 128) == 0      # d not multiple of 4
+    assert L.grpo_workspace_bytes(1, 512, 260, 1024, 1, 128) == 0      # bf16 needs multiple of 8
+    assert L.grpo_workspace_bytes(1, 512, 256, 1024, 5, 128) == 0      # bad dtype
+    assert L.grpo_workspace_bytes(9, 512, 256, 1024, 0, 128) == 0      # bad op
+
+
+def _fwd(**kw):
+    a = dict(H=FAKE, W=FAKE, y=FAKE, mask=FAKE, adv=FAKE, ref=FAKE, B=8, L=64, d=256, V=1024,
+             dt=0, beta=0.04, chunk=128, loss=FAKE, lp=FAKE, kl=FAKE, lse=FAKE, ws=FAKE,
+             wsb=1 << 40, s=None)
+    a.update(kw)
+    return L.grpo_loss_fwd(a["H"], a["W"], a["y"], a["mask"], a["adv"], a["ref"], a["B"], a["L"],
+                           a["d"], a["V"], a["dt"], a["beta"], a["chunk"], a["loss"], a["lp"],
+                           a["kl"], a["lse"], a["ws"], a["wsb"], a["s"])
+
+
+def test_loss_fwd_argument_errors():
+    assert _fwd(H=None) == -1
+    assert _fwd(lse=None) == -1
+    assert _fwd(B=0) == -1
+    assert _fwd(d=-4) == -1
+    assert _fwd(dt=3) == -1
+    assert _fwd(beta=float("nan")) == -1
+    assert _fwd(beta=float("inf")) == -1
+    assert _fwd(d=250) == -3
+    assert _fwd(ws=None) == -2
+    assert _fwd(wsb=16) == -2
+    assert b"workspace" in L.grpo_last_error()
+
+
+def test_loss_bwd_argument_errors():
+    def bwd(**kw):
+        a = dict(H=FAKE, dH=FAKE, dW=FAKE, g=1.0, wsb=1 << 40, ws=FAKE, B=8)
+        a.update(kw)
+        return L.grpo_loss_bwd(a["H"], FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], 64, 256,
+                               1024, 0, 0.04, a["g"], 128, a["dH"], a["dW"], a["ws"], a["wsb"],
+                               None)
+    assert bwd(dW=None) == -1
+    assert bwd(dH=None) == -1
+    assert bwd(g=float("nan")) == -1
+    assert bwd(B=-1) == -1
+    assert bwd(wsb=0) == -2
+
+
+def test_ref_and_advantages_argument_errors():
+    assert L.grpo_ref_logprobs(FAKE, FAKE, None, 512, 256, 1024, 0, 128, FAKE, FAKE, 1 << 40, None) == -1
+    assert L.grpo_ref_logprobs(FAKE, FAKE, FAKE, 512, 256, 1024, 0, 0, FAKE, FAKE, 1 << 40, None) == -1
+    assert L.grpo_ref_logprobs(FAKE, FAKE, FAKE, 512, 256, 1024, 0, 128, FAKE, FAKE, 8, None) == -2
+    assert L.grpo_advantages(None, 2, 4, 1e-4, FAKE, None) == -1
+    assert L.grpo_advantages(FAKE, 0, 4, 1e-4, FAKE, None) == -1
+    assert L.grpo_advantages(FAKE, 2, 4, float("nan"), FAKE, None) == -1
+    assert L.grpo_gemm_nt(FAKE, FAKE, 4, 4, 6, 1, FAKE, None) == -3    # 12 B rows
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    H = torch.zeros(4, 8)
+    with pytest.raises(ValueError):
+        gp.grpo_ref_logprobs(H, torch.zeros(16, 8), torch.zeros(4, dtype=torch.int32))

@@ -1,0 +1,196 @@
+"""GPU parity of the HIP path against the float64 oracle, element by element,
+at sizes that span several 256-wide tiles with ragged tails in tokens,
+vocabulary and hidden size; plus the method's invariants on the GPU.
+
+Tolerances.  float32 inputs: relative 1e-5 on the loss and on every lp.
+bfloat16 inputs: relative 2e-3 on the loss, gradient cosine >= 0.999 and
+max|g - g*| / max|g*| <= 1e-2 per tensor; lp within 1e-4 absolute (bf16
+products are exact in fp32, so lp differs only by fp32 accumulation order)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from tests.gpu_common import BETA, cosine, gpu_chain, max_abs_rel, oracle_chain, to64
+
+pytestmark = pytest.mark.gpu
+
+gp = pytest.importorskip("grpo_policy_loss_amd")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+BASE = workloads.WORKLOADS[0]
+
+
+def small(dtype, **kw):
+    # 6 sequences x 100 tokens = 600 tokens (3 token tiles, last ragged), d = 320
+    # (5 K slices of 64 bf16 / 10 of 32 f32), V = 1000 (4 vocab tiles, last 232 rows)
+    args = dict(name="small", prompts=2, G=3, L=100, d=320, V=1000, dtype=dtype, chunk=256,
+                len_lo=30, len_hi=100)
+    args.update(kw)
+    return BASE.scaled(**args)
+
+
+def inputs(w, seed=0):
+    return workloads.generate(w, seed=seed, device="cuda")
+
+
+# ----------------------------------------------------------------------------- tile main loop
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (300, 517, 192), (1000, 77, 320), (33, 600, 8)])
+def test_tile_gemm_matches_exact_product(dtype, M, N, K):
+    _need_gpu()
+    if dtype == torch.float32 and K % 4:
+        pytest.skip("f32 rows must be 16-byte multiples")
+    g = torch.Generator(device="cuda").manual_seed(M * 7 + N * 3 + K)
+    A = torch.randn(M, K, device="cuda", generator=g).to(dtype)
+    B = torch.randn(N, K, device="cuda", generator=g).to(dtype)
+    C = gp.grpo_gemm_nt(A, B)
+    torch.cuda.synchronize()
+    want = to64(A) @ to64(B).T
+    err = np.abs(to64(C) - want).max()
+    assert err <= 1e-5 * np.abs(want).max() + 1e-5, err
+
+
+# ----------------------------------------------------------------------------- advantages
+def test_advantages_match_oracle_and_degenerate_groups():
+    _need_gpu()
+    import oracle
+    r = torch.tensor([0, 1, 2, 3, 3, 3, 3, 3, 1, 0, 2, 2], dtype=torch.float32, device="cuda")
+    got = gp.grpo_advantages(r, 4, 1e-4).cpu().numpy()
+    want = oracle.group_advantages(r.cpu().numpy(), 4, 1e-4)
+    np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-7)
+    assert np.all(got[4:8] == 0.0)
+    one = gp.grpo_advantages(r, 1, 1e-4).cpu().numpy()
+    assert np.all(one == 0.0)
+    big = torch.randint(0, 4, (3 * 100,), device="cuda").float()     # G > 64: strided lanes
+    np.testing.assert_allclose(gp.grpo_advantages(big, 100).cpu().numpy(),
+                               oracle.group_advantages(big.cpu().numpy(), 100, 1e-4),
+                               rtol=1e-6, atol=1e-6)
+
+
+# ----------------------------------------------------------------------------- full chain
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [256, 300, 4096])
+def test_chain_matches_oracle(dtype, chunk):
+    _need_gpu()
+    w = small(dtype, chunk=chunk)
+    inp = inputs(w, seed=1)
+    g = gpu_chain(inp, w)
+    o = oracle_chain(inp, w)
+    lp, ref, lse, kl = to64(g["lp"]), to64(g["ref"]), to64(g["lse"]), to64(g["kl"])
+    loss = float(g["loss"].item())
+    np.testing.assert_allclose(to64(g["adv"]), o["adv"], rtol=1e-6, atol=1e-6)
+    if dtype == "f32":
+        np.testing.assert_allclose(lp, o["lp"], rtol=1e-5, atol=0)
+        np.testing.assert_allclose(ref, o["ref"], rtol=1e-5, atol=0)
+        np.testing.assert_allclose(lse, o["lse"], rtol=1e-5, atol=1e-6)
+        assert abs(loss - o["loss"]) <= 1e-5 * abs(o["loss"])
+        np.testing.assert_allclose(kl, o["kl"], rtol=1e-3, atol=1e-6)
+        assert max_abs_rel(to64(g["dH"]), o["dH"]) <= 1e-4
+        assert max_abs_rel(to64(g["dW"]), o["dW"]) <= 1e-4
+    else:
+        assert np.abs(lp - o["lp"]).max() <= 1e-4
+        assert np.abs(ref - o["ref"]).max() <= 1e-4
+        assert np.abs(lse - o["lse"]).max() <= 1e-4
+        assert abs(loss - o["loss"]) <= 2e-3 * abs(o["loss"])
+        assert np.abs(kl - o["kl"]).max() <= 1e-5
+        for k in ("dH", "dW"):
+            assert cosine(to64(g[k]), o[k]) >= 0.999, k
+            assert max_abs_rel(to64(g[k]), o[k]) <= 1e-2, k
+    # masked tokens get no gradient
+    m = inp["mask"].cpu().numpy().astype(bool)
+    assert np.all(to64(g["dH"])[~m] == 0.0)
+
+
+def test_chain_multiple_vocab_slabs_and_chunks():
+    """A chunk of 8192 f32 tokens limits the dZ slab to 8192 vocabulary rows, so
+    V = 20000 needs three slabs (the last one ragged); 8492 tokens need two chunks."""
+    _need_gpu()
+    w = BASE.scaled(name="slabs", prompts=1, G=4, L=2123, d=32, V=20000, dtype="f32",
+                    chunk=8192, len_lo=1000, len_hi=2123)
+    inp = inputs(w, seed=2)
+    g = gpu_chain(inp, w)
+    o = oracle_chain(inp, w)
+    np.testing.assert_allclose(to64(g["lp"]), o["lp"], rtol=1e-5, atol=0)
+    assert abs(g["loss"].item() - o["loss"]) <= 1e-5 * abs(o["loss"])
+    assert max_abs_rel(to64(g["dH"]), o["dH"]) <= 1e-4
+    assert max_abs_rel(to64(g["dW"]), o["dW"]) <= 1e-4
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_policy_equals_reference_kl_is_exactly_zero(dtype):
+    _need_gpu()
+    w = small(dtype)
+    inp = inputs(w, seed=3)
+    g = gpu_chain(inp, w, ref_from=inp["H"])
+    assert torch.equal(g["ref"], g["lp"])
+    assert torch.all(g["kl"] == 0)
+    A = np.repeat(g["adv"].cpu().numpy().astype(np.float64), w.L)
+    m = inp["mask"].cpu().numpy().astype(np.float64)
+    assert abs(g["loss"].item() - (-(m * A).sum() / m.sum())) <= 1e-6
+
+
+def test_bitwise_determinism_and_chunk_invariance():
+    _need_gpu()
+    w = small("bf16")
+    inp = inputs(w, seed=4)
+    a = gpu_chain(inp, w, chunk=256)
+    b = gpu_chain(inp, w, chunk=256)
+    for k in ("loss", "lp", "kl", "lse", "ref", "dH", "dW"):
+        assert torch.equal(a[k], b[k]), k
+    c = gpu_chain(inp, w, chunk=512)
+    assert torch.equal(a["lp"], c["lp"]) and torch.equal(a["lse"], c["lse"])
+
+
+def test_empty_mask_gives_zero_loss_and_gradients():
+    _need_gpu()
+    w = small("f32")
+    inp = inputs(w, seed=5)
+    inp["mask"].zero_()
+    g = gpu_chain(inp, w)
+    assert g["loss"].item() == 0.0
+    assert torch.all(g["dH"] == 0) and torch.all(g["dW"] == 0)
+
+
+def test_dw_accumulates_and_grad_loss_scales():
+    _need_gpu()
+    w = small("f32")
+    inp = inputs(w, seed=6)
+    g = gpu_chain(inp, w)
+    dH2, dW2 = gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], g["adv"], g["ref"],
+                                g["lp"], g["lse"], w.B, w.L, BETA, -2.0, w.chunk,
+                                dW=g["dW"].clone())
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(to64(dW2), -1.0 * to64(g["dW"]), rtol=1e-5,
+                               atol=1e-6 * np.abs(to64(g["dW"])).max())
+    np.testing.assert_allclose(to64(dH2), -2.0 * to64(g["dH"]), rtol=1e-5,
+                               atol=1e-6 * np.abs(to64(g["dH"])).max())
+
+
+@pytest.mark.parametrize("N,d,V", [(1, 8, 1), (7, 16, 3), (257, 8, 300)])
+def test_degenerate_shapes_pure_kl(N, d, V):
+    """One sequence (G = 1, so every advantage is 0): the gradient is the KL
+    term alone.  The reference hidden states are drawn independently, so
+    x = ref_lp - lp is O(1) and the KL gradient is well conditioned in fp32
+    (with H_ref = H + small noise, x is a difference of two nearly equal fp32
+    log-probs and carries ~1e-4 relative error by construction)."""
+    _need_gpu()
+    w = BASE.scaled(name="tiny", prompts=1, G=1, L=N, d=d, V=V, dtype="f32", chunk=100,
+                    len_lo=max(1, N // 2), len_hi=N)
+    inp = inputs(w, seed=7)
+    ref_h = workloads.draw_hidden(N, d, torch.float32, 99, "cuda")
+    g = gpu_chain(inp, w, ref_from=ref_h)
+    o = oracle_chain(inp, w, ref_from=ref_h)
+    assert np.all(o["adv"] == 0)
+    np.testing.assert_allclose(to64(g["lp"]), o["lp"], rtol=1e-5, atol=1e-6)
+    assert abs(g["loss"].item() - o["loss"]) <= 1e-5 * abs(o["loss"]) + 1e-7
+    if V == 1:          # a single class: lp = 0, no gradient at all
+        assert torch.all(g["dW"] == 0) and torch.all(g["dH"] == 0)
+    else:
+        assert max_abs_rel(to64(g["dW"]), o["dW"]) <= 1e-4
+        assert max_abs_rel(to64(g["dH"]), o["dH"]) <= 1e-4
