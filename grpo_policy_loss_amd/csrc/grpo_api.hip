@@ -59,7 +59,7 @@ FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
   p.cpad = round_up(p.C, grpo::kBN);
   p.S = (V + grpo::kBM - 1) / grpo::kBM;
   p.nchunks = (N + p.C - 1) / p.C;
-  p.parts_per_chunk = p.cpad / 256;
+  p.parts_per_chunk = (p.C + grpo::kMergeTokens - 1) / grpo::kMergeTokens;  // merge blocks per chunk
   Carve c;
   p.o_pm = c.take((size_t)(p.S * p.cpad) * 4);
   p.o_ps = c.take((size_t)(p.S * p.cpad) * 4);
@@ -75,7 +75,7 @@ FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
 constexpr int64_t kSlabBytes = 256ll << 20;
 
 struct BwdPlan {
-  int64_t C, cpad, vpad, vs, nslabs, nchunks;
+  int64_t C, cpad, vpad, vs, nslabs, nchunks, nsplit;
   size_t o_idx, o_cnt, o_wt, o_hact, o_ht, o_coef, o_lse, o_y, o_dz, o_dzt, o_dhacc, total;
 };
 
@@ -90,6 +90,10 @@ BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
   p.vs = std::min<int64_t>(vs, p.vpad);
   p.nslabs = (V + p.vs - 1) / p.vs;
   p.nchunks = (N + p.C - 1) / p.C;
+  // split the dH GEMM's vocabulary range so one launch has >= ~2 workgroups per CU
+  const int64_t dh_tiles = ((d + 255) / 256) * (p.cpad / 256);
+  p.nsplit = std::max<int64_t>(1, std::min<int64_t>(8, (512 + dh_tiles - 1) / dh_tiles));
+  p.nsplit = std::min<int64_t>(p.nsplit, std::max<int64_t>(1, p.vs / 256));
   Carve c;
   p.o_idx = c.take((size_t)N * 4);
   p.o_cnt = c.take(4);
@@ -101,7 +105,7 @@ BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
   p.o_y = c.take((size_t)p.cpad * 4);
   p.o_dz = c.take((size_t)(p.cpad * p.vs) * es);
   p.o_dzt = c.take((size_t)(p.vs * p.cpad) * es);
-  p.o_dhacc = c.take((size_t)(p.cpad * d) * 4);
+  p.o_dhacc = c.take((size_t)(p.nsplit * p.cpad * d) * 4);
   p.total = c.off;
   return p;
 }
@@ -160,10 +164,11 @@ int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* 
                                     cpart, (int)(c * p.parts_per_chunk), s));
   }
   if (mode == 1) {
-    // every full chunk writes all cpad/256 of its slots; a short last chunk
+    // every full chunk writes all of its slots; a short last chunk
     // writes only its first blocks, and the final sum reads exactly those
     const int64_t last_c0 = (p.nchunks - 1) * p.C;
-    const int64_t last_blocks = (std::min<int64_t>(p.C, N - last_c0) + 255) / 256;
+    const int64_t last_blocks =
+        (std::min<int64_t>(p.C, N - last_c0) + grpo::kMergeTokens - 1) / grpo::kMergeTokens;
     const int64_t nparts = (p.nchunks - 1) * p.parts_per_chunk + last_blocks;
     GRPO_HIP(grpo::launch_loss_final(lpart, cpart, (int)nparts, loss, s));
   }
@@ -205,11 +210,12 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
       GRPO_HIP(grpo::launch_dz<T>(W, H_act, d, V, v0, vs_valid, (int)p.vs, cnt, c0, C,
                                   (int)p.cpad, coef, lse_c, y_c, dZ, dZT, s));
       GRPO_HIP(grpo::launch_dh_gemm<T>(WT, p.vpad, v0, vs_valid, dZ, (int)p.vs, d, cnt, c0, C,
-                                       (int)p.cpad, sl == 0 ? 1 : 0, dH_acc, s));
+                                       (int)p.cpad, (int)p.nsplit, sl == 0 ? 1 : 0, dH_acc, s));
       GRPO_HIP(grpo::launch_dw_gemm<T>(HT, (int)p.cpad, dZT, d, V, v0, vs_valid, cnt, c0, C, dW,
                                        s));
     }
-    GRPO_HIP(grpo::launch_dh_scatter<T>(dH_acc, d, idx, cnt, c0, C, dH, s));
+    GRPO_HIP(grpo::launch_dh_scatter<T>(dH_acc, (int)p.nsplit, (int)p.cpad, d, idx, cnt, c0, C, dH,
+                                        s));
   }
   return GRPO_OK;
 }

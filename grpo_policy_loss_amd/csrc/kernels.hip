@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(64) k_advantages(const float* __restrict__ r, 
 
 // ---------------------------------------------------------------- forward tile
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
     k_lse_partials(const T* __restrict__ W, const T* __restrict__ H, const int32_t* __restrict__ y,
                    int64_t V, int64_t d, int n_tok, int cpad, int tm, int tn,
                    float* __restrict__ part_m, float* __restrict__ part_s,
@@ -130,16 +130,16 @@ __global__ void __launch_bounds__(kThreads, 1)
   const Operand A{(const char*)(W + m0 * d), rowb, mvalid, rowb};
   const Operand B{(const char*)(H + (int64_t)n0 * d), rowb, n_tok - n0, rowb};
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[kWM][kWN];
   tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave >> 1) * 128;
+  const int wm0 = (wave >> 2) * 128;
   const bool full = mvalid >= wm0 + 128;
 
-  float mx[4], sm[4];
+  float mx[kWN], sm[kWN];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kWN; ++j) {
     float m = kNegInf;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -158,7 +158,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   }
   // lanes l and l ^ 32 hold the same token column
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kWN; ++j) {
     const float om = __shfl_xor(mx[j], 32, 64);
     const float os = __shfl_xor(sm[j], 32, 64);
     lse_combine(mx[j], sm[j], om, os);
@@ -166,7 +166,7 @@ __global__ void __launch_bounds__(kThreads, 1)
 
   // target logit: exactly one lane of the grid holds z[t][y_t]
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kWN; ++j) {
     const int t = n0 + acc_col(wave, lane, j);
     if (t < n_tok) {
       const int r = y[t] - (int)(m0 + wm0);
@@ -183,21 +183,21 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
   }
 
-  // combine the two waves that share token columns, through LDS
+  // combine the two waves that share token columns (w and w + 4), through LDS
   __syncthreads();
-  float* red = (float*)smem;  // [2 column halves][128] max, then sums
-  if ((wave >> 1) == 1 && lane < 32) {
+  float* red = (float*)smem;  // [256 token columns] max, then [256] sums
+  if ((wave >> 2) == 1 && lane < 32) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      red[(wave & 1) * 128 + 32 * j + lane] = mx[j];
-      red[256 + (wave & 1) * 128 + 32 * j + lane] = sm[j];
+    for (int j = 0; j < kWN; ++j) {
+      red[acc_col(wave, lane, j)] = mx[j];
+      red[256 + acc_col(wave, lane, j)] = sm[j];
     }
   }
   __syncthreads();
-  if ((wave >> 1) == 0 && lane < 32) {
+  if ((wave >> 2) == 0 && lane < 32) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = (wave & 1) * 128 + 32 * j + lane;
+    for (int j = 0; j < kWN; ++j) {
+      const int c = acc_col(wave, lane, j);
       float m = mx[j], s = sm[j];
       lse_combine(m, s, red[c], red[256 + c]);
       const int t = n0 + c;
@@ -210,6 +210,12 @@ __global__ void __launch_bounds__(kThreads, 1)
 }
 
 // ---------------------------------------------------------------- forward merge
+// 256 threads = 32 tokens x 8 splits of the vocabulary-tile partials.  Split q
+// folds partials q, q + 8, ... of its token in order; the 8 split results are
+// then folded in order 0..7, so the result is independent of timing.
+constexpr int kMergeTok = kMergeTokens;
+constexpr int kMergeSplit = 8;
+
 __global__ void __launch_bounds__(256)
     k_lse_merge(int mode, const float* __restrict__ part_m, const float* __restrict__ part_s,
                 const float* __restrict__ zy, int S, int cpad, int n_tok, int64_t c0,
@@ -218,12 +224,12 @@ __global__ void __launch_bounds__(256)
                 const float* __restrict__ ref_lp, const uint8_t* __restrict__ mask,
                 const float* __restrict__ adv, int64_t L, float beta, double* loss_part,
                 int* cnt_part, int part0) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  double ml = 0.0;
-  int cnt = 0;
+  __shared__ float sm_m[kMergeSplit][kMergeTok], sm_s[kMergeSplit][kMergeTok];
+  const int tt = threadIdx.x % kMergeTok, q = threadIdx.x / kMergeTok;
+  const int t = blockIdx.x * kMergeTok + tt;
+  float M = kNegInf, Ssum = 0.f;
   if (t < n_tok) {
-    float M = kNegInf, Ssum = 0.f;
-    for (int s = 0; s < S; ++s) {
+    for (int s = q; s < S; s += kMergeSplit) {
       const float m = part_m[(int64_t)s * cpad + t];
       const float v = part_s[(int64_t)s * cpad + t];
       if (m > M) {
@@ -233,6 +239,18 @@ __global__ void __launch_bounds__(256)
         Ssum += v * exp2f((m - M) * kLog2e);
       }
     }
+  }
+  sm_m[q][tt] = M;
+  sm_s[q][tt] = Ssum;
+  __syncthreads();
+  // split 0 (lanes 0..31 of wave 0) finishes its token; waves 1..3 are done
+  if (threadIdx.x >= 64) return;
+  double ml = 0.0;
+  int cnt = 0;
+  if (q == 0 && t < n_tok) {
+    M = sm_m[0][tt];
+    Ssum = sm_s[0][tt];
+    for (int k = 1; k < kMergeSplit; ++k) lse_combine(M, Ssum, sm_m[k][tt], sm_s[k][tt]);
     const float lse = M + logf(Ssum);
     const int64_t tg = c0 + t;
     const int32_t yt = y[tg];
@@ -244,26 +262,18 @@ __global__ void __launch_bounds__(256)
       const float kl = expm1f(x) - x;
       out_kl[tg] = kl;
       if (mask[tg] != 0) {
-        const float ell = -(adv[tg / L] - beta * kl);
-        ml = (double)ell;
+        ml = (double)(-(adv[tg / L] - beta * kl));
         cnt = 1;
       }
     }
   }
   if (mode == 1) {
-    __shared__ double sml[4];
-    __shared__ int scnt[4];
+    // fixed-order butterfly over wave 0 (lanes 32..63 contribute 0)
     ml = wave_sum(ml);
     cnt = wave_sum(cnt);
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-      sml[wave] = ml;
-      scnt[wave] = cnt;
-    }
-    __syncthreads();
     if (threadIdx.x == 0) {
-      loss_part[part0 + blockIdx.x] = ((sml[0] + sml[1]) + sml[2]) + sml[3];
-      cnt_part[part0 + blockIdx.x] = scnt[0] + scnt[1] + scnt[2] + scnt[3];
+      loss_part[part0 + blockIdx.x] = ml;
+      cnt_part[part0 + blockIdx.x] = cnt;
     }
   }
 }
@@ -373,13 +383,26 @@ __global__ void __launch_bounds__(256)
 }
 
 // ---------------------------------------------------------------- backward tiles
+// LDS staging tile for the dZ stores: 256 rows of 256 bf16 with a 528-byte
+// pitch (16-byte aligned rows, shifted by one 16-byte bank group per row).
+constexpr int kStagePitch = 528;
+constexpr int kDzLdsBytes = (kLdsBytes > 256 * kStagePitch) ? kLdsBytes : 256 * kStagePitch;
+
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 1)
+__device__ __forceinline__ float dz_value(float z, float ct, float lb, int64_t v, int64_t yl,
+                                          int vs_valid) {
+  const float p = ex2(fmaf(z, kLog2e, -lb));
+  const float onehot = v == yl ? 1.f : 0.f;
+  return v < vs_valid ? ct * (onehot - p) : 0.f;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(kThreads, 2)
     k_dz(const T* __restrict__ W, const T* __restrict__ H_act, int64_t d, int64_t v0,
          int vs_valid, int vs, const int32_t* __restrict__ count, int64_t c0, int C, int cpad,
          int tm, int tn, const float* __restrict__ coef, const float* __restrict__ lse_c,
          const int32_t* __restrict__ y_c, T* __restrict__ dZ, T* __restrict__ dZT) {
-  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  __shared__ __attribute__((aligned(1024))) char smem[kDzLdsBytes];
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
   int n_act = count[0] - (int)c0;
   n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
@@ -391,70 +414,142 @@ __global__ void __launch_bounds__(kThreads, 1)
   const uint32_t rowb = (uint32_t)(d * (int64_t)sizeof(T));
   const Operand A{(const char*)(W + (v0 + m0) * d), rowb, vs_valid - m0, rowb};
   const Operand B{(const char*)(H_act + (int64_t)n0 * d), rowb, n_act - n0, rowb};
-  f32x16_t acc[4][4];
+  f32x16_t acc[kWM][kWN];
   tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float ct[kWN], lb[kWN];
+  int64_t yl[kWN];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kWN; ++j) {
     const int t = n0 + acc_col(wave, lane, j);
-    const float ct = coef[t];
-    const float lb = lse_c[t] * kLog2e;
-    const int64_t yl = (int64_t)y_c[t] - v0;  // target relative to the slab
+    ct[j] = coef[t];
+    lb[j] = lse_c[t] * kLog2e;
+    yl[j] = (int64_t)y_c[t] - v0;  // target relative to the slab
+  }
+  if (sizeof(T) == 4) {
+    // float32 (small shapes only): direct stores
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < kWN; ++j) {
+      const int t = n0 + acc_col(wave, lane, j);
+#pragma unroll
+      for (int i = 0; i < kWM; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int v = m0 + acc_row(wave, lane, i, 4 * g);
+          float q[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            q[u] = dz_value<T>(acc[i][j][4 * g + u], ct[j], lb[j], v + u, yl[j], vs_valid);
+          store4(dZ + (int64_t)t * vs + v, q[0], q[1], q[2], q[3]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) dZT[(int64_t)(v + u) * cpad + t] = to_elem<T>(q[u]);
+        }
+    }
+    return;
+  }
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+  typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+  // pass 1: stage as [token][vocab], store dZ rows (token-major, vocab contiguous)
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    const int tl = acc_col(wave, lane, j);
+#pragma unroll
+    for (int i = 0; i < kWM; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int v = m0 + acc_row(wave, lane, i, 4 * g);
+        const int vl = acc_row(wave, lane, i, 4 * g);
         float q[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float p = ex2(fmaf(acc[i][j][4 * g + u], kLog2e, -lb));
-          const float onehot = (v + u) == yl ? 1.f : 0.f;
-          q[u] = (v + u) < vs_valid ? ct * (onehot - p) : 0.f;
-        }
-        store4(dZ + (int64_t)t * vs + v, q[0], q[1], q[2], q[3]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) dZT[(int64_t)(v + u) * cpad + t] = to_elem<T>(q[u]);
+        for (int u = 0; u < 4; ++u)
+          q[u] = dz_value<T>(acc[i][j][4 * g + u], ct[j], lb[j], m0 + vl + u, yl[j], vs_valid);
+        *(bf16x4_t GRPO_LDS*)(lds + tl * kStagePitch + vl * 2) =
+            bf16x4_t{(__bf16)q[0], (__bf16)q[1], (__bf16)q[2], (__bf16)q[3]};
       }
-    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int idx = it * kThreads + (int)threadIdx.x;
+    const int r = idx >> 5, c = idx & 31;          // token row, 16-byte column
+    *(i32x4_t*)(dZ + (int64_t)(n0 + r) * vs + m0 + c * 8) =
+        *(const i32x4_t GRPO_LDS*)(lds + r * kStagePitch + c * 16);
+  }
+  // pass 2: stage as [vocab][token], store dZT rows (vocab-major, token contiguous)
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    const int tl = acc_col(wave, lane, j);
+#pragma unroll
+    for (int i = 0; i < kWM; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int vl = acc_row(wave, lane, i, 4 * g);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float q =
+              dz_value<T>(acc[i][j][4 * g + u], ct[j], lb[j], m0 + vl + u, yl[j], vs_valid);
+          *(__bf16 GRPO_LDS*)(lds + (vl + u) * kStagePitch + tl * 2) = (__bf16)q;
+        }
+      }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int idx = it * kThreads + (int)threadIdx.x;
+    const int r = idx >> 5, c = idx & 31;          // vocab row, 16-byte column
+    *(i32x4_t*)(dZT + (int64_t)(m0 + r) * cpad + n0 + c * 8) =
+        *(const i32x4_t GRPO_LDS*)(lds + r * kStagePitch + c * 16);
   }
 }
 
+// dH partial of split `sp`: vocabulary columns [k0, k1) of the slab.  Split
+// sp accumulates into its own buffer dH_acc[sp], so no two workgroups ever
+// write the same element and the final sum over splits has a fixed order.
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
     k_dh_gemm(const T* __restrict__ WT, int64_t vpad, int64_t v0, int vs_valid,
               const T* __restrict__ dZ, int vs, int64_t d, const int32_t* __restrict__ count,
-              int64_t c0, int C, int tm, int tn, int first, float* __restrict__ dH_acc) {
+              int64_t c0, int C, int cpad, int tm, int tn, int nsplit, int kchunk, int first,
+              float* __restrict__ dH_acc) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
   int n_act = count[0] - (int)c0;
   n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
+  // split index outermost, then the XCD-aware raster inside one split
+  const int per_split = tm * tn;
+  const int sp = blockIdx.x / per_split;
   int mt, nt;
-  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  tile_coords(blockIdx.x - sp * per_split, per_split, tm, tn, mt, nt);
   const int n0 = nt * kBN;
   if (n0 >= n_act) return;
   const int64_t m0 = (int64_t)mt * kBM;
-  const uint32_t kb = (uint32_t)(((int64_t)vs_valid * (int64_t)sizeof(T) + 15) & ~(int64_t)15);
-  const Operand A{(const char*)(WT + m0 * vpad + v0), (uint32_t)(vpad * (int64_t)sizeof(T)),
+  const int k0 = sp * kchunk;
+  const int k1 = (k0 + kchunk) < vs_valid ? (k0 + kchunk) : vs_valid;
+  const int klen = k1 > k0 ? k1 - k0 : 0;
+  const uint32_t kb = (uint32_t)(((int64_t)klen * (int64_t)sizeof(T) + 15) & ~(int64_t)15);
+  const Operand A{(const char*)(WT + m0 * vpad + v0 + k0), (uint32_t)(vpad * (int64_t)sizeof(T)),
                   (int)((d - m0) < kBM ? (d - m0) : kBM), kb};
-  const Operand B{(const char*)(dZ + (int64_t)n0 * vs), (uint32_t)(vs * (int64_t)sizeof(T)),
+  const Operand B{(const char*)(dZ + (int64_t)n0 * vs + k0), (uint32_t)(vs * (int64_t)sizeof(T)),
                   n_act - n0, kb};
-  f32x16_t acc[4][4];
+  f32x16_t acc[kWM][kWN];
   tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
+  if (klen == 0 && !first) return;
 
+  float* out = dH_acc + (int64_t)sp * cpad * d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kWN; ++j) {
     const int t = n0 + acc_col(wave, lane, j);
     if (t >= n_act) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kWM; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int64_t nd = m0 + acc_row(wave, lane, i, 4 * g);
         if (nd >= d) continue;
-        f32x4_t* p = (f32x4_t*)(dH_acc + (int64_t)t * d + nd);
+        f32x4_t* p = (f32x4_t*)(out + (int64_t)t * d + nd);
         f32x4_t v{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                   acc[i][j][4 * g + 3]};
         if (!first) v += *p;
@@ -464,7 +559,7 @@ __global__ void __launch_bounds__(kThreads, 1)
 }
 
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
     k_dw_gemm(const T* __restrict__ HT, int cpad, const T* __restrict__ dZT, int64_t d,
               int64_t v0, int vs_valid, const int32_t* __restrict__ count, int64_t c0, int C,
               int tm, int tn, float* __restrict__ dW) {
@@ -481,12 +576,12 @@ __global__ void __launch_bounds__(kThreads, 1)
   const uint32_t ldb = (uint32_t)(cpad * (int64_t)sizeof(T));
   const Operand A{(const char*)(HT + m0 * cpad), ldb, (int)((d - m0) < kBM ? (d - m0) : kBM), kb};
   const Operand B{(const char*)(dZT + (int64_t)n0 * cpad), ldb, vs_valid - n0, kb};
-  f32x16_t acc[4][4];
+  f32x16_t acc[kWM][kWN];
   tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < kWN; ++j) {
     const int v = n0 + acc_col(wave, lane, j);
     if (v >= vs_valid) continue;
 #pragma unroll
@@ -504,15 +599,18 @@ __global__ void __launch_bounds__(kThreads, 1)
 
 template <typename T>
 __global__ void __launch_bounds__(256)
-    k_dh_scatter(const float* __restrict__ dH_acc, int64_t d, const int32_t* __restrict__ idx,
-                 const int32_t* __restrict__ count, int64_t c0, int C, T* __restrict__ dH) {
+    k_dh_scatter(const float* __restrict__ dH_acc, int nsplit, int cpad, int64_t d,
+                 const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int64_t c0,
+                 int C, T* __restrict__ dH) {
   int n_act = count[0] - (int)c0;
   n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
   const int j = blockIdx.x;
   if (j >= n_act) return;
   const int64_t t = idx[c0 + j];
   for (int64_t k = threadIdx.x * 4; k < d; k += 1024) {
-    const f32x4_t v = *(const f32x4_t*)(dH_acc + (int64_t)j * d + k);
+    f32x4_t v = *(const f32x4_t*)(dH_acc + (int64_t)j * d + k);
+    for (int sp = 1; sp < nsplit; ++sp)
+      v += *(const f32x4_t*)(dH_acc + ((int64_t)sp * cpad + j) * d + k);
     store4(dH + t * d + k, v[0], v[1], v[2], v[3]);
   }
 }
@@ -526,7 +624,7 @@ __global__ void __launch_bounds__(256) k_zero(int4* __restrict__ p, int64_t n16,
 }
 
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(kThreads, 2)
     k_gemm_nt(const T* __restrict__ A, const T* __restrict__ B, int64_t M, int64_t N, int64_t K,
               int tm, int tn, float* __restrict__ C) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -537,13 +635,13 @@ __global__ void __launch_bounds__(kThreads, 1)
   const uint32_t rowb = (uint32_t)(K * (int64_t)sizeof(T));
   const Operand Ao{(const char*)(A + m0 * K), rowb, (int)((M - m0) < kBM ? (M - m0) : kBM), rowb};
   const Operand Bo{(const char*)(B + n0 * K), rowb, (int)((N - n0) < kBN ? (N - n0) : kBN), rowb};
-  f32x16_t acc[4][4];
+  f32x16_t acc[kWM][kWN];
   tile_mainloop<T>(acc, Ao, Bo, (int)((rowb + kBKB - 1) / kBKB), lds);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kWN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + acc_row(wave, lane, i, e), n = n0 + acc_col(wave, lane, j);
@@ -580,7 +678,7 @@ hipError_t launch_lse_merge(int mode, const float* part_m, const float* part_s, 
                             const uint8_t* mask, const float* adv, int64_t L, float beta,
                             double* loss_part, int* cnt_part, int part0, hipStream_t s) {
   ScopedKernelTimer timer_(KK_LSE_MERGE, s);
-  hipLaunchKernelGGL(k_lse_merge, dim3(cdiv(n_tok, 256)), dim3(256), 0, s, mode, part_m, part_s,
+  hipLaunchKernelGGL(k_lse_merge, dim3(cdiv(n_tok, kMergeTok)), dim3(256), 0, s, mode, part_m, part_s,
                      zy, S, cpad, n_tok, c0, y, V, out_lp, out_lse, out_kl, ref_lp, mask, adv, L,
                      beta, loss_part, cnt_part, part0);
   return hipGetLastError();
@@ -637,12 +735,14 @@ hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v
 template <typename T>
 hipError_t launch_dh_gemm(const T* WT, int64_t vpad, int64_t v0, int vs_valid, const T* dZ, int vs,
                           int64_t d, const int32_t* count, int64_t c0, int C, int cpad,
-                          int first, float* dH_acc, hipStream_t s) {
+                          int nsplit, int first, float* dH_acc, hipStream_t s) {
   ScopedKernelTimer timer_(KK_DH_GEMM, s);
-  (void)cpad;
   const int tm = cdiv(d, kBM), tn = cdiv(C, kBN);
-  hipLaunchKernelGGL(k_dh_gemm<T>, dim3(tm * tn), dim3(kThreads), 0, s, WT, vpad, v0, vs_valid, dZ,
-                     vs, d, count, c0, C, tm, tn, first, dH_acc);
+  // K range per split: a whole number of 64-element (128-byte bf16) slices
+  const int kchunk = (int)(((int64_t)cdiv(vs_valid, nsplit) + 63) / 64 * 64);
+  hipLaunchKernelGGL(k_dh_gemm<T>, dim3(tm * tn * nsplit), dim3(kThreads), 0, s, WT, vpad, v0,
+                     vs_valid, dZ, vs, d, count, c0, C, cpad, tm, tn, nsplit, kchunk, first,
+                     dH_acc);
   return hipGetLastError();
 }
 
@@ -659,10 +759,12 @@ hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZT, int64_t d, int64_
 }
 
 template <typename T>
-hipError_t launch_dh_scatter(const float* dH_acc, int64_t d, const int32_t* idx,
-                             const int32_t* count, int64_t c0, int C, T* dH, hipStream_t s) {
+hipError_t launch_dh_scatter(const float* dH_acc, int nsplit, int cpad, int64_t d,
+                             const int32_t* idx, const int32_t* count, int64_t c0, int C, T* dH,
+                             hipStream_t s) {
   ScopedKernelTimer timer_(KK_DH_SCATTER, s);
-  hipLaunchKernelGGL(k_dh_scatter<T>, dim3(C), dim3(256), 0, s, dH_acc, d, idx, count, c0, C, dH);
+  hipLaunchKernelGGL(k_dh_scatter<T>, dim3(C), dim3(256), 0, s, dH_acc, nsplit, cpad, d, idx,
+                     count, c0, C, dH);
   return hipGetLastError();
 }
 
@@ -702,12 +804,12 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
                                    const int32_t*, int64_t, int, int, const float*, const float*, \
                                    const int32_t*, T*, T*, hipStream_t);                          \
   template hipError_t launch_dh_gemm<T>(const T*, int64_t, int64_t, int, const T*, int, int64_t,  \
-                                        const int32_t*, int64_t, int, int, int, float*,           \
+                                        const int32_t*, int64_t, int, int, int, int, float*,      \
                                         hipStream_t);                                             \
   template hipError_t launch_dw_gemm<T>(const T*, int, const T*, int64_t, int64_t, int64_t, int,  \
                                         const int32_t*, int64_t, int, float*, hipStream_t);       \
-  template hipError_t launch_dh_scatter<T>(const float*, int64_t, const int32_t*, const int32_t*, \
-                                           int64_t, int, T*, hipStream_t);                        \
+  template hipError_t launch_dh_scatter<T>(const float*, int, int, int64_t, const int32_t*,      \
+                                           const int32_t*, int64_t, int, T*, hipStream_t);        \
   template hipError_t launch_gemm_nt<T>(const T*, const T*, int64_t, int64_t, int64_t, float*,    \
                                         hipStream_t);
 

@@ -6,6 +6,9 @@
 
 namespace grpo {
 
+// Tokens per block of the forward merge kernel (one loss partial per block).
+constexpr int kMergeTokens = 32;
+
 // Logical tile grid of one GEMM-shaped launch.
 struct Grid2 {
   int tm;  // tiles along M (A rows)
@@ -53,10 +56,12 @@ hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v
                      int vs, const int32_t* count, int64_t c0, int C, int cpad, const float* coef,
                      const float* lse_c, const int32_t* y_c, T* dZ, T* dZT, hipStream_t s);
 
+// dH_acc holds nsplit partial buffers of [cpad, d] floats; split sp covers
+// one contiguous share of the slab's vocabulary columns.
 template <typename T>
 hipError_t launch_dh_gemm(const T* WT, int64_t vpad, int64_t v0, int vs_valid, const T* dZ, int vs,
                           int64_t d, const int32_t* count, int64_t c0, int C, int cpad,
-                          int first, float* dH_acc, hipStream_t s);
+                          int nsplit, int first, float* dH_acc, hipStream_t s);
 
 template <typename T>
 hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZT, int64_t d, int64_t V, int64_t v0,
@@ -64,8 +69,9 @@ hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZT, int64_t d, int64_
                           hipStream_t s);
 
 template <typename T>
-hipError_t launch_dh_scatter(const float* dH_acc, int64_t d, const int32_t* idx,
-                             const int32_t* count, int64_t c0, int C, T* dH, hipStream_t s);
+hipError_t launch_dh_scatter(const float* dH_acc, int nsplit, int cpad, int64_t d,
+                             const int32_t* idx, const int32_t* count, int64_t c0, int C, T* dH,
+                             hipStream_t s);
 
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 

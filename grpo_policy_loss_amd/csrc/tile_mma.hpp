@@ -5,28 +5,35 @@
 // along k), on gfx950 (CDNA4) matrix cores.
 //
 // Layout and schedule:
-//  * 256 threads = 4 wave64s in a 2 x 2 grid; each wave owns 128 x 128 of the
-//    tile as 4 x 4 blocks of the 32 x 32 MFMA output (256 accumulator
-//    registers per lane).
+//  * 512 threads = 8 wave64s, two per SIMD (waves w and w + 4 share a SIMD),
+//    in a 2 (M) x 4 (N) grid; each wave owns 128 x 64 of the tile as 4 x 2
+//    blocks of the 32 x 32 MFMA output (128 accumulator registers per lane).
+//    Two waves per SIMD let one wave's LDS or barrier stalls be covered by
+//    the other's MFMAs, while all eight share one 256 x 256 tile (the tile
+//    size sets the L2 -> LDS traffic per flop).
 //  * K advances in 128-byte slices (64 bf16 or 32 f32).  Each slice of A and
 //    B (256 rows x 128 B = 32 KB each) is copied global -> LDS by the buffer
 //    unit directly (buffer_load_dwordx4 ... lds): no VGPR staging.  LDS is
 //    double buffered (2 x 64 KB), so the copy of slice k+1 runs while the
 //    matrix cores consume slice k.
+//  * MFMA operand fragments are double buffered in registers: the LDS reads
+//    of k-step s+1 are issued between the MFMAs of k-step s.
 //  * Out-of-range rows and k-columns read as zero: each operand is addressed
 //    through a buffer resource whose range ends at its last valid row, and an
 //    invalid row or column gets an offset past that range.  Tails in M, N
 //    and K therefore need no separate code path.
-//  * Within a 128-byte LDS row the eight 16-byte chunks are XOR-swizzled by
-//    (row & 7), so the ds_read_b128 of 8 consecutive rows at the same logical
-//    chunk hits 8 distinct bank groups.
+//  * gfx950's LDS serves 256 bytes per clock, i.e. one ds_read_b128 cycle
+//    covers 16 lanes = 16 rows of a fragment.  The eight 16-byte chunks of a
+//    128-byte LDS row are XOR-swizzled by f(r) = (r & 7) ^ ((r >> 3) & 1), so
+//    any 16 consecutive rows at one logical chunk hit 16 distinct bank groups.
 //  * bf16: v_mfma_f32_32x32x16_bf16, one per 16-byte chunk pair.
 //    f32:  v_mfma_f32_32x32x2_f32, four per chunk pair; lane l supplies
 //          element e of its 4-float chunk as its k = l/32 operand, so the
 //          four MFMAs together cover the 8 k of the pair.
 //
-// Output register layout (for both MFMAs): lane l, block (i, j), element e
-// holds C[wm0 + 32 i + 8 (e / 4) + 4 (l / 32) + e % 4][wn0 + 32 j + l % 32].
+// Output register layout (for both MFMAs): lane l of wave w, block (i, j),
+// element e holds C[128 (w / 4) + 32 i + 8 (e / 4) + 4 (l / 32) + e % 4]
+//                  [64 (w % 4) + 32 j + l % 32].
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -43,7 +50,9 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 constexpr int kBM = 256;          // tile rows (A rows)
 constexpr int kBN = 256;          // tile cols (B rows)
 constexpr int kBKB = 128;         // K slice in bytes
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWM = 4;           // 32-row MFMA blocks per wave
+constexpr int kWN = 2;           // 32-col MFMA blocks per wave
 constexpr int kTileBytes = kBM * kBKB;   // one operand slice in LDS: 32 KB
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kLdsBytes = 2 * kStageBytes;  // double buffered A + B: 128 KB
@@ -64,15 +73,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// Element-type policy.
-template <typename T> struct Elem;
-template <> struct Elem<float> {
-  static constexpr int kSize = 4;
-};
-template <> struct Elem<__bf16> {
-  static constexpr int kSize = 2;
-};
-
 // One operand's view for the loader: rows [row0, row0 + rows_valid) of a
 // row-major matrix with row pitch `ld_bytes`, k-bytes [0, k_bytes) valid.
 struct Operand {
@@ -82,141 +82,169 @@ struct Operand {
   uint32_t k_bytes;      // valid k extent in bytes (multiple of 16)
 };
 
+// Each wave copies 32 rows of an operand slice: 4 DMA instructions, each
+// moving 8 rows x 128 B (lane i fills slot i & 7 of row i >> 3).
 struct Loader {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t rowoff[8];    // byte offset of each of this lane's 8 rows (kOOB if absent)
-  uint32_t chunk_bytes;  // this lane's logical 16-byte chunk within a 128-byte slice
+  uint32_t rowoff[4];       // byte offset of each of this lane's 4 rows (kOOB if absent)
+  uint32_t chunk_bytes;     // logical 16-byte chunk this lane copies, even 8-row groups
+  uint32_t chunk_bytes_odd; // the same for odd 8-row groups (f(r) flips bit 0)
   uint32_t k_bytes;
 
   __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
     int rv = op.rows_valid < 0 ? 0 : (op.rows_valid > kBM ? kBM : op.rows_valid);
     rsrc = make_rsrc(op.base, (uint32_t)rv * op.ld_bytes);
-    const int r_in = lane >> 3;                       // row within an 8-row group
-    chunk_bytes = (uint32_t)(((lane & 7) ^ r_in) << 4);  // logical chunk stored at slot lane&7
+    const int r_in = lane >> 3;                          // row within an 8-row group
+    chunk_bytes = (uint32_t)(((lane & 7) ^ r_in) << 4);  // slot lane & 7 holds chunk slot ^ f(r)
+    chunk_bytes_odd = chunk_bytes ^ 16u;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int r = wave * 64 + j * 8 + r_in;
+    for (int j = 0; j < 4; ++j) {
+      int r = wave * 32 + j * 8 + r_in;
       rowoff[j] = r < rv ? (uint32_t)r * op.ld_bytes : kOOB;
     }
     k_bytes = op.k_bytes;
   }
 
-  // Issue the 8 direct-to-LDS copies of this wave's 64 rows of slice `kt`.
+  // Issue the 4 direct-to-LDS copies of this wave's 32 rows of slice `kt`.
   __device__ __forceinline__ void issue(int kt, char GRPO_LDS* tile, int wave) const {
-    const uint32_t kb = (uint32_t)kt * kBKB + chunk_bytes;
-    const bool kok = kb < k_bytes;
+    const uint32_t kb0 = (uint32_t)kt * kBKB + chunk_bytes;
+    const uint32_t kb1 = (uint32_t)kt * kBKB + chunk_bytes_odd;
+    const bool kok0 = kb0 < k_bytes, kok1 = kb1 < k_bytes;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t kb = (j & 1) ? kb1 : kb0;
+      const bool kok = (j & 1) ? kok1 : kok0;
       uint32_t off = kok ? rowoff[j] + kb : kOOB;
-      char GRPO_LDS* dst = tile + (wave * 64 + j * 8) * kBKB;
+      char GRPO_LDS* dst = tile + (wave * 32 + j * 8) * kBKB;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, off, 0, 0, 0);
     }
   }
 };
 
-__device__ __forceinline__ void wait_vmem_all() {
-  // s_waitcnt vmcnt(0), leaving expcnt / lgkmcnt unconstrained
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+// s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]); the counters not named are left unconstrained.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// vmcnt(8): all but the 8 copies (one slice) issued last have landed
+__device__ __forceinline__ void wait_vmem_but_one_slice() { __builtin_amdgcn_s_waitcnt(0x0F70 | 8); }
+__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <typename T> struct Frag;
+template <> struct Frag<__bf16> { typedef bf16x8_t type; };
+template <> struct Frag<float> { typedef f32x4_t type; };
+
+template <typename T>
+__device__ __forceinline__ void load_frags(typename Frag<T>::type (&a)[4], typename Frag<T>::type (&b)[kWN],
+                                           const char GRPO_LDS* buf, const uint32_t (&aoff)[4],
+                                           const uint32_t (&boff)[kWN], uint32_t swz) {
+  typedef typename Frag<T>::type F;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) a[i] = *(const F GRPO_LDS*)(buf + aoff[i] + swz);
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) b[j] = *(const F GRPO_LDS*)(buf + kTileBytes + boff[j] + swz);
 }
 
-template <typename T> struct Mma;
-
-template <> struct Mma<__bf16> {
-  // one k16 step for the whole 4 x 4 block set of a wave
-  __device__ __forceinline__ static void step(f32x16_t (&acc)[4][4], const char GRPO_LDS* As,
-                                              const char GRPO_LDS* Bs, const uint32_t (&aoff)[4],
-                                              const uint32_t (&boff)[4], uint32_t swz) {
-    bf16x8_t a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8_t GRPO_LDS*)(As + aoff[i] + swz);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const bf16x8_t GRPO_LDS*)(Bs + boff[j] + swz);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-};
-
-template <> struct Mma<float> {
-  __device__ __forceinline__ static void step(f32x16_t (&acc)[4][4], const char GRPO_LDS* As,
-                                              const char GRPO_LDS* Bs, const uint32_t (&aoff)[4],
-                                              const uint32_t (&boff)[4], uint32_t swz) {
-    f32x4_t a[4], b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(const f32x4_t GRPO_LDS*)(As + aoff[i] + swz);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(const f32x4_t GRPO_LDS*)(Bs + boff[j] + swz);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
-  }
-};
-
-// The main loop.  `lds` must be kLdsBytes of workgroup memory.  On return all
-// waves have finished reading LDS only if the caller issues a barrier.
-template <typename T>
-__device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[4][4], const Operand& A,
-                                              const Operand& B, int k_slices,
-                                              char GRPO_LDS* lds) {
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int wm0 = (wave >> 1) * 128;
-  const int wn0 = (wave & 1) * 128;
-
+__device__ __forceinline__ void mfma_all(f32x16_t (&acc)[4][kWN], const bf16x8_t (&a)[4], const bf16x8_t (&b)[kWN]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kWN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+}
+__device__ __forceinline__ void mfma_all(f32x16_t (&acc)[4][kWN], const f32x4_t (&a)[4], const f32x4_t (&b)[kWN]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kWN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling hint: alternate one MFMA and one LDS read, n times.
+#define GRPO_SCHED_MFMA_DS(n)                                  \
+  _Pragma("unroll") for (int q_ = 0; q_ < (n); ++q_) {          \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          \
+  }
+
+// The main loop.  `lds` must be kLdsBytes of workgroup memory.  On return
+// the caller must barrier before reusing LDS.
+template <typename T>
+__device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[4][kWN], const Operand& A,
+                                              const Operand& B, int k_slices,
+                                              char GRPO_LDS* lds) {
+  typedef typename Frag<T>::type F;
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int wm0 = (wave >> 2) * 128;
+  const int wn0 = (wave & 3) * 64;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < kWN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
   Loader la, lb;
   la.init(A, wave, lane);
   lb.init(B, wave, lane);
-
-  // fragment row offsets inside a slice (bytes) and the per-step swizzle
-  uint32_t aoff[4], boff[4];
+  uint32_t aoff[4], boff[kWN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    aoff[i] = (uint32_t)(wm0 + 32 * i + (lane & 31)) * kBKB;
-    boff[i] = (uint32_t)(wn0 + 32 * i + (lane & 31)) * kBKB;
-  }
+  for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(wm0 + 32 * i + (lane & 31)) * kBKB;
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) boff[j] = (uint32_t)(wn0 + 32 * j + (lane & 31)) * kBKB;
   const uint32_t half = (uint32_t)(lane >> 5);
-  const uint32_t r7 = (uint32_t)(lane & 7);
+  const uint32_t r7 = (uint32_t)((lane & 7) ^ ((lane >> 3) & 1));
+  uint32_t swz[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) swz[s] = (((2u * s + half) ^ r7) << 4);
+  if (k_slices <= 0) return;
 
-  if (k_slices > 0) {
-    la.issue(0, lds, wave);
-    lb.issue(0, lds + kTileBytes, wave);
+  la.issue(0, lds, wave);
+  lb.issue(0, lds + kTileBytes, wave);
+  if (k_slices > 1) {
+    la.issue(1, lds + kStageBytes, wave);
+    lb.issue(1, lds + kStageBytes + kTileBytes, wave);
+    wait_vmem_but_one_slice();
+  } else {
+    wait_vmem_all();
   }
+  __builtin_amdgcn_s_barrier();
+  F fa[2][4], fb[2][kWN];
+  load_frags<T>(fa[0], fb[0], lds, aoff, boff, swz[0]);
+
   for (int kt = 0; kt < k_slices; ++kt) {
     char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
-    wait_vmem_all();
-    __builtin_amdgcn_s_barrier();
-    if (kt + 1 < k_slices) {
-      char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-      la.issue(kt + 1, nxt, wave);
-      lb.issue(kt + 1, nxt + kTileBytes, wave);
-    }
+    char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t swz = (((2u * s + half) ^ r7) << 4);
-      Mma<T>::step(acc, cur, cur + kTileBytes, aoff, boff, swz);
+      const int p = s & 1;
+      if (s < 3) {
+        load_frags<T>(fa[p ^ 1], fb[p ^ 1], cur, aoff, boff, swz[s + 1]);
+        mfma_all(acc, fa[p], fb[p]);
+        GRPO_SCHED_MFMA_DS(6);
+      } else {
+        mfma_all(acc, fa[p], fb[p]);
+        if (kt + 1 < k_slices) {
+          wait_vmem_all();
+          wait_lds_all();
+          __builtin_amdgcn_s_barrier();
+          if (kt + 2 < k_slices) {
+            la.issue(kt + 2, cur, wave);
+            lb.issue(kt + 2, cur + kTileBytes, wave);
+          }
+          load_frags<T>(fa[p ^ 1], fb[p ^ 1], nxt, aoff, boff, swz[0]);
+        }
+      }
     }
   }
 }
 
 // Coordinates of accumulator element (i, j, e) of this lane, tile-relative.
 __device__ __forceinline__ int acc_row(int wave, int lane, int i, int e) {
-  return (wave >> 1) * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  return (wave >> 2) * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
 }
 __device__ __forceinline__ int acc_col(int wave, int lane, int j) {
-  return (wave & 1) * 128 + 32 * j + (lane & 31);
+  return (wave & 3) * 64 + 32 * j + (lane & 31);
 }
 
 }  // namespace grpo
