@@ -13,8 +13,11 @@ sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -28,6 +31,95 @@ DEFAULT_WORKLOAD = "qwen2.5-1.5b-bf16"
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+CSRC = os.path.join(ROOT, "grpo_policy_loss_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30      # calibration copy for the HBM byte counters
+
+
+def kernel_source_hash():
+    """sha256 of the HIP sources: a traffic measurement is valid only for these."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(kernel, workload):
+    return os.path.join(PROFILES, f"traffic_{kernel}_{workload}.md")
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when there is none or the kernels changed since the counters were taken."""
+    path = traffic_file(kernel, workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        m = re.search(r"^traffic_record: (\{.*\})$", f.read(), flags=re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def summarize_traffic(fetch_csv, write_csv, workload, kernel="lse_partials"):
+    """Turn two rocprofv3 --pmc runs of `bench.py --traffic-probe` (FETCH_SIZE,
+    then WRITE_SIZE, in KiB per dispatch) into profiles/traffic_<kernel>_<workload>.md.
+    Each counter is scaled by what it reads for the 1 GiB calibration copy."""
+    def per_dispatch(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        return vals
+    f = per_dispatch(fetch_csv, "FETCH_SIZE")
+    w = per_dispatch(write_csv, "WRITE_SIZE")
+    def pick(vals, pat):
+        return [v for (d, n), v in sorted(vals.items(), key=lambda kv: int(kv[0][0])) if pat in n]
+    kpat = "k_" + kernel
+    copy_f, copy_w = pick(f, "copyBuffer"), pick(w, "copyBuffer")
+    kf, kw = pick(f, kpat), pick(w, kpat)
+    if not (copy_f and copy_w and kf and kw):
+        raise SystemExit("counter CSVs lack the calibration copy or the kernel")
+    scale_f = copy_f[-1] * 1024 / COPY_BYTES          # KiB counted per true byte read
+    scale_w = copy_w[-1] * 1024 / COPY_BYTES
+    fetch = sum(kf) / len(kf) * 1024 / scale_f
+    write = sum(kw) / len(kw) * 1024 / scale_w
+    rec = {"kernel": kernel, "workload": workload, "source_hash": kernel_source_hash(),
+           "launches": len(kf), "fetch_bytes_per_launch": round(fetch),
+           "write_bytes_per_launch": round(write), "hbm_bytes_per_launch": round(fetch + write),
+           "copy_fetch_scale": round(scale_f, 4), "copy_write_scale": round(scale_w, 4)}
+    lines = [f"# HBM traffic of `k_{kernel}` on the {workload} workload", "",
+             "Two counter runs of `bench.py --traffic-probe` (a 1 GiB device copy for calibration,",
+             "then one reference log-prob pass = one launch of the kernel per chunk), then this summary:", "",
+             "```",
+             "cd /tmp && export TMPDIR=/tmp",
+             f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/tf -o run -- python3 $R/bench.py --traffic-probe --workload {workload}",
+             f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/tw -o run -- python3 $R/bench.py --traffic-probe --workload {workload}",
+             f"python3 $R/bench.py --summarize-traffic $R/gpurun_out/tf/run_counter_collection.csv $R/gpurun_out/tw/run_counter_collection.csv --workload {workload}",
+             "```", "",
+             "| quantity | value |", "|---|---|",
+             f"| calibration copy: FETCH_SIZE KiB counted per true KiB read | {scale_f:.4f} |",
+             f"| calibration copy: WRITE_SIZE KiB counted per true KiB written | {scale_w:.4f} |",
+             f"| launches measured | {len(kf)} |",
+             f"| FETCH_SIZE per launch (scaled) | {fetch / 1e6:.1f} MB |",
+             f"| WRITE_SIZE per launch (scaled) | {write / 1e6:.1f} MB |",
+             f"| HBM bytes per launch | {(fetch + write) / 1e6:.1f} MB |", "",
+             "The benchmark reports this figure as `roofline.traffic` only while the HIP sources",
+             "hash to `source_hash` below; after any kernel change it reports null.", "",
+             "traffic_record: " + json.dumps(rec)]
+    path = traffic_file(kernel, workload)
+    with open(path, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print(path)
 
 
 def alg_flops(kind, d, V, N, N_act):
@@ -87,7 +179,15 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a 1 GiB calibration copy and one reference pass, then exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the traffic summary from two counter runs of --traffic-probe")
     args = ap.parse_args()
+
+    if args.summarize_traffic:
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -117,6 +217,18 @@ def main():
     dW = torch.zeros(V, d, dtype=torch.float32, device=dev)
     dH = torch.empty_like(inp["H"])
     stream = torch.cuda.current_stream()
+
+    if args.traffic_probe:
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, workspace=ws_f)
+        torch.cuda.synchronize()
+        log("[bench] traffic probe done")
+        return
 
     def step(ev=None):
         if ev is not None:
@@ -168,9 +280,11 @@ def main():
     roof = None
     if dom_flops is not None:
         achieved = dom_flops * args.steps / (dom_ms * 1e-3) / 1e12
+        tb = read_traffic(dom_name, w.name)
         roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved * 1e12 / peak, 4),
-                "traffic": None, "launches": dom_launches,
+                "traffic": tb, "traffic_unit": "bytes per launch (HBM, counters)",
+                "launches": dom_launches,
                 "avg_launch_ms": round(dom_ms / dom_launches, 4)}
 
     cpu = None

@@ -73,6 +73,7 @@ FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
 // Backward workspace.  The dZ slab (and its transpose) covers `vs`
 // vocabulary rows of one chunk; vs is chosen so each is at most 256 MiB.
 constexpr int64_t kSlabBytes = 256ll << 20;
+constexpr int64_t kCUs = 256;  // MI355X compute units (one 512-thread workgroup each)
 
 struct BwdPlan {
   int64_t C, cpad, vpad, vs, nslabs, nchunks, nsplit;
@@ -85,15 +86,51 @@ BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
   p.C = std::min<int64_t>(chunk, N);
   p.cpad = round_up(p.C, grpo::kBN);
   p.vpad = round_up(V, grpo::kBM);
-  int64_t vs = kSlabBytes / (p.cpad * (int64_t)es);
-  vs = std::max<int64_t>(grpo::kBM, vs / grpo::kBM * grpo::kBM);
-  p.vs = std::min<int64_t>(vs, p.vpad);
-  p.nslabs = (V + p.vs - 1) / p.vs;
   p.nchunks = (N + p.C - 1) / p.C;
-  // split the dH GEMM's vocabulary range so one launch has >= ~2 workgroups per CU
-  const int64_t dh_tiles = ((d + 255) / 256) * (p.cpad / 256);
-  p.nsplit = std::max<int64_t>(1, std::min<int64_t>(8, (512 + dh_tiles - 1) / dh_tiles));
-  p.nsplit = std::min<int64_t>(p.nsplit, std::max<int64_t>(1, p.vs / 256));
+  int64_t vs_max = kSlabBytes / (p.cpad * (int64_t)es);
+  vs_max = std::max<int64_t>(grpo::kBM, vs_max / grpo::kBM * grpo::kBM);
+  vs_max = std::min<int64_t>(vs_max, p.vpad);
+  // Split the dH GEMM's vocabulary range when its tile grid alone cannot fill the
+  // chip: pick the split count (1..8) whose launch wastes the least of its last
+  // wave of workgroups (one 512-thread workgroup per CU), preferring fewer splits.
+  const int64_t ct = p.cpad / 256, dt = (d + 255) / 256;
+  const int64_t dh_tiles = dt * ct;
+  p.nsplit = 1;
+  if (dh_tiles < 2 * kCUs) {
+    double best = -1.0;
+    for (int64_t n = 1; n <= 8 && n * 256 <= vs_max; ++n) {
+      const int64_t wg = dh_tiles * n;
+      const double fill = (double)wg / (double)(((wg + kCUs - 1) / kCUs) * kCUs);
+      const double score = fill * std::min(1.0, (double)wg / (2.0 * kCUs));
+      if (score > best + 1e-9) {
+        best = score;
+        p.nsplit = n;
+      }
+    }
+  }
+  // Slab width: every launch runs in whole waves of kCUs workgroups, so model a
+  // chunk's backward as sum over slabs of waves(launch) x K-length(launch) for the
+  // dz (K = d), dW (K = chunk) and dH (K = slab / nsplit) GEMMs, and take the
+  // cheapest multiple of 256 up to the memory budget.
+  auto waves = [](int64_t wg) { return (wg + kCUs - 1) / kCUs; };
+  double best_cost = 0.0;
+  p.vs = vs_max;
+  for (int64_t vs = vs_max; vs >= std::max<int64_t>(256, vs_max / 2); vs -= 256) {
+    const int64_t ns = (V + vs - 1) / vs;
+    double cost = 0.0;
+    for (int64_t sl = 0; sl < ns; ++sl) {
+      const int64_t w = std::min<int64_t>(vs, V - sl * vs);
+      const int64_t vt = (w + 255) / 256;
+      cost += (double)waves(vt * ct) * (double)d;
+      cost += (double)waves(dt * vt) * (double)p.cpad;
+      cost += (double)waves(dh_tiles * p.nsplit) * (double)w / (double)p.nsplit;
+    }
+    if (vs == vs_max || cost < best_cost * (1.0 - 1e-6)) {
+      best_cost = cost;
+      p.vs = vs;
+    }
+  }
+  p.nslabs = (V + p.vs - 1) / p.vs;
   Carve c;
   p.o_idx = c.take((size_t)N * 4);
   p.o_cnt = c.take(4);
