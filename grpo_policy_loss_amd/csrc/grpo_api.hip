@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <algorithm>
@@ -71,8 +72,20 @@ FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
 }
 
 // Backward workspace.  The dZ slab (and its transpose) covers `vs`
-// vocabulary rows of one chunk; vs is chosen so each is at most 256 MiB.
-constexpr int64_t kSlabBytes = 256ll << 20;
+// vocabulary rows of one chunk, vs chosen so each is at most the slab budget:
+// 2 GiB by default, or GRPO_SLAB_MIB MiB when that variable is set.  It is
+// read at every call, so a workspace query and the backward it sizes must run
+// under the same setting.  Both slabs together hold chunk x vs x 4 bytes,
+// never more than one chunk's float32 logits.  Fewer, wider slabs mean fewer
+// read-modify-write passes over the dH split partials: at the Qwen2.5-1.5B
+// shape one full-vocabulary slab runs the backward about 10 % faster than
+// 256 MiB slabs, for 2 GB more workspace.
+constexpr int64_t kSlabBytesDefault = 2048ll << 20;
+int64_t slab_bytes() {
+  const char* e = getenv("GRPO_SLAB_MIB");
+  const long long mib = e ? atoll(e) : 0;
+  return mib > 0 ? (int64_t)mib << 20 : kSlabBytesDefault;
+}
 constexpr int64_t kCUs = 256;  // MI355X compute units (one 512-thread workgroup each)
 
 struct BwdPlan {
@@ -87,7 +100,7 @@ BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
   p.cpad = round_up(p.C, grpo::kBN);
   p.vpad = round_up(V, grpo::kBM);
   p.nchunks = (N + p.C - 1) / p.C;
-  int64_t vs_max = kSlabBytes / (p.cpad * (int64_t)es);
+  int64_t vs_max = slab_bytes() / (p.cpad * (int64_t)es);
   vs_max = std::max<int64_t>(grpo::kBM, vs_max / grpo::kBM * grpo::kBM);
   vs_max = std::min<int64_t>(vs_max, p.vpad);
   // Split the dH GEMM's vocabulary range when its tile grid alone cannot fill the

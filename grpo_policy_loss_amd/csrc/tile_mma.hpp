@@ -221,30 +221,47 @@ __device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[4][kWN], const Ope
   F fa[2][4], fb[2][kWN];
   load_frags<T>(fa[0], fb[0], lds, aoff, boff, swz[0]);
 
-  for (int kt = 0; kt < k_slices; ++kt) {
+  // Steady state: every slice but the last.  The slice barrier sits after the
+  // third k-step, once every wave holds the slice's last fragments in
+  // registers: the stage is then free for the copy of slice kt + 2, and after
+  // the copying waves' vmcnt wait slice kt + 1 is visible, so its first
+  // fragments load under the fourth k-step's MFMAs instead of after the barrier.
+  for (int kt = 0; kt + 1 < k_slices; ++kt) {
     char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
     char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int p = s & 1;
-      if (s < 3) {
-        load_frags<T>(fa[p ^ 1], fb[p ^ 1], cur, aoff, boff, swz[s + 1]);
-        mfma_all(acc, fa[p], fb[p]);
-        GRPO_SCHED_MFMA_DS(6);
-      } else {
-        mfma_all(acc, fa[p], fb[p]);
-        if (kt + 1 < k_slices) {
-          wait_vmem_all();
-          wait_lds_all();
-          __builtin_amdgcn_s_barrier();
-          if (kt + 2 < k_slices) {
-            la.issue(kt + 2, cur, wave);
-            lb.issue(kt + 2, cur + kTileBytes, wave);
-          }
-          load_frags<T>(fa[p ^ 1], fb[p ^ 1], nxt, aoff, boff, swz[0]);
-        }
-      }
+    load_frags<T>(fa[1], fb[1], cur, aoff, boff, swz[1]);
+    mfma_all(acc, fa[0], fb[0]);
+    GRPO_SCHED_MFMA_DS(6);
+    load_frags<T>(fa[0], fb[0], cur, aoff, boff, swz[2]);
+    mfma_all(acc, fa[1], fb[1]);
+    GRPO_SCHED_MFMA_DS(6);
+    load_frags<T>(fa[1], fb[1], cur, aoff, boff, swz[3]);
+    mfma_all(acc, fa[0], fb[0]);
+    GRPO_SCHED_MFMA_DS(6);
+    wait_vmem_all();
+    wait_lds_all();
+    __builtin_amdgcn_s_barrier();
+    if (kt + 2 < k_slices) {
+      la.issue(kt + 2, cur, wave);
+      lb.issue(kt + 2, cur + kTileBytes, wave);
     }
+    load_frags<T>(fa[0], fb[0], nxt, aoff, boff, swz[0]);
+    mfma_all(acc, fa[1], fb[1]);
+    GRPO_SCHED_MFMA_DS(6);
+  }
+  // last slice: no copy left to wait for
+  {
+    char GRPO_LDS* cur = lds + ((k_slices - 1) & 1) * kStageBytes;
+    load_frags<T>(fa[1], fb[1], cur, aoff, boff, swz[1]);
+    mfma_all(acc, fa[0], fb[0]);
+    GRPO_SCHED_MFMA_DS(6);
+    load_frags<T>(fa[0], fb[0], cur, aoff, boff, swz[2]);
+    mfma_all(acc, fa[1], fb[1]);
+    GRPO_SCHED_MFMA_DS(6);
+    load_frags<T>(fa[1], fb[1], cur, aoff, boff, swz[3]);
+    mfma_all(acc, fa[0], fb[0]);
+    GRPO_SCHED_MFMA_DS(6);
+    mfma_all(acc, fa[1], fb[1]);
   }
 }
 

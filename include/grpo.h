@@ -74,7 +74,10 @@ typedef enum { GRPO_OP_REF = 0, GRPO_OP_FWD = 1, GRPO_OP_BWD = 2 } grpo_op;
  * arguments.  It never scales with N*V: the forward keeps only per-token
  * split partials of one chunk, the backward one bounded [chunk x V_s] slab
  * of dZ (and its transpose), a transposed copy of W and one chunk of hidden
- * states.
+ * states.  Each dZ slab is at most 2 GiB (V_s <= V), or at most
+ * GRPO_SLAB_MIB MiB when that environment variable is set; a smaller budget
+ * trades speed for memory.  The variable is read at every call: query the
+ * workspace and run the backward under the same setting.
  */
 size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk);
 

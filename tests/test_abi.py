@@ -52,11 +52,34 @@ def test_workspace_bytes_bounded_and_independent_of_N_times_V(op):
     N, d, V, chunk = 163840, 4096, 128256, 8192
     ws = L.grpo_workspace_bytes(op, N, d, V, 1, chunk)
     assert ws > 0
-    assert ws < N * V * 2 / 10           # far below one bf16 (tokens x vocab) tensor
+    assert ws < N * V * 4 / 10           # far below the float32 (tokens x vocab) logits
     if op == 2:
+        # dZ and its transpose hold at most one chunk's float32 logits; the rest is
+        # W transposed (bf16), per-chunk hidden-state copies and dH split partials
+        # (at most 8 float32 copies of a chunk), and the 4 B/token index list
+        Vp = -(-V // 256) * 256
+        assert ws <= chunk * Vp * 4 + d * Vp * 2 + 2 * chunk * d * 2 + 8 * chunk * d * 4 \
+            + 4 * N + (1 << 20)
         # grows with N only through the active-index list (4 B per token)
         ws2 = L.grpo_workspace_bytes(op, 2 * N, d, V, 1, chunk)
         assert ws2 - ws <= 4 * N + 512
+
+
+def test_slab_budget_variable_bounds_the_backward_workspace(monkeypatch):
+    # Qwen2.5-1.5B shape, bf16: the default budget holds the whole vocabulary in
+    # one slab (4096 x 151936 x 2 B = 1.24 GB each for dZ and its transpose)
+    N, d, V, chunk = 32768, 1536, 151936, 4096
+    monkeypatch.delenv("GRPO_SLAB_MIB", raising=False)
+    full = L.grpo_workspace_bytes(2, N, d, V, 1, chunk)
+    assert full >= 2 * chunk * V * 2
+    monkeypatch.setenv("GRPO_SLAB_MIB", "256")
+    small = L.grpo_workspace_bytes(2, N, d, V, 1, chunk)
+    # 256 MiB of bf16 at 4096 rows is at most 32768 vocabulary columns per slab
+    Vp = -(-V // 256) * 256
+    assert full - small >= 2 * chunk * (Vp - 32768) * 2
+    assert small >= 2 * chunk * 16384 * 2                   # the planner keeps >= half the budget
+    monkeypatch.setenv("GRPO_SLAB_MIB", "0")                 # not positive: the default
+    assert L.grpo_workspace_bytes(2, N, d, V, 1, chunk) == full
 
 
 def test_workspace_bytes_rejects_bad_shapes():

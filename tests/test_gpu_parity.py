@@ -107,10 +107,12 @@ def test_chain_matches_oracle(dtype, chunk):
     assert np.all(to64(g["dH"])[~m] == 0.0)
 
 
-def test_chain_multiple_vocab_slabs_and_chunks():
-    """A chunk of 8192 f32 tokens limits the dZ slab to 8192 vocabulary rows, so
-    V = 20000 needs three slabs (the last one ragged); 8492 tokens need two chunks."""
+def test_chain_multiple_vocab_slabs_and_chunks(monkeypatch):
+    """With a 256 MiB slab budget a chunk of 8192 f32 tokens limits the dZ slab to
+    8192 vocabulary rows, so V = 20000 needs three slabs (the last one ragged);
+    8492 tokens need two chunks."""
     _need_gpu()
+    monkeypatch.setenv("GRPO_SLAB_MIB", "256")
     w = BASE.scaled(name="slabs", prompts=1, G=4, L=2123, d=32, V=20000, dtype="f32",
                     chunk=8192, len_lo=1000, len_hi=2123)
     inp = inputs(w, seed=2)
