@@ -90,7 +90,7 @@ constexpr int64_t kCUs = 256;  // MI355X compute units (one 512-thread workgroup
 
 struct BwdPlan {
   int64_t C, cpad, vpad, vs, nslabs, nchunks, nsplit;
-  size_t o_idx, o_cnt, o_wt, o_hact, o_ht, o_coef, o_lse, o_y, o_dz, o_dzt, o_dhacc, total;
+  size_t o_idx, o_cnt, o_wt, o_hact, o_ht, o_coef, o_lse, o_y, o_tgt, o_dz, o_dzt, o_dhacc, total;
 };
 
 BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
@@ -153,6 +153,7 @@ BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
   p.o_coef = c.take((size_t)p.cpad * 4);
   p.o_lse = c.take((size_t)p.cpad * 4);
   p.o_y = c.take((size_t)p.cpad * 4);
+  p.o_tgt = c.take((size_t)p.cpad * 4);
   p.o_dz = c.take((size_t)(p.cpad * p.vs) * es);
   p.o_dzt = c.take((size_t)(p.vs * p.cpad) * es);
   p.o_dhacc = c.take((size_t)(p.nsplit * p.cpad * d) * 4);
@@ -239,6 +240,7 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
   float* coef = (float*)(ws + p.o_coef);
   float* lse_c = (float*)(ws + p.o_lse);
   int32_t* y_c = (int32_t*)(ws + p.o_y);
+  float* tgt_c = (float*)(ws + p.o_tgt);
   T* dZ = (T*)(ws + p.o_dz);
   T* dZT = (T*)(ws + p.o_dzt);
   float* dH_acc = (float*)(ws + p.o_dhacc);
@@ -252,13 +254,13 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
     const int64_t c0 = c * p.C;
     const int C = (int)p.C;
     GRPO_HIP(grpo::launch_bwd_prep<T>(H, d, idx, cnt, c0, C, (int)p.cpad, y, mask, adv, ref_lp, lp,
-                                      lse, L, beta, grad_loss, H_act, coef, lse_c, y_c, s));
+                                      lse, L, beta, grad_loss, H_act, coef, lse_c, y_c, tgt_c, s));
     GRPO_HIP(grpo::launch_transpose<T>(H_act, p.cpad, d, HT, p.cpad, s));
     for (int64_t sl = 0; sl < p.nslabs; ++sl) {
       const int64_t v0 = sl * p.vs;
       const int vs_valid = (int)std::min<int64_t>(p.vs, V - v0);
       GRPO_HIP(grpo::launch_dz<T>(W, H_act, d, V, v0, vs_valid, (int)p.vs, cnt, c0, C,
-                                  (int)p.cpad, coef, lse_c, y_c, dZ, dZT, s));
+                                  (int)p.cpad, coef, lse_c, y_c, tgt_c, dZ, dZT, s));
       GRPO_HIP(grpo::launch_dh_gemm<T>(WT, p.vpad, v0, vs_valid, dZ, (int)p.vs, d, cnt, c0, C,
                                        (int)p.cpad, (int)p.nsplit, sl == 0 ? 1 : 0, dH_acc, s));
       GRPO_HIP(grpo::launch_dw_gemm<T>(HT, (int)p.cpad, dZT, d, V, v0, vs_valid, cnt, c0, C, dW,

@@ -357,7 +357,7 @@ __global__ void __launch_bounds__(256)
                const float* __restrict__ ref_lp, const float* __restrict__ lp,
                const float* __restrict__ lse, int64_t L, float beta, float grad_loss,
                T* __restrict__ H_act, float* __restrict__ coef, float* __restrict__ lse_c,
-               int32_t* __restrict__ y_c) {
+               int32_t* __restrict__ y_c, float* __restrict__ tgt_c) {
   const int cnt = count[0];
   if (c0 >= cnt) return;
   const int j = blockIdx.x;
@@ -371,13 +371,18 @@ __global__ void __launch_bounds__(256)
     if (valid) {
       const float x = ref_lp[t] - lp[t];
       const float scale = grad_loss / (float)(cnt > 0 ? cnt : 1);
-      coef[j] = scale * (-adv[t / L] - beta * expm1f(x));
+      const float c = scale * (-adv[t / L] - beta * expm1f(x));
+      coef[j] = c;
       lse_c[j] = lse[t];
       y_c[j] = y[t];
+      // the target's own dZ entry c (1 - p_y), with p_y = exp(lp): the logit the
+      // backward recomputes is bitwise the forward's, so lp holds the same p_y
+      tgt_c[j] = c * -expm1f(lp[t]);
     } else {
       coef[j] = 0.f;
       lse_c[j] = 0.f;
       y_c[j] = -1;
+      tgt_c[j] = 0.f;
     }
   }
 }
@@ -401,7 +406,8 @@ __global__ void __launch_bounds__(kThreads, 2)
     k_dz(const T* __restrict__ W, const T* __restrict__ H_act, int64_t d, int64_t v0,
          int vs_valid, int vs, const int32_t* __restrict__ count, int64_t c0, int C, int cpad,
          int tm, int tn, const float* __restrict__ coef, const float* __restrict__ lse_c,
-         const int32_t* __restrict__ y_c, T* __restrict__ dZ, T* __restrict__ dZT) {
+         const int32_t* __restrict__ y_c, const float* __restrict__ tgt_c, T* __restrict__ dZ,
+         T* __restrict__ dZT) {
   __shared__ __attribute__((aligned(1024))) char smem[kDzLdsBytes];
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
   int n_act = count[0] - (int)c0;
@@ -450,7 +456,29 @@ __global__ void __launch_bounds__(kThreads, 2)
   }
   typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
   typedef __attribute__((ext_vector_type(4))) int i32x4_t;
-  // pass 1: stage as [token][vocab], store dZ rows (token-major, vocab contiguous)
+  typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+  typedef __attribute__((ext_vector_type(8))) short s16x8_t;
+  // 1. every entry as if it were not the target, in place: -c_t p
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    const float nc = -ct[j];
+#pragma unroll
+    for (int i = 0; i < kWM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = nc * ex2(fmaf(acc[i][j][e], kLog2e, -lb[j]));
+  }
+  if (m0 + kBM > vs_valid) {
+    // ragged last vocabulary tile of the slab: rows past it hold zeros
+#pragma unroll
+    for (int i = 0; i < kWM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (m0 + acc_row(wave, lane, i, e) >= vs_valid) {
+#pragma unroll
+          for (int j = 0; j < kWN; ++j) acc[i][j][e] = 0.f;
+        }
+  }
+  // 2. stage the tile as bf16 [token][vocab]
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
@@ -460,47 +488,48 @@ __global__ void __launch_bounds__(kThreads, 2)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int vl = acc_row(wave, lane, i, 4 * g);
-        float q[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          q[u] = dz_value<T>(acc[i][j][4 * g + u], ct[j], lb[j], m0 + vl + u, yl[j], vs_valid);
         *(bf16x4_t GRPO_LDS*)(lds + tl * kStagePitch + vl * 2) =
-            bf16x4_t{(__bf16)q[0], (__bf16)q[1], (__bf16)q[2], (__bf16)q[3]};
+            bf16x4_t{(__bf16)acc[i][j][4 * g], (__bf16)acc[i][j][4 * g + 1],
+                     (__bf16)acc[i][j][4 * g + 2], (__bf16)acc[i][j][4 * g + 3]};
       }
   }
   __syncthreads();
+  // 3. the target entry of each token, c_t (1 - p_y), if it falls in this tile
+  if (threadIdx.x < kBN) {
+    const int tl = (int)threadIdx.x;
+    const int64_t yr = (int64_t)y_c[n0 + tl] - v0 - m0;  // y_c = -1 for padding tokens
+    if (yr >= 0 && yr < kBM && m0 + yr < vs_valid)
+      *(__bf16 GRPO_LDS*)(lds + tl * kStagePitch + yr * 2) = (__bf16)tgt_c[n0 + tl];
+  }
+  __syncthreads();
+  // 4. dZ rows (token-major, vocabulary contiguous), 16 bytes per thread
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
     const int idx = it * kThreads + (int)threadIdx.x;
-    const int r = idx >> 5, c = idx & 31;          // token row, 16-byte column
+    const int r = idx >> 5, c = idx & 31;
     *(i32x4_t*)(dZ + (int64_t)(n0 + r) * vs + m0 + c * 8) =
         *(const i32x4_t GRPO_LDS*)(lds + r * kStagePitch + c * 16);
   }
-  // pass 2: stage as [vocab][token], store dZT rows (vocab-major, token contiguous)
-  __syncthreads();
+  // 5. dZT rows (vocabulary-major, token contiguous) through transposed LDS reads.
+  // A 16-lane group moves one unit of 4 vocabulary rows x 32 tokens: lane m reads
+  // the 4 entries (4 vocabulary rows) of token 8 (m & 3) + (m >> 2) (and of the
+  // token 4 further), and ds_read_b64_tr_b16 hands lane m the 4 consecutive tokens
+  // 8 (m >> 2) + 0..3 (then + 4..7) of vocabulary row m & 3.
+  {
+    const int m = lane & 15;
+    const int rd = 8 * (m & 3) + (m >> 2);
 #pragma unroll
-  for (int j = 0; j < kWN; ++j) {
-    const int tl = acc_col(wave, lane, j);
-#pragma unroll
-    for (int i = 0; i < kWM; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int vl = acc_row(wave, lane, i, 4 * g);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float q =
-              dz_value<T>(acc[i][j][4 * g + u], ct[j], lb[j], m0 + vl + u, yl[j], vs_valid);
-          *(__bf16 GRPO_LDS*)(lds + (vl + u) * kStagePitch + tl * 2) = (__bf16)q;
-        }
-      }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
-    const int idx = it * kThreads + (int)threadIdx.x;
-    const int r = idx >> 5, c = idx & 31;          // vocab row, 16-byte column
-    *(i32x4_t*)(dZT + (int64_t)(m0 + r) * cpad + n0 + c * 8) =
-        *(const i32x4_t GRPO_LDS*)(lds + r * kStagePitch + c * 16);
+    for (int it = 0; it < 16; ++it) {
+      const int u = it * 32 + wave * 4 + (lane >> 4);
+      const int quad = u >> 3, blk = u & 7;   // one wave: 4 rows x 128 tokens
+      const char GRPO_LDS* src = lds + (32 * blk + rd) * kStagePitch + quad * 8;
+      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GRPO_LDS s16x4_t*)src);
+      const s16x4_t hi =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((GRPO_LDS s16x4_t*)(src + 4 * kStagePitch));
+      const s16x8_t v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      *(i32x4_t*)(dZT + (int64_t)(m0 + 4 * quad + (m & 3)) * cpad + n0 + 32 * blk + 8 * (m >> 2)) =
+          __builtin_bit_cast(i32x4_t, v8);
+    }
   }
 }
 
@@ -712,23 +741,24 @@ hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int3
                            int64_t c0, int C, int cpad, const int32_t* y, const uint8_t* mask,
                            const float* adv, const float* ref_lp, const float* lp,
                            const float* lse, int64_t L, float beta, float grad_loss, T* H_act,
-                           float* coef, float* lse_c, int32_t* y_c, hipStream_t s) {
+                           float* coef, float* lse_c, int32_t* y_c, float* tgt_c, hipStream_t s) {
   ScopedKernelTimer timer_(KK_BWD_PREP, s);
   (void)mask;
   hipLaunchKernelGGL(k_bwd_prep<T>, dim3(cpad), dim3(256), 0, s, H, d, idx, count, c0, C, y, adv,
-                     ref_lp, lp, lse, L, beta, grad_loss, H_act, coef, lse_c, y_c);
+                     ref_lp, lp, lse, L, beta, grad_loss, H_act, coef, lse_c, y_c, tgt_c);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,
                      int vs, const int32_t* count, int64_t c0, int C, int cpad, const float* coef,
-                     const float* lse_c, const int32_t* y_c, T* dZ, T* dZT, hipStream_t s) {
+                     const float* lse_c, const int32_t* y_c, const float* tgt_c, T* dZ, T* dZT,
+                     hipStream_t s) {
   ScopedKernelTimer timer_(KK_DZ, s);
   (void)V;
   const int tm = cdiv(vs_valid, kBM), tn = cdiv(C, kBN);
   hipLaunchKernelGGL(k_dz<T>, dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0, vs_valid, vs,
-                     count, c0, C, cpad, tm, tn, coef, lse_c, y_c, dZ, dZT);
+                     count, c0, C, cpad, tm, tn, coef, lse_c, y_c, tgt_c, dZ, dZT);
   return hipGetLastError();
 }
 
@@ -799,10 +829,10 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
                                          int64_t, int, int, const int32_t*, const uint8_t*,        \
                                          const float*, const float*, const float*, const float*,  \
                                          int64_t, float, float, T*, float*, float*, int32_t*,      \
-                                         hipStream_t);                                            \
+                                         float*, hipStream_t);                                    \
   template hipError_t launch_dz<T>(const T*, const T*, int64_t, int64_t, int64_t, int, int,       \
                                    const int32_t*, int64_t, int, int, const float*, const float*, \
-                                   const int32_t*, T*, T*, hipStream_t);                          \
+                                   const int32_t*, const float*, T*, T*, hipStream_t);            \
   template hipError_t launch_dh_gemm<T>(const T*, int64_t, int64_t, int, const T*, int, int64_t,  \
                                         const int32_t*, int64_t, int, int, int, int, float*,      \
                                         hipStream_t);                                             \

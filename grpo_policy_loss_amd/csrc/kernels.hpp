@@ -49,12 +49,13 @@ hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int3
                            int64_t c0, int C, int cpad, const int32_t* y, const uint8_t* mask,
                            const float* adv, const float* ref_lp, const float* lp,
                            const float* lse, int64_t L, float beta, float grad_loss, T* H_act,
-                           float* coef, float* lse_c, int32_t* y_c, hipStream_t s);
+                           float* coef, float* lse_c, int32_t* y_c, float* tgt_c, hipStream_t s);
 
 template <typename T>
 hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,
                      int vs, const int32_t* count, int64_t c0, int C, int cpad, const float* coef,
-                     const float* lse_c, const int32_t* y_c, T* dZ, T* dZT, hipStream_t s);
+                     const float* lse_c, const int32_t* y_c, const float* tgt_c, T* dZ, T* dZT,
+                     hipStream_t s);
 
 // dH_acc holds nsplit partial buffers of [cpad, d] floats; split sp covers
 // one contiguous share of the slab's vocabulary columns.

@@ -74,6 +74,23 @@ def test_advantages_match_oracle_and_degenerate_groups():
 
 
 # ----------------------------------------------------------------------------- full chain
+def test_chain_bf16_multiple_vocab_slabs(monkeypatch):
+    """bf16 path across slabs: with a 1 MiB slab budget a 256-token chunk holds at
+    most 2048 vocabulary rows, so V = 5000 needs three slabs (the last one ragged)
+    and the targets, uniform over V, fall in every slab."""
+    _need_gpu()
+    monkeypatch.setenv("GRPO_SLAB_MIB", "1")
+    w = BASE.scaled(name="slabs-bf16", prompts=2, G=3, L=111, d=64, V=5000, dtype="bf16",
+                    chunk=256, len_lo=50, len_hi=111)
+    inp = inputs(w, seed=4)
+    g = gpu_chain(inp, w)
+    o = oracle_chain(inp, w)
+    assert abs(g["loss"].item() - o["loss"]) <= 2e-3 * abs(o["loss"])
+    for k in ("dH", "dW"):
+        assert cosine(to64(g[k]), o[k]) >= 0.999, k
+        assert max_abs_rel(to64(g[k]), o[k]) <= 1e-2, k
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("chunk", [256, 300, 4096])
 def test_chain_matches_oracle(dtype, chunk):
