@@ -147,25 +147,33 @@ def cpu_baseline(w, inp, seconds=15.0):
     mask = inp["mask"].cpu().numpy()
     r = inp["rewards"].cpu().numpy()
 
+    # per-token advantages, so a sample may end inside a sequence (seq_len 1 below)
+    adv_tok = np.repeat(oracle.group_advantages(r, w.G), w.L)
+
     def run(n):
         Hs = H[:n].double().numpy()
         Hr = H_ref[:n].double().numpy()
-        ys, ms = y[:n], mask[:n]
-        adv = oracle.group_advantages(r, w.G)[:1]
+        ys, ms, adv = y[:n], mask[:n], adv_tok[:n]
         t0 = time.perf_counter()
         ref, _ = oracle.token_logprobs(Hr, W64, ys)
-        oracle.loss_forward(Hs, W64, ys, ms, adv, ref, n, 0.04)
-        oracle.loss_backward(Hs, W64, ys, ms, adv, ref, n, 0.04)
+        oracle.loss_forward(Hs, W64, ys, ms, adv, ref, 1, 0.04)
+        oracle.loss_backward(Hs, W64, ys, ms, adv, ref, 1, 0.04)
         return time.perf_counter() - t0
 
-    n = min(16, w.L)
-    t = run(n)
-    n2 = int(max(16, min(w.L, 4096, n * seconds / max(t, 1e-3))))
-    t2 = run(n2)
+    # size the sample to about `seconds` of work: small runs carry fixed costs, so
+    # rescale from each measured run until one lands within half of the target
+    cap = min(w.N, 8192)
+    n, t = 16, run(16)
+    for _ in range(3):
+        if t >= 0.5 * seconds or n >= cap:
+            break
+        n = int(max(16, min(cap, n * seconds / max(t, 1e-3))))
+        t = run(n)
+    n2, t2 = n, t
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     return {"value": n2 / t2, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n2} flattened tokens of sequence 0 (ref + fwd + bwd, float64 "
+            "sample": f"first {n2} flattened tokens of the batch (ref + fwd + bwd, float64 "
                       f"NumPy, full V={w.V}, d={w.d}); {t2:.1f} s on "
                       f"{len(os.sched_getaffinity(0))} visible host CPUs"}
 
