@@ -86,7 +86,7 @@ int64_t slab_bytes() {
   const long long mib = e ? atoll(e) : 0;
   return mib > 0 ? (int64_t)mib << 20 : kSlabBytesDefault;
 }
-constexpr int64_t kCUs = 256;  // MI355X compute units (one 512-thread workgroup each)
+constexpr int64_t kCUs = 256;  // MI355X compute units (one GEMM workgroup each: 128 KB LDS, 4 full-register waves)
 
 struct BwdPlan {
   int64_t C, cpad, vpad, vs, nslabs, nchunks, nsplit;
@@ -105,7 +105,7 @@ BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
   vs_max = std::min<int64_t>(vs_max, p.vpad);
   // Split the dH GEMM's vocabulary range when its tile grid alone cannot fill the
   // chip: pick the split count (1..8) whose launch wastes the least of its last
-  // wave of workgroups (one 512-thread workgroup per CU), preferring fewer splits.
+  // wave of workgroups (one GEMM workgroup per CU), preferring fewer splits.
   const int64_t ct = p.cpad / 256, dt = (d + 255) / 256;
   const int64_t dh_tiles = dt * ct;
   p.nsplit = 1;

@@ -114,7 +114,7 @@ __global__ void __launch_bounds__(64) k_advantages(const float* __restrict__ r, 
 
 // ---------------------------------------------------------------- forward tile
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, 1)
     k_lse_partials(const T* __restrict__ W, const T* __restrict__ H, const int32_t* __restrict__ y,
                    int64_t V, int64_t d, int n_tok, int cpad, int tm, int tn,
                    float* __restrict__ part_m, float* __restrict__ part_s,
@@ -130,38 +130,42 @@ __global__ void __launch_bounds__(kThreads, 2)
   const Operand A{(const char*)(W + m0 * d), rowb, mvalid, rowb};
   const Operand B{(const char*)(H + (int64_t)n0 * d), rowb, n_tok - n0, rowb};
 
-  f32x16_t acc[kWM][kWN];
+  Acc acc;
   tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm0 = (wave >> 2) * 128;
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int wm0 = (wave >> 1) * 128;
   const bool full = mvalid >= wm0 + 128;
 
+  // per token column j of this lane: (max, sum exp) over its 32 vocabulary rows
   float mx[kWN], sm[kWN];
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
     float m = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kWM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
+      for (int e = 0; e < kAcc; ++e)
         if (full || acc_row(wave, lane, i, e) < mvalid) m = fmaxf(m, acc[i][j][e]);
     const float mb = m * kLog2e;
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kWM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
+      for (int e = 0; e < kAcc; ++e)
         if (full || acc_row(wave, lane, i, e) < mvalid) s += ex2(fmaf(acc[i][j][e], kLog2e, -mb));
     mx[j] = m;
     sm[j] = s;
   }
-  // lanes l and l ^ 32 hold the same token column
+  // the four 16-lane groups of a wave hold the same token columns
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
-    const float om = __shfl_xor(mx[j], 32, 64);
-    const float os = __shfl_xor(sm[j], 32, 64);
-    lse_combine(mx[j], sm[j], om, os);
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+      const float om = __shfl_xor(mx[j], o, 64);
+      const float os = __shfl_xor(sm[j], o, 64);
+      lse_combine(mx[j], sm[j], om, os);
+    }
   }
 
   // target logit: exactly one lane of the grid holds z[t][y_t]
@@ -170,23 +174,23 @@ __global__ void __launch_bounds__(kThreads, 2)
     const int t = n0 + acc_col(wave, lane, j);
     if (t < n_tok) {
       const int r = y[t] - (int)(m0 + wm0);
-      if (r >= 0 && r < 128 && r < mvalid - wm0 && ((r >> 2) & 1) == (lane >> 5)) {
-        const int ti = r >> 5, te = ((r >> 3) & 3) * 4 + (r & 3);
+      if (r >= 0 && r < 128 && r < mvalid - wm0 && ((r >> 2) & 3) == (lane >> 4)) {
+        const int ti = r >> 4, te = r & 3;
         float v = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < kWM; ++i)
 #pragma unroll
-          for (int e = 0; e < 16; ++e)
+          for (int e = 0; e < kAcc; ++e)
             if (i == ti && e == te) v = acc[i][j][e];
         zy[t] = v;
       }
     }
   }
 
-  // combine the two waves that share token columns (w and w + 4), through LDS
+  // combine the two waves that share token columns (w and w + 2), through LDS
   __syncthreads();
   float* red = (float*)smem;  // [256 token columns] max, then [256] sums
-  if ((wave >> 2) == 1 && lane < 32) {
+  if ((wave >> 1) == 1 && lane < 16) {
 #pragma unroll
     for (int j = 0; j < kWN; ++j) {
       red[acc_col(wave, lane, j)] = mx[j];
@@ -194,7 +198,7 @@ __global__ void __launch_bounds__(kThreads, 2)
     }
   }
   __syncthreads();
-  if ((wave >> 2) == 0 && lane < 32) {
+  if ((wave >> 1) == 0 && lane < 16) {
 #pragma unroll
     for (int j = 0; j < kWN; ++j) {
       const int c = acc_col(wave, lane, j);
@@ -402,7 +406,7 @@ __device__ __forceinline__ float dz_value(float z, float ct, float lb, int64_t v
 }
 
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, 1)
     k_dz(const T* __restrict__ W, const T* __restrict__ H_act, int64_t d, int64_t v0,
          int vs_valid, int vs, const int32_t* __restrict__ count, int64_t c0, int C, int cpad,
          int tm, int tn, const float* __restrict__ coef, const float* __restrict__ lse_c,
@@ -420,10 +424,10 @@ __global__ void __launch_bounds__(kThreads, 2)
   const uint32_t rowb = (uint32_t)(d * (int64_t)sizeof(T));
   const Operand A{(const char*)(W + (v0 + m0) * d), rowb, vs_valid - m0, rowb};
   const Operand B{(const char*)(H_act + (int64_t)n0 * d), rowb, n_act - n0, rowb};
-  f32x16_t acc[kWM][kWN];
+  Acc acc;
   tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   float ct[kWN], lb[kWN];
   int64_t yl[kWN];
 #pragma unroll
@@ -439,18 +443,16 @@ __global__ void __launch_bounds__(kThreads, 2)
     for (int j = 0; j < kWN; ++j) {
       const int t = n0 + acc_col(wave, lane, j);
 #pragma unroll
-      for (int i = 0; i < kWM; ++i)
+      for (int i = 0; i < kWM; ++i) {
+        const int v = m0 + acc_row(wave, lane, i, 0);
+        float q[kAcc];
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int v = m0 + acc_row(wave, lane, i, 4 * g);
-          float q[4];
+        for (int u = 0; u < kAcc; ++u)
+          q[u] = dz_value<T>(acc[i][j][u], ct[j], lb[j], v + u, yl[j], vs_valid);
+        store4(dZ + (int64_t)t * vs + v, q[0], q[1], q[2], q[3]);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            q[u] = dz_value<T>(acc[i][j][4 * g + u], ct[j], lb[j], v + u, yl[j], vs_valid);
-          store4(dZ + (int64_t)t * vs + v, q[0], q[1], q[2], q[3]);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) dZT[(int64_t)(v + u) * cpad + t] = to_elem<T>(q[u]);
-        }
+        for (int u = 0; u < kAcc; ++u) dZT[(int64_t)(v + u) * cpad + t] = to_elem<T>(q[u]);
+      }
     }
     return;
   }
@@ -465,46 +467,44 @@ __global__ void __launch_bounds__(kThreads, 2)
 #pragma unroll
     for (int i = 0; i < kWM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = nc * ex2(fmaf(acc[i][j][e], kLog2e, -lb[j]));
+      for (int e = 0; e < kAcc; ++e) acc[i][j][e] = nc * ex2(fmaf(acc[i][j][e], kLog2e, -lb[j]));
   }
   if (m0 + kBM > vs_valid) {
     // ragged last vocabulary tile of the slab: rows past it hold zeros
 #pragma unroll
     for (int i = 0; i < kWM; ++i)
 #pragma unroll
-      for (int e = 0; e < 16; ++e)
+      for (int e = 0; e < kAcc; ++e)
         if (m0 + acc_row(wave, lane, i, e) >= vs_valid) {
 #pragma unroll
           for (int j = 0; j < kWN; ++j) acc[i][j][e] = 0.f;
         }
   }
-  // 2. stage the tile as bf16 [token][vocab]
+  // 2. stage the tile as bf16 [token][vocab]: each lane holds 4 consecutive
+  // vocabulary rows of one token per block
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
     const int tl = acc_col(wave, lane, j);
 #pragma unroll
-    for (int i = 0; i < kWM; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int vl = acc_row(wave, lane, i, 4 * g);
-        *(bf16x4_t GRPO_LDS*)(lds + tl * kStagePitch + vl * 2) =
-            bf16x4_t{(__bf16)acc[i][j][4 * g], (__bf16)acc[i][j][4 * g + 1],
-                     (__bf16)acc[i][j][4 * g + 2], (__bf16)acc[i][j][4 * g + 3]};
-      }
+    for (int i = 0; i < kWM; ++i) {
+      const int vl = acc_row(wave, lane, i, 0);
+      *(bf16x4_t GRPO_LDS*)(lds + tl * kStagePitch + vl * 2) =
+          bf16x4_t{(__bf16)acc[i][j][0], (__bf16)acc[i][j][1], (__bf16)acc[i][j][2],
+                   (__bf16)acc[i][j][3]};
+    }
   }
   __syncthreads();
   // 3. the target entry of each token, c_t (1 - p_y), if it falls in this tile
-  if (threadIdx.x < kBN) {
-    const int tl = (int)threadIdx.x;
+  for (int tl = (int)threadIdx.x; tl < kBN; tl += kThreads) {
     const int64_t yr = (int64_t)y_c[n0 + tl] - v0 - m0;  // y_c = -1 for padding tokens
     if (yr >= 0 && yr < kBM && m0 + yr < vs_valid)
       *(__bf16 GRPO_LDS*)(lds + tl * kStagePitch + yr * 2) = (__bf16)tgt_c[n0 + tl];
   }
   __syncthreads();
   // 4. dZ rows (token-major, vocabulary contiguous), 16 bytes per thread
-#pragma unroll
-  for (int it = 0; it < 16; ++it) {
+#pragma unroll 8
+  for (int it = 0; it < kBN * 32 / kThreads; ++it) {
     const int idx = it * kThreads + (int)threadIdx.x;
     const int r = idx >> 5, c = idx & 31;
     *(i32x4_t*)(dZ + (int64_t)(n0 + r) * vs + m0 + c * 8) =
@@ -518,9 +518,10 @@ __global__ void __launch_bounds__(kThreads, 2)
   {
     const int m = lane & 15;
     const int rd = 8 * (m & 3) + (m >> 2);
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int u = it * 32 + wave * 4 + (lane >> 4);
+    constexpr int kGroups = kThreads / 16;   // 16-lane groups in the workgroup
+#pragma unroll 8
+    for (int it = 0; it < 512 / kGroups; ++it) {
+      const int u = it * kGroups + wave * 4 + (lane >> 4);
       const int quad = u >> 3, blk = u & 7;   // one wave: 4 rows x 128 tokens
       const char GRPO_LDS* src = lds + (32 * blk + rd) * kStagePitch + quad * 8;
       const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GRPO_LDS s16x4_t*)src);
@@ -537,7 +538,7 @@ __global__ void __launch_bounds__(kThreads, 2)
 // sp accumulates into its own buffer dH_acc[sp], so no two workgroups ever
 // write the same element and the final sum over splits has a fixed order.
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, 1)
     k_dh_gemm(const T* __restrict__ WT, int64_t vpad, int64_t v0, int vs_valid,
               const T* __restrict__ dZ, int vs, int64_t d, const int32_t* __restrict__ count,
               int64_t c0, int C, int cpad, int tm, int tn, int nsplit, int kchunk, int first,
@@ -562,33 +563,30 @@ __global__ void __launch_bounds__(kThreads, 2)
                   (int)((d - m0) < kBM ? (d - m0) : kBM), kb};
   const Operand B{(const char*)(dZ + (int64_t)n0 * vs + k0), (uint32_t)(vs * (int64_t)sizeof(T)),
                   n_act - n0, kb};
-  f32x16_t acc[kWM][kWN];
+  Acc acc;
   tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
   if (klen == 0 && !first) return;
 
   float* out = dH_acc + (int64_t)sp * cpad * d;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
     const int t = n0 + acc_col(wave, lane, j);
     if (t >= n_act) continue;
 #pragma unroll
-    for (int i = 0; i < kWM; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t nd = m0 + acc_row(wave, lane, i, 4 * g);
-        if (nd >= d) continue;
-        f32x4_t* p = (f32x4_t*)(out + (int64_t)t * d + nd);
-        f32x4_t v{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                  acc[i][j][4 * g + 3]};
-        if (!first) v += *p;
-        *p = v;
-      }
+    for (int i = 0; i < kWM; ++i) {
+      const int64_t nd = m0 + acc_row(wave, lane, i, 0);   // 4 consecutive d
+      if (nd >= d) continue;
+      f32x4_t* p = (f32x4_t*)(out + (int64_t)t * d + nd);
+      f32x4_t v = acc[i][j];
+      if (!first) v += *p;
+      *p = v;
+    }
   }
 }
 
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, 1)
     k_dw_gemm(const T* __restrict__ HT, int cpad, const T* __restrict__ dZT, int64_t d,
               int64_t v0, int vs_valid, const int32_t* __restrict__ count, int64_t c0, int C,
               int tm, int tn, float* __restrict__ dW) {
@@ -605,24 +603,21 @@ __global__ void __launch_bounds__(kThreads, 2)
   const uint32_t ldb = (uint32_t)(cpad * (int64_t)sizeof(T));
   const Operand A{(const char*)(HT + m0 * cpad), ldb, (int)((d - m0) < kBM ? (d - m0) : kBM), kb};
   const Operand B{(const char*)(dZT + (int64_t)n0 * cpad), ldb, vs_valid - n0, kb};
-  f32x16_t acc[kWM][kWN];
+  Acc acc;
   tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
     const int v = n0 + acc_col(wave, lane, j);
     if (v >= vs_valid) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int64_t nd = m0 + acc_row(wave, lane, i, 4 * g);
-        if (nd >= d) continue;
-        f32x4_t* p = (f32x4_t*)(dW + (v0 + v) * d + nd);
-        *p += f32x4_t{acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                      acc[i][j][4 * g + 3]};
-      }
+    for (int i = 0; i < kWM; ++i) {
+      const int64_t nd = m0 + acc_row(wave, lane, i, 0);   // 4 consecutive d
+      if (nd >= d) continue;
+      f32x4_t* p = (f32x4_t*)(dW + (v0 + v) * d + nd);
+      *p += acc[i][j];
+    }
   }
 }
 
@@ -653,7 +648,7 @@ __global__ void __launch_bounds__(256) k_zero(int4* __restrict__ p, int64_t n16,
 }
 
 template <typename T>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, 1)
     k_gemm_nt(const T* __restrict__ A, const T* __restrict__ B, int64_t M, int64_t N, int64_t K,
               int tm, int tn, float* __restrict__ C) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -664,15 +659,15 @@ __global__ void __launch_bounds__(kThreads, 2)
   const uint32_t rowb = (uint32_t)(K * (int64_t)sizeof(T));
   const Operand Ao{(const char*)(A + m0 * K), rowb, (int)((M - m0) < kBM ? (M - m0) : kBM), rowb};
   const Operand Bo{(const char*)(B + n0 * K), rowb, (int)((N - n0) < kBN ? (N - n0) : kBN), rowb};
-  f32x16_t acc[kWM][kWN];
+  Acc acc;
   tile_mainloop<T>(acc, Ao, Bo, (int)((rowb + kBKB - 1) / kBKB), lds);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kWM; ++i)
 #pragma unroll
     for (int j = 0; j < kWN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < kAcc; ++e) {
         const int64_t m = m0 + acc_row(wave, lane, i, e), n = n0 + acc_col(wave, lane, j);
         if (m < M && n < N) C[m * N + n] = acc[i][j][e];
       }

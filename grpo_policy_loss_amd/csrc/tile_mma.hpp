@@ -5,25 +5,28 @@
 // along k), on gfx950 (CDNA4) matrix cores.
 //
 // Layout and schedule:
-//  * 512 threads = 8 wave64s, two per SIMD (waves w and w + 4 share a SIMD),
-//    in a 2 (M) x 4 (N) grid; each wave owns 128 x 64 of the tile as 4 x 2
-//    blocks of the 32 x 32 MFMA output (128 accumulator registers per lane).
-//    Two waves per SIMD let one wave's LDS or barrier stalls be covered by
-//    the other's MFMAs, while all eight share one 256 x 256 tile (the tile
-//    size sets the L2 -> LDS traffic per flop).
-//  * K advances in 128-byte slices (64 bf16 or 32 f32).  Each slice of A and
-//    B (256 rows x 128 B = 32 KB each) is copied global -> LDS by the buffer
-//    unit directly (buffer_load_dwordx4 ... lds): no VGPR staging.  LDS is
-//    double buffered (2 x 64 KB), so the copy of slice k+1 runs while the
-//    matrix cores consume slice k.
-//  * Only waves 0..3 (one per SIMD) issue those copies.  Issuing a copy can
-//    hold a wave for many cycles while the address unit drains; when both
-//    waves of a SIMD did it at once (right after the slice barrier) the
-//    matrix core sat idle.  With one copying wave per SIMD, its partner's
-//    MFMAs keep the matrix core busy meanwhile (measured: +2.5 to +5 points
-//    of bf16 peak on 8k-16k GEMMs).
-//  * MFMA operand fragments are double buffered in registers: the LDS reads
-//    of k-step s+1 are issued between the MFMAs of k-step s.
+//  * 256 threads = 4 wave64s, one per SIMD, in a 2 (M) x 2 (N) grid; each wave
+//    owns 128 x 128 of the tile as 8 x 8 blocks of the 16 x 16 MFMA output
+//    (256 accumulator registers per lane, which the compiler keeps in AGPRs).
+//    The 128 x 128 wave tile needs a third less LDS fragment traffic than
+//    eight 128 x 64 wave tiles, and that data movement costs clock: the chip
+//    is power-limited under this load.
+//  * K advances in 128-byte slices (64 bf16 or 32 f32), two k-steps of 64 bytes
+//    each.  Each slice of A and B (256 rows x 128 B = 32 KB each) is copied
+//    global -> LDS by the buffer unit directly (buffer_load_dwordx4 ... lds):
+//    no VGPR staging.  LDS is double buffered (2 x 64 KB).
+//  * Every instruction of a k-step is placed by hand (scheduling fences): the
+//    64 MFMAs of the step, one LDS fragment read for the next k-step after each
+//    even MFMA of its first half, and -- in the step after the slice barrier --
+//    one slice copy after every fourth MFMA.  Left to itself the compiler
+//    clusters the copies (each needs its own M0 write) and the matrix core
+//    idles; the fixed order measured +8 points of bf16 peak over the
+//    compiler's schedule of the same loop.
+//  * Slice barrier after the first k-step: every wave then holds the slice's
+//    last fragments, so the stage is free for the copy of slice kt + 2, and
+//    (after each wave's own vmcnt wait) slice kt + 1 is visible.  Copies of
+//    slice kt + 2 go out during the second k-step of slice kt and are waited
+//    for one k-step later at the earliest.
 //  * Out-of-range rows and k-columns read as zero: each operand is addressed
 //    through a buffer resource whose range ends at its last valid row, and an
 //    invalid row or column gets an offset past that range.  Tails in M, N
@@ -32,14 +35,14 @@
 //    covers 16 lanes = 16 rows of a fragment.  The eight 16-byte chunks of a
 //    128-byte LDS row are XOR-swizzled by f(r) = (r & 7) ^ ((r >> 3) & 1), so
 //    any 16 consecutive rows at one logical chunk hit 16 distinct bank groups.
-//  * bf16: v_mfma_f32_32x32x16_bf16, one per 16-byte chunk pair.
-//    f32:  v_mfma_f32_32x32x2_f32, four per chunk pair; lane l supplies
-//          element e of its 4-float chunk as its k = l/32 operand, so the
-//          four MFMAs together cover the 8 k of the pair.
+//  * bf16: v_mfma_f32_16x16x32_bf16; lane l supplies row l % 16 of A (of B)
+//          and the 16-byte chunk l / 16 of the 64-byte k-step.
+//    f32:  v_mfma_f32_16x16x4_f32, four per k-step; lane l supplies element e
+//          of its 4-float chunk l / 16 to MFMA e, so the four MFMAs together
+//          cover the 16 k of the step (in a permuted k order that A and B share).
 //
-// Output register layout (for both MFMAs): lane l of wave w, block (i, j),
-// element e holds C[128 (w / 4) + 32 i + 8 (e / 4) + 4 (l / 32) + e % 4]
-//                  [64 (w % 4) + 32 j + l % 32].
+// Output register layout (both MFMAs): lane l of wave w, block (i, j),
+// element e holds C[128 (w / 2) + 16 i + 4 (l / 16) + e][128 (w % 2) + 16 j + l % 16].
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -49,16 +52,16 @@ namespace grpo {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 #define GRPO_LDS __attribute__((address_space(3)))
 
 constexpr int kBM = 256;          // tile rows (A rows)
 constexpr int kBN = 256;          // tile cols (B rows)
 constexpr int kBKB = 128;         // K slice in bytes
-constexpr int kThreads = 512;
-constexpr int kWM = 4;           // 32-row MFMA blocks per wave
-constexpr int kWN = 2;           // 32-col MFMA blocks per wave
+constexpr int kThreads = 256;
+constexpr int kWM = 8;            // 16-row MFMA blocks per wave
+constexpr int kWN = 8;            // 16-col MFMA blocks per wave
+constexpr int kAcc = 4;           // accumulator values per block and lane
 constexpr int kTileBytes = kBM * kBKB;   // one operand slice in LDS: 32 KB
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kLdsBytes = 2 * kStageBytes;  // double buffered A + B: 128 KB
@@ -68,6 +71,8 @@ constexpr uint32_t kOOB = 0x80000000u;   // an offset past every resource range
 // measured +1 to +3 points of bf16 peak on the tile GEMM.  (nt, the streaming hint,
 // costs 6 points: the L2 then stops keeping panels that neighbouring CUs reuse.)
 constexpr int kCopyPolicy = 16;
+
+typedef f32x4_t Acc[kWM][kWN];
 
 // Raw buffer resource: base, no stride, `bytes` valid bytes from base.  The
 // inputs are workgroup-uniform; readfirstlane makes that visible to the
@@ -93,9 +98,8 @@ struct Operand {
   uint32_t k_bytes;      // valid k extent in bytes (multiple of 16)
 };
 
-// Waves 0..3 each copy 64 rows of an operand slice: 8 DMA instructions, each
-// moving 8 rows x 128 B (lane i fills slot i & 7 of row i >> 3).  Waves 4..7
-// copy nothing (their issue() is empty).
+// Each wave copies 64 rows of an operand slice: 8 DMA instructions, each
+// moving 8 rows x 128 B (lane i fills slot i & 7 of row i >> 3 of the group).
 struct Loader {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t rowoff[8];       // byte offset of each of this lane's 8 rows (kOOB if absent)
@@ -111,27 +115,23 @@ struct Loader {
     chunk_bytes_odd = chunk_bytes ^ 16u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      int r = (wave & 3) * 64 + j * 8 + r_in;
+      int r = wave * 64 + j * 8 + r_in;
       rowoff[j] = r < rv ? (uint32_t)r * op.ld_bytes : kOOB;
     }
     k_bytes = op.k_bytes;
   }
 
-  // Issue the 8 direct-to-LDS copies of this wave's 64 rows of slice `kt`
-  // (waves 0..3 only).
+  // Copy instruction j (rows 8 j .. 8 j + 7 of this wave's 64) of slice `kt`.
+  // A slice past the end reads as zeros.
+  __device__ __forceinline__ void issue1(int kt, int j, char GRPO_LDS* tile, int wave) const {
+    const uint32_t kb = (uint32_t)kt * kBKB + ((j & 1) ? chunk_bytes_odd : chunk_bytes);
+    const uint32_t off = kb < k_bytes ? rowoff[j] + kb : kOOB;
+    char GRPO_LDS* dst = tile + (wave * 64 + j * 8) * kBKB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, off, 0, 0, kCopyPolicy);
+  }
   __device__ __forceinline__ void issue(int kt, char GRPO_LDS* tile, int wave) const {
-    if (wave >= 4) return;
-    const uint32_t kb0 = (uint32_t)kt * kBKB + chunk_bytes;
-    const uint32_t kb1 = (uint32_t)kt * kBKB + chunk_bytes_odd;
-    const bool kok0 = kb0 < k_bytes, kok1 = kb1 < k_bytes;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t kb = (j & 1) ? kb1 : kb0;
-      const bool kok = (j & 1) ? kok1 : kok0;
-      uint32_t off = kok ? rowoff[j] + kb : kOOB;
-      char GRPO_LDS* dst = tile + (wave * 64 + j * 8) * kBKB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, off, 0, 0, kCopyPolicy);
-    }
+    for (int j = 0; j < 8; ++j) issue1(kt, j, tile, wave);
   }
 };
 
@@ -142,140 +142,121 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 __device__ __forceinline__ void wait_vmem_but_one_slice() { __builtin_amdgcn_s_waitcnt(0x0F70 | 0x4000); }
 __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+#define GRPO_FENCE() __builtin_amdgcn_sched_barrier(0)
+
 template <typename T> struct Frag;
 template <> struct Frag<__bf16> { typedef bf16x8_t type; };
 template <> struct Frag<float> { typedef f32x4_t type; };
 
-template <typename T>
-__device__ __forceinline__ void load_frags(typename Frag<T>::type (&a)[4], typename Frag<T>::type (&b)[kWN],
-                                           const char GRPO_LDS* buf, const uint32_t (&aoff)[4],
-                                           const uint32_t (&boff)[kWN], uint32_t swz) {
+__device__ __forceinline__ f32x4_t mfma_block(f32x4_t c, const bf16x8_t& a, const bf16x8_t& b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_block(f32x4_t c, const f32x4_t& a, const f32x4_t& b) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+// One 64-byte k-step of the wave's 8 x 8 blocks, in a fixed order.  After
+// block q: for READ and even q < 32, LDS read q / 2 of the next k-step's
+// fragments (a0..a7, then b0..b7) from stage `rst` at chunk offset `sw`; for
+// COPY and q % 4 == 3, copy instruction q / 4 of slice `ckt` into stage `cst`
+// (A rows for q / 4 < 8, then B rows).
+template <typename T, bool READ, bool COPY>
+__device__ __forceinline__ void kstep(Acc& acc, const typename Frag<T>::type (&a)[kWM],
+                                      const typename Frag<T>::type (&b)[kWN],
+                                      typename Frag<T>::type (&na)[kWM], typename Frag<T>::type (&nb)[kWN],
+                                      const char GRPO_LDS* rst, uint32_t abase, uint32_t bbase,
+                                      uint32_t sw, const Loader& la, const Loader& lb, int ckt,
+                                      char GRPO_LDS* cst, int wave) {
   typedef typename Frag<T>::type F;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) a[i] = *(const F GRPO_LDS*)(buf + aoff[i] + swz);
-#pragma unroll
-  for (int j = 0; j < kWN; ++j) b[j] = *(const F GRPO_LDS*)(buf + kTileBytes + boff[j] + swz);
-}
-
-__device__ __forceinline__ void mfma_all(f32x16_t (&acc)[4][kWN], const bf16x8_t (&a)[4], const bf16x8_t (&b)[kWN]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < kWN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-}
-__device__ __forceinline__ void mfma_all(f32x16_t (&acc)[4][kWN], const f32x4_t (&a)[4], const f32x4_t (&b)[kWN]) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < kWN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i][e], b[j][e], acc[i][j], 0, 0, 0);
-}
-
-// Scheduling hint: alternate one MFMA and one LDS read, n times.
-#define GRPO_SCHED_MFMA_DS(n)                                  \
-  _Pragma("unroll") for (int q_ = 0; q_ < (n); ++q_) {          \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          \
+  for (int q = 0; q < kWM * kWN; ++q) {
+    const int i = q / kWN, j = q % kWN;
+    acc[i][j] = mfma_block(acc[i][j], a[i], b[j]);
+    GRPO_FENCE();
+    if (READ && (q & 1) == 0 && q < 32) {
+      const int f = q >> 1;
+      if (f < kWM) na[f] = *(const F GRPO_LDS*)(rst + abase + f * 16 * kBKB + sw);
+      else nb[f - kWM] = *(const F GRPO_LDS*)(rst + kTileBytes + bbase + (f - kWM) * 16 * kBKB + sw);
+      GRPO_FENCE();
+    }
+    if (COPY && (q & 3) == 3) {
+      const int c = q >> 2;
+      if (c < 8) la.issue1(ckt, c, cst, wave);
+      else lb.issue1(ckt, c - 8, cst + kTileBytes, wave);
+      GRPO_FENCE();
+    }
   }
+}
 
-// The main loop.  `lds` must be kLdsBytes of workgroup memory.  On return
-// the caller must barrier before reusing LDS.
+// The main loop.  `lds` must be kLdsBytes of workgroup memory.  On return no
+// copy is in flight; the caller must barrier before reusing LDS.
 template <typename T>
-__device__ __forceinline__ void tile_mainloop(f32x16_t (&acc)[4][kWN], const Operand& A,
-                                              const Operand& B, int k_slices,
-                                              char GRPO_LDS* lds) {
+__device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const Operand& B,
+                                              int k_slices, char GRPO_LDS* lds) {
   typedef typename Frag<T>::type F;
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int wm0 = (wave >> 2) * 128;
-  const int wn0 = (wave & 3) * 64;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < kWM; ++i)
 #pragma unroll
     for (int j = 0; j < kWN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < kAcc; ++e) acc[i][j][e] = 0.f;
+  if (k_slices <= 0) return;
   Loader la, lb;
   la.init(A, wave, lane);
   lb.init(B, wave, lane);
-  uint32_t aoff[4], boff[kWN];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) aoff[i] = (uint32_t)(wm0 + 32 * i + (lane & 31)) * kBKB;
-#pragma unroll
-  for (int j = 0; j < kWN; ++j) boff[j] = (uint32_t)(wn0 + 32 * j + (lane & 31)) * kBKB;
-  const uint32_t half = (uint32_t)(lane >> 5);
-  const uint32_t r7 = (uint32_t)((lane & 7) ^ ((lane >> 3) & 1));
-  uint32_t swz[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) swz[s] = (((2u * s + half) ^ r7) << 4);
-  if (k_slices <= 0) return;
+  const uint32_t abase = (uint32_t)((wave >> 1) * 128 + (lane & 15)) * kBKB;
+  const uint32_t bbase = (uint32_t)((wave & 1) * 128 + (lane & 15)) * kBKB;
+  // fragment rows are 16-aligned blocks + lane % 16, so f(row) depends on the lane only
+  const uint32_t fr = (uint32_t)((lane & 7) ^ ((lane >> 3) & 1));
+  const uint32_t sw0 = ((0u + (uint32_t)(lane >> 4)) ^ fr) << 4;
+  const uint32_t sw1 = ((4u + (uint32_t)(lane >> 4)) ^ fr) << 4;
 
+  // slices 0 and 1 (slice 1 reads as zeros when there is none)
   la.issue(0, lds, wave);
   lb.issue(0, lds + kTileBytes, wave);
-  if (k_slices > 1) {
-    la.issue(1, lds + kStageBytes, wave);
-    lb.issue(1, lds + kStageBytes + kTileBytes, wave);
-    wait_vmem_but_one_slice();
-  } else {
-    wait_vmem_all();
-  }
+  la.issue(1, lds + kStageBytes, wave);
+  lb.issue(1, lds + kStageBytes + kTileBytes, wave);
+  wait_vmem_but_one_slice();
   __builtin_amdgcn_s_barrier();
-  F fa[2][4], fb[2][kWN];
-  load_frags<T>(fa[0], fb[0], lds, aoff, boff, swz[0]);
+  F fa0[kWM], fb0[kWN], fa1[kWM], fb1[kWN];
+#pragma unroll
+  for (int f = 0; f < kWM; ++f) fa0[f] = *(const F GRPO_LDS*)(lds + abase + f * 16 * kBKB + sw0);
+#pragma unroll
+  for (int f = 0; f < kWN; ++f)
+    fb0[f] = *(const F GRPO_LDS*)(lds + kTileBytes + bbase + f * 16 * kBKB + sw0);
 
-  // Steady state: every slice but the last.  The slice barrier sits after the
-  // third k-step, once every wave holds the slice's last fragments in
-  // registers: the stage is then free for the copy of slice kt + 2, and after
-  // the copying waves' vmcnt wait slice kt + 1 is visible, so its first
-  // fragments load under the fourth k-step's MFMAs instead of after the barrier.
-  for (int kt = 0; kt + 1 < k_slices; ++kt) {
+  int kt = 0;
+  for (; kt + 1 < k_slices; ++kt) {
     char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
     char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    load_frags<T>(fa[1], fb[1], cur, aoff, boff, swz[1]);
-    mfma_all(acc, fa[0], fb[0]);
-    GRPO_SCHED_MFMA_DS(6);
-    load_frags<T>(fa[0], fb[0], cur, aoff, boff, swz[2]);
-    mfma_all(acc, fa[1], fb[1]);
-    GRPO_SCHED_MFMA_DS(6);
-    load_frags<T>(fa[1], fb[1], cur, aoff, boff, swz[3]);
-    mfma_all(acc, fa[0], fb[0]);
-    GRPO_SCHED_MFMA_DS(6);
-    wait_vmem_all();
+    // k-step 0: read k-step 1's fragments of this slice
+    kstep<T, true, false>(acc, fa0, fb0, fa1, fb1, cur, abase, bbase, sw1, la, lb, 0, cur, wave);
+    wait_vmem_all();   // this wave's copies of slice kt + 1 have landed
     wait_lds_all();
     __builtin_amdgcn_s_barrier();
-    if (kt + 2 < k_slices) {
-      la.issue(kt + 2, cur, wave);
-      lb.issue(kt + 2, cur + kTileBytes, wave);
-    }
-    load_frags<T>(fa[0], fb[0], nxt, aoff, boff, swz[0]);
-    mfma_all(acc, fa[1], fb[1]);
-    GRPO_SCHED_MFMA_DS(6);
+    GRPO_FENCE();
+    // k-step 1: read slice kt + 1's first fragments; copy slice kt + 2 into this
+    // slice's stage (zeros past the end, drained below)
+    kstep<T, true, true>(acc, fa1, fb1, fa0, fb0, nxt, abase, bbase, sw0, la, lb, kt + 2, cur, wave);
   }
-  // last slice: no copy left to wait for
   {
-    char GRPO_LDS* cur = lds + ((k_slices - 1) & 1) * kStageBytes;
-    load_frags<T>(fa[1], fb[1], cur, aoff, boff, swz[1]);
-    mfma_all(acc, fa[0], fb[0]);
-    GRPO_SCHED_MFMA_DS(6);
-    load_frags<T>(fa[0], fb[0], cur, aoff, boff, swz[2]);
-    mfma_all(acc, fa[1], fb[1]);
-    GRPO_SCHED_MFMA_DS(6);
-    load_frags<T>(fa[1], fb[1], cur, aoff, boff, swz[3]);
-    mfma_all(acc, fa[0], fb[0]);
-    GRPO_SCHED_MFMA_DS(6);
-    mfma_all(acc, fa[1], fb[1]);
+    char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
+    kstep<T, true, false>(acc, fa0, fb0, fa1, fb1, cur, abase, bbase, sw1, la, lb, 0, cur, wave);
+    kstep<T, false, false>(acc, fa1, fb1, fa0, fb0, cur, abase, bbase, sw0, la, lb, 0, cur, wave);
   }
+  wait_vmem_all();
 }
 
 // Coordinates of accumulator element (i, j, e) of this lane, tile-relative.
 __device__ __forceinline__ int acc_row(int wave, int lane, int i, int e) {
-  return (wave >> 2) * 128 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+  return (wave >> 1) * 128 + 16 * i + 4 * (lane >> 4) + e;
 }
 __device__ __forceinline__ int acc_col(int wave, int lane, int j) {
-  return (wave & 3) * 64 + 32 * j + (lane & 31);
+  return (wave & 1) * 128 + 16 * j + (lane & 15);
 }
 
 }  // namespace grpo
