@@ -1,0 +1,129 @@
+"""Planted mistakes: each case edits the oracle's own source (one plausible slip:
+a dropped term, a wrong sign, index or estimator, a transposed or misaligned
+operand), loads the edited copy in place of the oracle, and runs every pin of
+tests/test_oracle_pins.py against it.  At least one pin must fail for every
+case, and the unedited source must pass them all.  CPU only; the edits live
+in memory, never on disk."""
+import inspect
+import os
+import types
+
+import pytest
+
+import oracle
+import oracle.grpo_oracle as grpo_oracle
+import tests.test_oracle_pins as pins
+
+SOURCE_PATH = os.path.join(os.path.dirname(grpo_oracle.__file__), "grpo_oracle.py")
+PUBLIC = [n for n in dir(oracle) if not n.startswith("_") and inspect.isfunction(getattr(oracle, n))]
+
+# (name, [(text, replacement), ...]): every text must occur exactly once
+MUTATIONS = [
+    ("advantages: population std (ddof 0)",
+     [("std = np.sqrt((dev * dev).sum(axis=1, keepdims=True) / (n - 1))",
+       "std = np.sqrt((dev * dev).sum(axis=1, keepdims=True) / n)")]),
+    ("advantages: eps under the square root",
+     [("return (dev / (std + eps)).reshape(-1)",
+       "return (dev / np.sqrt(std * std + eps)).reshape(-1)")]),
+    ("advantages: sign flipped",
+     [("dev = r - mean", "dev = mean - r")]),
+    ("advantages: batch mean instead of group mean",
+     [("mean = r.sum(axis=1, keepdims=True) / n",
+       "mean = r.mean() + 0.0 * r.sum(axis=1, keepdims=True)")]),
+    ("lse: max term dropped",
+     [("lse = M + np.log(np.exp(Z - M[:, None]).sum(axis=1))",
+       "lse = np.log(np.exp(Z - M[:, None]).sum(axis=1))")]),
+    ("lse: no max shift",
+     [("lse = M + np.log(np.exp(Z - M[:, None]).sum(axis=1))",
+       "lse = np.log(np.exp(Z).sum(axis=1))")]),
+    ("target gather off by one",
+     [("lp = Z[np.arange(Z.shape[0]), np.asarray(y_rows, dtype=np.int64)] - lse",
+       "lp = Z[np.arange(Z.shape[0]), (np.asarray(y_rows, dtype=np.int64) + 1) % Z.shape[1]] - lse")]),
+    ("logits against a reordered vocabulary",
+     [("return _f64(H_rows) @ _f64(W).T", "return _f64(H_rows) @ _f64(W)[::-1].T")]),
+    ("kl: the -1 term dropped",
+     [("return np.exp(x) - x - 1.0", "return np.exp(x) - x")]),
+    ("kl: x = lp - ref (forward direction)",
+     [("x = _f64(ref_lp) - _f64(lp)\n    return np.exp(x) - x - 1.0",
+       "x = _f64(lp) - _f64(ref_lp)\n    return np.exp(x) - x - 1.0")]),
+    ("kl: quadratic estimator in place of k3",
+     [("return np.exp(x) - x - 1.0", "return 0.5 * x * x")]),
+    ("token advantages tiled instead of repeated",
+     [("return np.repeat(_f64(adv), seq_len)", "return np.tile(_f64(adv), seq_len)")]),
+    ("loss: mean over every token, not the unmasked ones",
+     [("loss = (m * ell).sum() / max(m.sum(), 1.0)", "loss = (m * ell).sum() / len(m)")]),
+    ("loss: KL penalty added instead of subtracted",
+     [("ell = -(R * A_t - beta * kl)", "ell = -(R * A_t + beta * kl)")]),
+    ("gradient: KL derivative sign",
+     [("(-A_t + beta * (1.0 - np.exp(x)))", "(-A_t + beta * (np.exp(x) - 1.0))")]),
+    ("gradient: advantage sign",
+     [("(-A_t + beta * (1.0 - np.exp(x)))", "(A_t + beta * (1.0 - np.exp(x)))")]),
+    ("gradient: mean normalisation dropped",
+     [("return grad_loss * m / max(m.sum(), 1.0) *", "return grad_loss * m *")]),
+    ("gradient: grad_loss ignored",
+     [("return grad_loss * m / max(m.sum(), 1.0) *", "return 1.0 * m / max(m.sum(), 1.0) *")]),
+    ("dZ: p - onehot instead of onehot - p",
+     [("dZ = -P\n", "dZ = P.copy()\n"),
+      ("dZ[np.arange(len(sel)), y[sel].astype(np.int64)] += 1.0",
+       "dZ[np.arange(len(sel)), y[sel].astype(np.int64)] -= 1.0")]),
+    ("dZ: softmax normalised over the whole block",
+     [("P /= P.sum(axis=1, keepdims=True)", "P /= P.sum()")]),
+    ("dZ: onehot at the wrong index",
+     [("dZ[np.arange(len(sel)), y[sel].astype(np.int64)] += 1.0",
+       "dZ[np.arange(len(sel)), (y[sel].astype(np.int64) + 1) % Wf.shape[0]] += 1.0")]),
+    ("dW: hidden rows misaligned with dZ rows",
+     [("dW += dZ.T @ Hs", "dW += dZ.T @ Hs[::-1]")]),
+    ("dH: vocabulary order of W reversed",
+     [("g = dZ @ Wf", "g = dZ @ Wf[::-1]")]),
+    ("backward: recomputed logits against the transposed head",
+     [("Z = Hs @ Wf.T", "Z = Hs @ Wf[::-1].T")]),
+]
+
+
+def _load(edits):
+    src = open(SOURCE_PATH).read()
+    for old, new in edits:
+        assert src.count(old) == 1, f"mutation anchor not unique or missing: {old!r}"
+        src = src.replace(old, new)
+    mod = types.ModuleType("grpo_oracle_mutant")
+    mod.__file__ = SOURCE_PATH
+    exec(compile(src, "grpo_oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+def _pin_cases():
+    for name, fn in inspect.getmembers(pins, inspect.isfunction):
+        if not name.startswith("test_"):
+            continue
+        marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+        if not marks:
+            yield name, fn, {}
+            continue
+        argnames, values = marks[0].args[0], marks[0].args[1]
+        names = [a.strip() for a in argnames.split(",")]
+        for v in values:
+            yield f"{name}{v}", fn, dict(zip(names, v if len(names) > 1 else [v]))
+
+
+def _failing_pins(mod, monkeypatch):
+    for n in PUBLIC:
+        monkeypatch.setattr(oracle, n, getattr(mod, n))
+        monkeypatch.setattr(grpo_oracle, n, getattr(mod, n))
+    failed = []
+    for name, fn, kw in _pin_cases():
+        try:
+            fn(**kw)
+        except Exception:       # an assertion, or the mutant breaking outright
+            failed.append(name)
+    monkeypatch.undo()
+    return failed
+
+
+def test_unmutated_source_passes_every_pin(monkeypatch):
+    assert _failing_pins(_load([]), monkeypatch) == []
+
+
+@pytest.mark.parametrize("name,edits", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, edits, monkeypatch):
+    failed = _failing_pins(_load(edits), monkeypatch)
+    assert failed, f"no pin catches: {name}"
