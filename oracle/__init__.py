@@ -2,6 +2,8 @@
 from .grpo_oracle import (  # noqa: F401
     group_advantages,
     logits,
+    logit_transform,
+    logit_transform_slope,
     lse_and_target,
     token_logprobs,
     reverse_kl_k3,

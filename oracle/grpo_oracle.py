@@ -86,6 +86,43 @@ def logits(H_rows, W):
     return _f64(H_rows) @ _f64(W).T
 
 
+def _xform(opts):
+    """(s, cap, T) from a logit-transform options dict; 0 (or absent) means off."""
+    o = opts or {}
+    mul = float(o.get("logit_scale_multiply", 0.0))
+    div = float(o.get("logit_scale_divide", 0.0))
+    cap = float(o.get("logit_softcapping", 0.0))
+    T = float(o.get("temperature", 0.0))
+    s = (mul if mul != 0.0 else 1.0) / (div if div != 0.0 else 1.0)
+    return s, cap, (T if T != 0.0 else 1.0)
+
+
+def logit_transform(Z, opts=None):
+    """Logits after the optional scale, softcap and temperature, float64.
+
+    [P-docs, Flattened sequence length chunking]: the chunked log-softmax
+    takes logit_scale_multiply, logit_scale_divide, logit_softcapping and
+    temperature, and its notes say softcapping and temperature are supported.
+    The pages give no formulas; the plainest reading, applied in the order of
+    the call's arguments: z * multiply, / divide, cap * tanh(z / cap), / T.
+    A zero multiply, divide or cap is "off"; a zero temperature means 1.
+    """
+    s, cap, T = _xform(opts)
+    U = _f64(Z) * s
+    if cap != 0.0:
+        U = cap * np.tanh(U / cap)
+    return U / T
+
+
+def logit_transform_slope(Z, opts=None):
+    """d logit_transform(z) / dz, elementwise: (s / T) (1 - tanh^2(s z / cap))."""
+    s, cap, T = _xform(opts)
+    if cap == 0.0:
+        return np.full(np.shape(Z), s / T)
+    t = np.tanh(_f64(Z) * s / cap)
+    return (s / T) * (1.0 - t * t)
+
+
 def lse_and_target(Z, y_rows):
     """Max-shifted log-sum-exp of each row of Z and the target log-prob.
 
@@ -98,12 +135,13 @@ def lse_and_target(Z, y_rows):
     return lp, lse
 
 
-def token_logprobs(H, W, y, rows=None, block=ROW_BLOCK):
+def token_logprobs(H, W, y, rows=None, block=ROW_BLOCK, opts=None):
     """(lp, lse) for every token (or for the listed `rows`), float64.
 
     [P-docs, Flattened sequence length chunking]: the selective log-softmax
     of the hidden states through the LM head, gathered at the completion ids.
-    The logits of `block` rows are formed in full, then reduced.
+    The logits of `block` rows are formed in full, transformed (`opts`, see
+    logit_transform), then reduced.
     """
     H = np.asarray(H)
     y = np.asarray(y)
@@ -112,7 +150,10 @@ def token_logprobs(H, W, y, rows=None, block=ROW_BLOCK):
     lse = np.empty(len(idx))
     for b0 in range(0, len(idx), block):
         sel = idx[b0:b0 + block]
-        lp[b0:b0 + block], lse[b0:b0 + block] = lse_and_target(logits(H[sel], W), y[sel])
+        Z = logits(H[sel], W)
+        if opts:
+            Z = logit_transform(Z, opts)
+        lp[b0:b0 + block], lse[b0:b0 + block] = lse_and_target(Z, y[sel])
     return lp, lse
 
 
@@ -138,7 +179,7 @@ def token_advantages(adv, seq_len):
     return np.repeat(_f64(adv), seq_len)
 
 
-def loss_forward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04):
+def loss_forward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04, opts=None):
     """Masked token-mean GRPO loss plus the per-token outputs.
 
     l_t = -(R_t * A_t - beta * kl_t), with R_t = exp(lp_t - stopgrad(lp_t)),
@@ -147,7 +188,7 @@ def loss_forward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04):
     flattened tokens (an empty mask gives 0).
     lp, kl and lse are reported for every token, masked or not.
     """
-    lp, lse = token_logprobs(H, W, y)
+    lp, lse = token_logprobs(H, W, y, opts=opts)
     kl = reverse_kl_k3(ref_lp, lp)
     A_t = token_advantages(adv, seq_len)
     R = 1.0
@@ -171,13 +212,14 @@ def loss_coefficients(mask, adv, ref_lp, lp, seq_len, beta=0.04, grad_loss=1.0):
 
 
 def loss_backward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04, grad_loss=1.0,
-                  dh_rows=None, want_dW=True, block=ROW_BLOCK):
+                  dh_rows=None, want_dW=True, block=ROW_BLOCK, opts=None):
     """Gradients of the loss w.r.t. H and W, float64.
 
     [P-docs, Offloading activations]: the backward recomputes the logits of
     each slice instead of keeping them from the forward.  Per token:
-      p_t = softmax(z_t);  dZ_t = c_t (onehot(y_t) - p_t)
-      dH_t = dZ_t W;       dW = sum_t dZ_t^T h_t
+      p_t = softmax(f(z_t));  dZ_t = c_t (onehot(y_t) - p_t) f'(z_t)
+      dH_t = dZ_t W;          dW = sum_t dZ_t^T h_t
+    with f the logit transform of `opts` (the identity without it).
     Returns (dH, dW).  dH has one row per entry of `dh_rows` (all tokens if
     None).  dW is the value the GPU adds to its accumulator (None when
     want_dW is False).  Only unmasked tokens contribute to dW (c_t = 0
@@ -193,7 +235,7 @@ def loss_backward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04, grad_loss=1.0,
     rows = np.arange(N) if dh_rows is None else np.asarray(dh_rows, dtype=np.int64)
     need = np.union1d(active, rows) if want_dW else np.unique(rows)
     # per-token coefficient needs lp of the token: recompute from full logits
-    lp_need, _ = token_logprobs(H, W, y, rows=need, block=block)
+    lp_need, _ = token_logprobs(H, W, y, rows=need, block=block, opts=opts)
     lp_all[need] = lp_need
     c = loss_coefficients(mask, adv, ref_lp, lp_all, seq_len, beta, grad_loss)
     dW = np.zeros_like(Wf)
@@ -203,12 +245,15 @@ def loss_backward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04, grad_loss=1.0,
         sel = need[b0:b0 + block]
         Hs = _f64(H[sel])
         Z = Hs @ Wf.T
-        M = Z.max(axis=1, keepdims=True)
-        P = np.exp(Z - M)
+        Zf = logit_transform(Z, opts) if opts else Z
+        M = Zf.max(axis=1, keepdims=True)
+        P = np.exp(Zf - M)
         P /= P.sum(axis=1, keepdims=True)
         dZ = -P
         dZ[np.arange(len(sel)), y[sel].astype(np.int64)] += 1.0
         dZ *= c[sel][:, None]
+        if opts:
+            dZ *= logit_transform_slope(Z, opts)
         if want_dW:
             dW += dZ.T @ Hs
         g = dZ @ Wf

@@ -75,6 +75,20 @@ MUTATIONS = [
      [("dW += dZ.T @ Hs", "dW += dZ.T @ Hs[::-1]")]),
     ("dH: vocabulary order of W reversed",
      [("g = dZ @ Wf", "g = dZ @ Wf[::-1]")]),
+    ("transform: temperature multiplies instead of divides",
+     [("    return U / T\n", "    return U * T\n")]),
+    ("transform: softcap without the outer cap factor",
+     [("U = cap * np.tanh(U / cap)", "U = np.tanh(U / cap)")]),
+    ("transform slope: the 1 - tanh^2 factor dropped",
+     [("return (s / T) * (1.0 - t * t)", "return (s / T) * (1.0 + 0.0 * t)")]),
+    ("transform slope: 1 / T dropped",
+     [("return (s / T) * (1.0 - t * t)", "return s * (1.0 - t * t)")]),
+    ("transform: divide applied as a multiply",
+     [("s = (mul if mul != 0.0 else 1.0) / (div if div != 0.0 else 1.0)",
+       "s = (mul if mul != 0.0 else 1.0) * (div if div != 0.0 else 1.0)")]),
+    ("backward: softmax of the raw logits, not the transformed ones",
+     [("M = Zf.max(axis=1, keepdims=True)\n        P = np.exp(Zf - M)",
+       "M = Z.max(axis=1, keepdims=True)\n        P = np.exp(Z - M)")]),
     ("backward: recomputed logits against the transposed head",
      [("Z = Hs @ Wf.T", "Z = Hs @ Wf[::-1].T")]),
 ]

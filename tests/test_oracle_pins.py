@@ -285,6 +285,123 @@ def test_grad_loss_scales_linearly():
         np.testing.assert_allclose(got, -2.5 * base, rtol=1e-13, atol=1e-14 * np.abs(base).max())
 
 
+# --------------------------------------------------------------------------- logit transforms
+XFORMS = [
+    {"temperature": 0.7},
+    {"logit_softcapping": 1.5},
+    {"logit_scale_multiply": 1.3, "logit_scale_divide": 0.8, "logit_softcapping": 2.0,
+     "temperature": 1.25},
+]
+
+
+def test_transform_off_is_the_identity():
+    p = _problem(20)
+    Z = oracle.logits(p["H"], p["W"])
+    zero = {"logit_scale_multiply": 0.0, "logit_scale_divide": 0.0, "logit_softcapping": 0.0,
+            "temperature": 0.0}
+    assert np.array_equal(oracle.logit_transform(Z, zero), Z)
+    assert np.array_equal(oracle.logit_transform_slope(Z, zero), np.ones_like(Z))
+
+
+def test_temperature_is_log_softmax_of_scaled_logits():
+    p = _problem(21)
+    T = 0.7
+    lp, lse = oracle.token_logprobs(p["H"], p["W"], p["y"], opts={"temperature": T})
+    Z = (p["H"] @ p["W"].T) / T
+    want = scipy.special.log_softmax(Z, axis=1)[np.arange(p["N"]), p["y"]]
+    np.testing.assert_allclose(lp, want, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(Z, axis=1), rtol=1e-13)
+
+
+def test_scale_divide_and_temperature_are_the_same_linear_map():
+    p = _problem(22)
+    a, _ = oracle.token_logprobs(p["H"], p["W"], p["y"], opts={"logit_scale_multiply": 2.0})
+    b, _ = oracle.token_logprobs(p["H"], p["W"], p["y"], opts={"logit_scale_divide": 0.5})
+    c, _ = oracle.token_logprobs(p["H"], p["W"], p["y"], opts={"temperature": 0.5})
+    d, _ = oracle.token_logprobs(2.0 * p["H"], p["W"], p["y"])
+    for got in (b, c, d):
+        np.testing.assert_allclose(got, a, rtol=1e-12, atol=1e-13)
+
+
+def test_softcap_bounds_closed_form_and_large_cap_limit():
+    Z = np.linspace(-500.0, 500.0, 2001).reshape(1, -1)
+    cap, T = 30.0, 2.0
+    f = oracle.logit_transform(Z, {"logit_softcapping": cap, "temperature": T})
+    assert np.all(np.abs(f) < cap / T)
+    assert np.all(np.diff(f) > 0)                                     # monotone
+    z = cap * math.atanh(0.5)                                        # tanh(z / cap) = 1/2
+    assert oracle.logit_transform(np.array([[z]]), {"logit_softcapping": cap})[0, 0] == \
+        pytest.approx(cap / 2, rel=1e-14)
+    assert oracle.logit_transform_slope(np.array([[z]]), {"logit_softcapping": cap})[0, 0] == \
+        pytest.approx(0.75, rel=1e-14)                               # 1 - tanh^2
+    small = np.linspace(-3, 3, 13).reshape(1, -1)
+    np.testing.assert_allclose(oracle.logit_transform(small, {"logit_softcapping": 1e7}), small,
+                               rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("opts", XFORMS)
+def test_transform_gradients_match_central_differences_of_surrogate(opts):
+    p = _problem(23, ref_sigma=0.7)
+    lp0, _ = oracle.token_logprobs(p["H"], p["W"], p["y"], opts=opts)
+    dH, dW = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                  p["L"], BETA, opts=opts)
+
+    def J(H, W):
+        lp, _ = oracle.token_logprobs(H, W, p["y"], opts=opts)
+        A_t = np.repeat(p["adv"], p["L"])
+        x = p["ref_lp"] - lp
+        ell = -(np.exp(lp - lp0) * A_t - BETA * (np.exp(x) - x - 1))
+        m = p["mask"].astype(np.float64)
+        return (m * ell).sum() / max(m.sum(), 1.0)
+
+    rng = np.random.default_rng(24)
+    h = 1e-6
+    for _ in range(10):
+        t, k = rng.integers(0, p["N"]), rng.integers(0, p["d"])
+        Hp, Hm = p["H"].copy(), p["H"].copy()
+        Hp[t, k] += h
+        Hm[t, k] -= h
+        fd = (J(Hp, p["W"]) - J(Hm, p["W"])) / (2 * h)
+        assert abs(fd - dH[t, k]) < 1e-8 + 1e-6 * abs(fd), (t, k, fd, dH[t, k])
+        v, k = rng.integers(0, p["V"]), rng.integers(0, p["d"])
+        Wp, Wm = p["W"].copy(), p["W"].copy()
+        Wp[v, k] += h
+        Wm[v, k] -= h
+        fd = (J(p["H"], Wp) - J(p["H"], Wm)) / (2 * h)
+        assert abs(fd - dW[v, k]) < 1e-8 + 1e-6 * abs(fd), (v, k, fd, dW[v, k])
+
+
+@pytest.mark.parametrize("opts", XFORMS)
+def test_transform_gradients_match_torch_autograd(opts):
+    p = _problem(25)
+    H = torch.tensor(p["H"], requires_grad=True)
+    W = torch.tensor(p["W"], requires_grad=True)
+    mul = opts.get("logit_scale_multiply", 0.0) or 1.0
+    div = opts.get("logit_scale_divide", 0.0) or 1.0
+    cap = opts.get("logit_softcapping", 0.0)
+    T = opts.get("temperature", 0.0) or 1.0
+    Z = (H @ W.T) * mul / div
+    if cap:
+        Z = cap * torch.tanh(Z / cap)
+    Z = Z / T
+    B, L = len(p["adv"]), p["L"]
+    logp = torch.log_softmax(Z, dim=1)
+    lp = logp[torch.arange(logp.shape[0]), torch.as_tensor(p["y"]).long()].reshape(B, L)
+    ratio = (lp - lp.detach()).exp()
+    x = torch.as_tensor(p["ref_lp"]).reshape(B, L) - lp
+    m = torch.as_tensor(p["mask"]).double().reshape(B, L)
+    per_token = BETA * (x.exp() - x - 1.0) - ratio * torch.as_tensor(p["adv"]).reshape(B, 1)
+    loss = (per_token * m).sum() / torch.clamp(m.sum(), min=1.0)
+    loss.backward()
+    out = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"],
+                              BETA, opts=opts)
+    assert out["loss"] == pytest.approx(loss.item(), rel=1e-13)
+    dH, dW = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                  p["L"], BETA, opts=opts)
+    np.testing.assert_allclose(dH, H.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
 # --------------------------------------------------------------------------- workload shapes
 def test_long_context_workload_reproduces_pages_logit_memory():
     """8 x 20480 tokens x 128256 vocab x 4 B is the pages' 78.3 GB of logits;
