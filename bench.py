@@ -131,7 +131,7 @@ def alg_flops(kind, d, V, N, N_act):
     return None
 
 
-def cpu_baseline(w, inp, seconds=15.0):
+def cpu_baseline(w, inp, seconds=15.0, opts=None):
     """The float64 oracle, as it stands, on a bounded sample: the first n
     flattened tokens of the batch, run through reference log-probs, loss forward
     and loss backward, on all host threads BLAS uses."""
@@ -155,9 +155,9 @@ def cpu_baseline(w, inp, seconds=15.0):
         Hr = H_ref[:n].double().numpy()
         ys, ms, adv = y[:n], mask[:n], adv_tok[:n]
         t0 = time.perf_counter()
-        ref, _ = oracle.token_logprobs(Hr, W64, ys)
-        oracle.loss_forward(Hs, W64, ys, ms, adv, ref, 1, 0.04)
-        oracle.loss_backward(Hs, W64, ys, ms, adv, ref, 1, 0.04)
+        ref, _ = oracle.token_logprobs(Hr, W64, ys, opts=opts)
+        oracle.loss_forward(Hs, W64, ys, ms, adv, ref, 1, 0.04, opts=opts)
+        oracle.loss_backward(Hs, W64, ys, ms, adv, ref, 1, 0.04, opts=opts)
         return time.perf_counter() - t0
 
     # size the sample to about `seconds` of work: small runs carry fixed costs, so
@@ -187,11 +187,20 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--temperature", type=float, default=0.0,
+                    help="logit temperature (0: off); the logit options apply to every pass")
+    ap.add_argument("--softcap", type=float, default=0.0, help="logit softcapping (0: off)")
+    ap.add_argument("--scale-multiply", type=float, default=0.0, help="logit scale multiply (0: off)")
+    ap.add_argument("--scale-divide", type=float, default=0.0, help="logit scale divide (0: off)")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB calibration copy and one reference pass, then exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two counter runs of --traffic-probe")
     args = ap.parse_args()
+    xopts = {k: v for k, v in (("logit_scale_multiply", args.scale_multiply),
+                               ("logit_scale_divide", args.scale_divide),
+                               ("logit_softcapping", args.softcap),
+                               ("temperature", args.temperature)) if v} or None
 
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload)
@@ -233,7 +242,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-        gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, workspace=ws_f)
+        gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, workspace=ws_f,
+                             logit_opts=xopts)
         torch.cuda.synchronize()
         log("[bench] traffic probe done")
         return
@@ -242,16 +252,19 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         adv = gp.grpo_advantages(inp["rewards"], w.G, workloads.EPS)
-        ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, workspace=ws_f)
+        ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, workspace=ws_f,
+                                   logit_opts=xopts)
         if ev is not None:
             ev[1].record(stream)
         loss, lp, kl, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref,
-                                             B, L, workloads.BETA, w.chunk, workspace=ws_f)
+                                             B, L, workloads.BETA, w.chunk, workspace=ws_f,
+                                             logit_opts=xopts)
         if ev is not None:
             ev[2].record(stream)
         dW.zero_()
         gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp, lse, B, L,
-                         workloads.BETA, 1.0, w.chunk, dW=dW, dH=dH, workspace=ws_b)
+                         workloads.BETA, 1.0, w.chunk, dW=dW, dH=dH, workspace=ws_b,
+                         logit_opts=xopts)
         if ev is not None:
             ev[3].record(stream)
         return loss
@@ -298,7 +311,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host ...")
-        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, xopts)
         log(f"[bench] oracle {cpu['value']:.2f} tokens/s")
 
     out = {
@@ -316,7 +329,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": N, "active_tokens": N_act, "d": d, "V": V,
                    "chunk": w.chunk, "beta": workloads.BETA,
-                   "step": "advantages + reference log-probs + loss fwd + loss bwd"},
+                   "step": "advantages + reference log-probs + loss fwd + loss bwd",
+                   **({"logit_opts": xopts} if xopts else {})},
         "fwd_bwd_tokens_per_s": round(N / ((ms_fwd + ms_bwd) * 1e-3), 1),
         "fwd_bwd_mfma_frac": round(fb_flops / ((ms_fwd + ms_bwd) * 1e-3) / peak, 4),
         "ms": {"advantages+ref": round(ms_ref, 3), "fwd": round(ms_fwd, 3),

@@ -21,6 +21,16 @@ STATUS = {0: "GRPO_OK", -1: "GRPO_ERR_INVALID_ARG", -2: "GRPO_ERR_WORKSPACE",
 
 _i64, _f32, _vp, _sz, _int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
 
+
+
+class LogitOpts(ctypes.Structure):
+    """grpo_logit_opts: zero fields are off (temperature 0 means 1)."""
+    _fields_ = [("logit_scale_multiply", ctypes.c_float), ("logit_scale_divide", ctypes.c_float),
+                ("logit_softcapping", ctypes.c_float), ("temperature", ctypes.c_float)]
+
+
+_OPTS_P = ctypes.POINTER(LogitOpts)
+
 # name -> (restype, argtypes); mirrors include/grpo.h
 SIGNATURES = {
     "grpo_workspace_bytes": (_sz, [_int, _i64, _i64, _i64, _int, _i64]),
@@ -30,6 +40,12 @@ SIGNATURES = {
                              _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "grpo_loss_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
                              _f32, _f32, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "grpo_ref_logprobs_ex": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _int, _i64, _OPTS_P, _vp,
+                                    _vp, _sz, _vp]),
+    "grpo_loss_fwd_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _f32,
+                                _i64, _OPTS_P, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "grpo_loss_bwd_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                _int, _f32, _f32, _i64, _OPTS_P, _vp, _vp, _vp, _sz, _vp]),
     "grpo_gemm_nt": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
     "grpo_timing_begin": (_int, []),
     "grpo_timing_end": (_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_int),
@@ -92,6 +108,16 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def _opts(logit_opts):
+    """A grpo_logit_opts pointer from a dict of its fields (None: the identity)."""
+    if logit_opts is None:
+        return None
+    unknown = set(logit_opts) - {f for f, _ in LogitOpts._fields_}
+    if unknown:
+        raise ValueError(f"unknown logit options: {sorted(unknown)}")
+    return ctypes.pointer(LogitOpts(**{k: float(v) for k, v in logit_opts.items()}))
+
+
 def _want(t: torch.Tensor, dtype, name):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
@@ -121,7 +147,8 @@ def grpo_advantages(rewards: torch.Tensor, group_size: int, eps: float = 1e-4, o
     return out
 
 
-def grpo_ref_logprobs(H_ref, W, y, chunk: int = 4096, out=None, workspace=None):
+def grpo_ref_logprobs(H_ref, W, y, chunk: int = 4096, out=None, workspace=None,
+                      logit_opts=None):
     _dev(H_ref, W, y)
     _want(y, torch.int32, "y")
     N, d = H_ref.shape
@@ -131,15 +158,17 @@ def grpo_ref_logprobs(H_ref, W, y, chunk: int = 4096, out=None, workspace=None):
         raise ValueError("shape/dtype mismatch between H_ref, W, y")
     out = torch.empty(N, dtype=torch.float32, device=H_ref.device) if out is None else out
     ws = _workspace(GRPO_OP_REF, N, d, V, dt, chunk, H_ref.device, workspace)
-    _check("grpo_ref_logprobs", lib().grpo_ref_logprobs(
-        _ptr(H_ref), _ptr(W), _ptr(y), N, d, V, dt, chunk, _ptr(out), _ptr(ws),
+    _check("grpo_ref_logprobs_ex", lib().grpo_ref_logprobs_ex(
+        _ptr(H_ref), _ptr(W), _ptr(y), N, d, V, dt, chunk, _opts(logit_opts), _ptr(out), _ptr(ws),
         ws.numel(), _stream()))
     return out
 
 
 def grpo_loss_fwd(H, W, y, mask, adv, ref_lp, B: int, L: int, beta: float = 0.04,
-                  chunk: int = 4096, workspace=None):
-    """Returns (loss[1], lp[N], kl[N], lse[N]), all float32 on the GPU."""
+                  chunk: int = 4096, workspace=None, logit_opts=None):
+    """Returns (loss[1], lp[N], kl[N], lse[N]), all float32 on the GPU.  `logit_opts`:
+    dict of grpo_logit_opts fields (logit_scale_multiply, logit_scale_divide,
+    logit_softcapping, temperature), or None for the identity."""
     _dev(H, W, y, mask, adv, ref_lp)
     _want(y, torch.int32, "y")
     _want(mask, torch.uint8, "mask")
@@ -157,16 +186,19 @@ def grpo_loss_fwd(H, W, y, mask, adv, ref_lp, B: int, L: int, beta: float = 0.04
     kl = torch.empty(N, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
     ws = _workspace(GRPO_OP_FWD, N, d, V, dt, chunk, dev, workspace)
-    _check("grpo_loss_fwd", lib().grpo_loss_fwd(
+    _check("grpo_loss_fwd_ex", lib().grpo_loss_fwd_ex(
         _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(adv), _ptr(ref_lp), B, L, d, V, dt, beta,
-        chunk, _ptr(loss), _ptr(lp), _ptr(kl), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+        chunk, _opts(logit_opts), _ptr(loss), _ptr(lp), _ptr(kl), _ptr(lse), _ptr(ws),
+        ws.numel(), _stream()))
     return loss, lp, kl, lse
 
 
 def grpo_loss_bwd(H, W, y, mask, adv, ref_lp, lp, lse, B: int, L: int, beta: float = 0.04,
-                  grad_loss: float = 1.0, chunk: int = 4096, dW=None, dH=None, workspace=None):
+                  grad_loss: float = 1.0, chunk: int = 4096, dW=None, dH=None, workspace=None,
+                  logit_opts=None):
     """Returns (dH[N, d] in H's dtype, dW[V, d] float32).  dW is accumulated into
-    when given (zeros are allocated otherwise)."""
+    when given (zeros are allocated otherwise).  `logit_opts` must be those of
+    the forward that produced lp and lse."""
     _dev(H, W, y, mask, adv, ref_lp, lp, lse)
     N, d = H.shape
     V = W.shape[0]
@@ -179,10 +211,10 @@ def grpo_loss_bwd(H, W, y, mask, adv, ref_lp, lp, lse, B: int, L: int, beta: flo
     _dev(dH, dW)
     _want(dW, torch.float32, "dW")
     ws = _workspace(GRPO_OP_BWD, N, d, V, dt, chunk, dev, workspace)
-    _check("grpo_loss_bwd", lib().grpo_loss_bwd(
+    _check("grpo_loss_bwd_ex", lib().grpo_loss_bwd_ex(
         _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(adv), _ptr(ref_lp), _ptr(lp), _ptr(lse),
-        B, L, d, V, dt, beta, grad_loss, chunk, _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(),
-        _stream()))
+        B, L, d, V, dt, beta, grad_loss, chunk, _opts(logit_opts), _ptr(dH), _ptr(dW), _ptr(ws),
+        ws.numel(), _stream()))
     return dH, dW
 
 

@@ -194,11 +194,36 @@ int check_shape(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
     if (e_ != hipSuccess) return hip_fail(e_, #call);     \
   } while (0)
 
+// The kernels' form of a grpo_logit_opts (NULL: identity).
+int make_xform(const grpo_logit_opts* o, grpo::LogitXform* xf) {
+  *xf = grpo::LogitXform{1.f, 1.f, 1.f, 0};
+  if (o == nullptr) return GRPO_OK;
+  const float v[4] = {o->logit_scale_multiply, o->logit_scale_divide, o->logit_softcapping,
+                      o->temperature};
+  for (float x : v)
+    if (!isfinite(x) || x < 0.f)
+      return fail(GRPO_ERR_INVALID_ARG,
+                  "logit opts must be finite and >= 0 (multiply %g divide %g cap %g T %g)",
+                  (double)v[0], (double)v[1], (double)v[2], (double)v[3]);
+  const double scale = (v[0] != 0.f ? (double)v[0] : 1.0) / (v[1] != 0.f ? (double)v[1] : 1.0);
+  const double T = v[3] != 0.f ? (double)v[3] : 1.0;
+  xf->k = (float)(scale / T);
+  if (v[2] != 0.f) {
+    xf->softcap = 1;
+    xf->a = (float)(scale / (double)v[2]);
+    xf->b = (float)((double)v[2] / T);
+  }
+  if (!isfinite(xf->k) || xf->k <= 0.f || !isfinite(xf->a) || xf->a <= 0.f ||
+      !isfinite(xf->b) || xf->b <= 0.f)
+    return fail(GRPO_ERR_INVALID_ARG, "logit opts give a degenerate scale");
+  return GRPO_OK;
+}
+
 template <typename T>
 int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* mask,
              const float* adv, const float* ref_lp, int64_t N, int64_t L, int64_t d, int64_t V,
-             float beta, int64_t chunk, float* loss, float* out_lp, float* out_kl,
-             float* out_lse, char* ws, hipStream_t s) {
+             float beta, int64_t chunk, const grpo::LogitXform& xf, float* loss,
+             float* out_lp, float* out_kl, float* out_lse, char* ws, hipStream_t s) {
   const FwdPlan p = plan_fwd(N, V, chunk);
   float* pm = (float*)(ws + p.o_pm);
   float* ps = (float*)(ws + p.o_ps);
@@ -208,8 +233,8 @@ int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* 
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const int64_t c0 = c * p.C;
     const int n_tok = (int)std::min<int64_t>(p.C, N - c0);
-    GRPO_HIP(grpo::launch_lse_partials<T>(W, H + c0 * d, y + c0, V, d, n_tok, (int)p.cpad, pm, ps,
-                                          zy, s));
+    GRPO_HIP(grpo::launch_lse_partials<T>(W, H + c0 * d, y + c0, V, d, n_tok, (int)p.cpad, xf, pm,
+                                          ps, zy, s));
     GRPO_HIP(grpo::launch_lse_merge(mode, pm, ps, zy, (int)p.S, (int)p.cpad, n_tok, c0, y, V,
                                     out_lp, out_lse, out_kl, ref_lp, mask, adv, L, beta, lpart,
                                     cpart, (int)(c * p.parts_per_chunk), s));
@@ -229,8 +254,8 @@ int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* 
 template <typename T>
 int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, const float* adv,
              const float* ref_lp, const float* lp, const float* lse, int64_t N, int64_t L,
-             int64_t d, int64_t V, float beta, float grad_loss, int64_t chunk, T* dH, float* dW,
-             char* ws, int dtype, hipStream_t s) {
+             int64_t d, int64_t V, float beta, float grad_loss, int64_t chunk,
+             const grpo::LogitXform& xf, T* dH, float* dW, char* ws, int dtype, hipStream_t s) {
   const BwdPlan p = plan_bwd(N, d, V, dtype, chunk);
   int32_t* idx = (int32_t*)(ws + p.o_idx);
   int32_t* cnt = (int32_t*)(ws + p.o_cnt);
@@ -254,13 +279,14 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
     const int64_t c0 = c * p.C;
     const int C = (int)p.C;
     GRPO_HIP(grpo::launch_bwd_prep<T>(H, d, idx, cnt, c0, C, (int)p.cpad, y, mask, adv, ref_lp, lp,
-                                      lse, L, beta, grad_loss, H_act, coef, lse_c, y_c, tgt_c, s));
+                                      lse, L, beta, grad_loss, xf, H_act, coef, lse_c, y_c, tgt_c,
+                                      s));
     GRPO_HIP(grpo::launch_transpose<T>(H_act, p.cpad, d, HT, p.cpad, s));
     for (int64_t sl = 0; sl < p.nslabs; ++sl) {
       const int64_t v0 = sl * p.vs;
       const int vs_valid = (int)std::min<int64_t>(p.vs, V - v0);
       GRPO_HIP(grpo::launch_dz<T>(W, H_act, d, V, v0, vs_valid, (int)p.vs, cnt, c0, C,
-                                  (int)p.cpad, coef, lse_c, y_c, tgt_c, dZ, dZT, s));
+                                  (int)p.cpad, xf, coef, lse_c, y_c, tgt_c, dZ, dZT, s));
       GRPO_HIP(grpo::launch_dh_gemm<T>(WT, p.vpad, v0, vs_valid, dZ, (int)p.vs, d, cnt, c0, C,
                                        (int)p.cpad, (int)p.nsplit, sl == 0 ? 1 : 0, dH_acc, s));
       GRPO_HIP(grpo::launch_dw_gemm<T>(HT, (int)p.cpad, dZT, d, V, v0, vs_valid, cnt, c0, C, dW,
@@ -313,10 +339,12 @@ int grpo_advantages(const float* rewards, int64_t num_groups, int64_t group_size
   return GRPO_OK;
 }
 
-int grpo_ref_logprobs(const void* H_ref, const void* W, const int32_t* y, int64_t N, int64_t d,
-                      int64_t V, int dtype, int64_t chunk, float* ref_lp, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+int grpo_ref_logprobs_ex(const void* H_ref, const void* W, const int32_t* y, int64_t N, int64_t d,
+                         int64_t V, int dtype, int64_t chunk, const grpo_logit_opts* opts,
+                         float* ref_lp, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  grpo::LogitXform xf;
+  if (make_xform(opts, &xf) != GRPO_OK) return GRPO_ERR_INVALID_ARG;
   GRPO_CHECK_PTR(H_ref);
   GRPO_CHECK_PTR(W);
   GRPO_CHECK_PTR(y);
@@ -330,18 +358,28 @@ int grpo_ref_logprobs(const void* H_ref, const void* W, const int32_t* y, int64_
   hipStream_t s = (hipStream_t)stream;
   if (dtype == GRPO_BF16)
     return lse_pass<__bf16>(0, (const __bf16*)H_ref, (const __bf16*)W, y, nullptr, nullptr,
-                            nullptr, N, 1, d, V, 0.f, chunk, nullptr, ref_lp, nullptr, nullptr,
-                            (char*)workspace, s);
+                            nullptr, N, 1, d, V, 0.f, chunk, xf, nullptr, ref_lp, nullptr,
+                            nullptr, (char*)workspace, s);
   return lse_pass<float>(0, (const float*)H_ref, (const float*)W, y, nullptr, nullptr, nullptr, N,
-                         1, d, V, 0.f, chunk, nullptr, ref_lp, nullptr, nullptr,
+                         1, d, V, 0.f, chunk, xf, nullptr, ref_lp, nullptr, nullptr,
                          (char*)workspace, s);
 }
 
-int grpo_loss_fwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
-                  const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
-                  int64_t V, int dtype, float beta, int64_t chunk, float* loss, float* lp,
-                  float* kl, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+int grpo_ref_logprobs(const void* H_ref, const void* W, const int32_t* y, int64_t N, int64_t d,
+                      int64_t V, int dtype, int64_t chunk, float* ref_lp, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return grpo_ref_logprobs_ex(H_ref, W, y, N, d, V, dtype, chunk, nullptr, ref_lp, workspace,
+                              workspace_bytes, stream);
+}
+
+int grpo_loss_fwd_ex(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                     const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
+                     int64_t V, int dtype, float beta, int64_t chunk, const grpo_logit_opts* opts,
+                     float* loss, float* lp, float* kl, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  grpo::LogitXform xf;
+  if (make_xform(opts, &xf) != GRPO_OK) return GRPO_ERR_INVALID_ARG;
   GRPO_CHECK_PTR(H);
   GRPO_CHECK_PTR(W);
   GRPO_CHECK_PTR(y);
@@ -365,17 +403,27 @@ int grpo_loss_fwd(const void* H, const void* W, const int32_t* y, const uint8_t*
   hipStream_t s = (hipStream_t)stream;
   if (dtype == GRPO_BF16)
     return lse_pass<__bf16>(1, (const __bf16*)H, (const __bf16*)W, y, mask, adv, ref_lp, N, L, d,
-                            V, beta, chunk, loss, lp, kl, lse, (char*)workspace, s);
+                            V, beta, chunk, xf, loss, lp, kl, lse, (char*)workspace, s);
   return lse_pass<float>(1, (const float*)H, (const float*)W, y, mask, adv, ref_lp, N, L, d, V,
-                         beta, chunk, loss, lp, kl, lse, (char*)workspace, s);
+                         beta, chunk, xf, loss, lp, kl, lse, (char*)workspace, s);
 }
 
-int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
-                  const float* adv, const float* ref_lp, const float* lp, const float* lse,
-                  int64_t B, int64_t L, int64_t d, int64_t V, int dtype, float beta,
-                  float grad_loss, int64_t chunk, void* dH, float* dW, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+int grpo_loss_fwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                  const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
+                  int64_t V, int dtype, float beta, int64_t chunk, float* loss, float* lp,
+                  float* kl, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return grpo_loss_fwd_ex(H, W, y, mask, adv, ref_lp, B, L, d, V, dtype, beta, chunk, nullptr,
+                          loss, lp, kl, lse, workspace, workspace_bytes, stream);
+}
+
+int grpo_loss_bwd_ex(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                     const float* adv, const float* ref_lp, const float* lp, const float* lse,
+                     int64_t B, int64_t L, int64_t d, int64_t V, int dtype, float beta,
+                     float grad_loss, int64_t chunk, const grpo_logit_opts* opts, void* dH,
+                     float* dW, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
+  grpo::LogitXform xf;
+  if (make_xform(opts, &xf) != GRPO_OK) return GRPO_ERR_INVALID_ARG;
   GRPO_CHECK_PTR(H);
   GRPO_CHECK_PTR(W);
   GRPO_CHECK_PTR(y);
@@ -400,10 +448,20 @@ int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t*
   hipStream_t s = (hipStream_t)stream;
   if (dtype == GRPO_BF16)
     return bwd_pass<__bf16>((const __bf16*)H, (const __bf16*)W, y, mask, adv, ref_lp, lp, lse, N,
-                            L, d, V, beta, grad_loss, chunk, (__bf16*)dH, dW, (char*)workspace,
-                            dtype, s);
+                            L, d, V, beta, grad_loss, chunk, xf, (__bf16*)dH, dW,
+                            (char*)workspace, dtype, s);
   return bwd_pass<float>((const float*)H, (const float*)W, y, mask, adv, ref_lp, lp, lse, N, L, d,
-                         V, beta, grad_loss, chunk, (float*)dH, dW, (char*)workspace, dtype, s);
+                         V, beta, grad_loss, chunk, xf, (float*)dH, dW, (char*)workspace, dtype,
+                         s);
+}
+
+int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                  const float* adv, const float* ref_lp, const float* lp, const float* lse,
+                  int64_t B, int64_t L, int64_t d, int64_t V, int dtype, float beta,
+                  float grad_loss, int64_t chunk, void* dH, float* dW, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  return grpo_loss_bwd_ex(H, W, y, mask, adv, ref_lp, lp, lse, B, L, d, V, dtype, beta,
+                          grad_loss, chunk, nullptr, dH, dW, workspace, workspace_bytes, stream);
 }
 
 int grpo_gemm_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int dtype,

@@ -2,9 +2,10 @@
 //
 // Forward (per chunk of flattened tokens):
 //   k_lse_partials: MFMA tile z^T = W_tile . H_tile^T (vocab rows x token
-//     columns), folded in registers into a (max, sum-exp) pair per token for
-//     that 256-row vocabulary tile, plus the target logit z[y] when the
-//     target falls in the tile.  Logits never leave registers.
+//     columns), transformed (scale, softcap, temperature) and folded in
+//     registers into a (max, sum-exp) pair per token for that 256-row
+//     vocabulary tile, plus the transformed target logit when the target falls
+//     in the tile.  Logits never leave registers.
 //   k_lse_merge: fixed-order merge of the per-tile pairs into lse and lp; in
 //     loss mode also kl and the masked per-block loss sums.
 //   k_loss_final: fixed-order sum of the block sums -> loss.
@@ -28,6 +29,18 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// tanh(x) = 1 - 2 / (exp(2x) + 1): saturates to +-1 for large |x|, absolute
+// error ~1e-7 near 0 (relative to the softcap that multiplies it).
+__device__ __forceinline__ float tanh_fast(float x) {
+  return 1.f - 2.f * __builtin_amdgcn_rcpf(ex2(x * (2.f * kLog2e)) + 1.f);
+}
+
+// The logit transform of one raw logit (see LogitXform).
+template <bool SC>
+__device__ __forceinline__ float xform(float z, const LogitXform& xf) {
+  return SC ? xf.b * tanh_fast(xf.a * z) : xf.k * z;
+}
 
 // Online log-sum-exp pair combination in base e, carried as (max, sum of
 // exp(z - max)).  An empty side has max = -inf and sum = 0.
@@ -113,10 +126,10 @@ __global__ void __launch_bounds__(64) k_advantages(const float* __restrict__ r, 
 }
 
 // ---------------------------------------------------------------- forward tile
-template <typename T>
+template <typename T, bool SC>
 __global__ void __launch_bounds__(kThreads, 1)
     k_lse_partials(const T* __restrict__ W, const T* __restrict__ H, const int32_t* __restrict__ y,
-                   int64_t V, int64_t d, int n_tok, int cpad, int tm, int tn,
+                   int64_t V, int64_t d, int n_tok, int cpad, int tm, int tn, LogitXform xf,
                    float* __restrict__ part_m, float* __restrict__ part_s,
                    float* __restrict__ zy) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -137,7 +150,9 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int wm0 = (wave >> 1) * 128;
   const bool full = mvalid >= wm0 + 128;
 
-  // per token column j of this lane: (max, sum exp) over its 32 vocabulary rows
+  // per token column j of this lane: (max, sum exp) of the transformed logits
+  // over its 32 vocabulary rows.  The transform is increasing, so the max of
+  // the transformed logits is the transform of the raw max.
   float mx[kWN], sm[kWN];
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
@@ -147,14 +162,25 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
       for (int e = 0; e < kAcc; ++e)
         if (full || acc_row(wave, lane, i, e) < mvalid) m = fmaxf(m, acc[i][j][e]);
-    const float mb = m * kLog2e;
+    const float mt = m == kNegInf ? kNegInf : xform<SC>(m, xf);
+    const float mb = mt * kLog2e;
     float s = 0.f;
+    if (SC) {
 #pragma unroll
-    for (int i = 0; i < kWM; ++i)
+      for (int i = 0; i < kWM; ++i)
 #pragma unroll
-      for (int e = 0; e < kAcc; ++e)
-        if (full || acc_row(wave, lane, i, e) < mvalid) s += ex2(fmaf(acc[i][j][e], kLog2e, -mb));
-    mx[j] = m;
+        for (int e = 0; e < kAcc; ++e)
+          if (full || acc_row(wave, lane, i, e) < mvalid)
+            s += ex2(fmaf(xform<true>(acc[i][j][e], xf), kLog2e, -mb));
+    } else {
+      const float kl = xf.k * kLog2e;
+#pragma unroll
+      for (int i = 0; i < kWM; ++i)
+#pragma unroll
+        for (int e = 0; e < kAcc; ++e)
+          if (full || acc_row(wave, lane, i, e) < mvalid) s += ex2(fmaf(acc[i][j][e], kl, -mb));
+    }
+    mx[j] = mt;
     sm[j] = s;
   }
   // the four 16-lane groups of a wave hold the same token columns
@@ -182,7 +208,7 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
           for (int e = 0; e < kAcc; ++e)
             if (i == ti && e == te) v = acc[i][j][e];
-        zy[t] = v;
+        zy[t] = xform<SC>(v, xf);
       }
     }
   }
@@ -360,8 +386,8 @@ __global__ void __launch_bounds__(256)
                const int32_t* __restrict__ y, const float* __restrict__ adv,
                const float* __restrict__ ref_lp, const float* __restrict__ lp,
                const float* __restrict__ lse, int64_t L, float beta, float grad_loss,
-               T* __restrict__ H_act, float* __restrict__ coef, float* __restrict__ lse_c,
-               int32_t* __restrict__ y_c, float* __restrict__ tgt_c) {
+               LogitXform xf, T* __restrict__ H_act, float* __restrict__ coef,
+               float* __restrict__ lse_c, int32_t* __restrict__ y_c, float* __restrict__ tgt_c) {
   const int cnt = count[0];
   if (c0 >= cnt) return;
   const int j = blockIdx.x;
@@ -379,9 +405,15 @@ __global__ void __launch_bounds__(256)
       coef[j] = c;
       lse_c[j] = lse[t];
       y_c[j] = y[t];
-      // the target's own dZ entry c (1 - p_y), with p_y = exp(lp): the logit the
-      // backward recomputes is bitwise the forward's, so lp holds the same p_y
-      tgt_c[j] = c * -expm1f(lp[t]);
+      // the target's own dZ entry c (1 - p_y) f'(z_y), with p_y = exp(lp): the
+      // logit the backward recomputes is bitwise the forward's, so lp holds the
+      // same p_y; with a cap, f'(z_y) = a b (1 - t^2), t = z'_y / b = (lp + lse) / b
+      float slope = xf.k;
+      if (xf.softcap) {
+        const float tt = fminf(1.f, fmaxf(-1.f, (lp[t] + lse[t]) / xf.b));
+        slope = xf.a * xf.b * (1.f - tt * tt);
+      }
+      tgt_c[j] = c * -expm1f(lp[t]) * slope;
     } else {
       coef[j] = 0.f;
       lse_c[j] = 0.f;
@@ -397,19 +429,27 @@ __global__ void __launch_bounds__(256)
 constexpr int kStagePitch = 528;
 constexpr int kDzLdsBytes = (kLdsBytes > 256 * kStagePitch) ? kLdsBytes : 256 * kStagePitch;
 
-template <typename T>
+// c_t (onehot - p) f'(z) for one raw logit z (float32 path).
+template <bool SC>
 __device__ __forceinline__ float dz_value(float z, float ct, float lb, int64_t v, int64_t yl,
-                                          int vs_valid) {
-  const float p = ex2(fmaf(z, kLog2e, -lb));
+                                          int vs_valid, const LogitXform& xf) {
+  float slope = xf.k, zt = xf.k * z;
+  if (SC) {
+    const float t = tanh_fast(xf.a * z);
+    zt = xf.b * t;
+    slope = xf.a * xf.b * (1.f - t * t);
+  }
+  const float p = ex2(fmaf(zt, kLog2e, -lb));
   const float onehot = v == yl ? 1.f : 0.f;
-  return v < vs_valid ? ct * (onehot - p) : 0.f;
+  return v < vs_valid ? ct * (onehot - p) * slope : 0.f;
 }
 
-template <typename T>
+template <typename T, bool SC>
 __global__ void __launch_bounds__(kThreads, 1)
     k_dz(const T* __restrict__ W, const T* __restrict__ H_act, int64_t d, int64_t v0,
          int vs_valid, int vs, const int32_t* __restrict__ count, int64_t c0, int C, int cpad,
-         int tm, int tn, const float* __restrict__ coef, const float* __restrict__ lse_c,
+         int tm, int tn, LogitXform xf, const float* __restrict__ coef,
+         const float* __restrict__ lse_c,
          const int32_t* __restrict__ y_c, const float* __restrict__ tgt_c, T* __restrict__ dZ,
          T* __restrict__ dZT) {
   __shared__ __attribute__((aligned(1024))) char smem[kDzLdsBytes];
@@ -448,7 +488,7 @@ __global__ void __launch_bounds__(kThreads, 1)
         float q[kAcc];
 #pragma unroll
         for (int u = 0; u < kAcc; ++u)
-          q[u] = dz_value<T>(acc[i][j][u], ct[j], lb[j], v + u, yl[j], vs_valid);
+          q[u] = dz_value<SC>(acc[i][j][u], ct[j], lb[j], v + u, yl[j], vs_valid, xf);
         store4(dZ + (int64_t)t * vs + v, q[0], q[1], q[2], q[3]);
 #pragma unroll
         for (int u = 0; u < kAcc; ++u) dZT[(int64_t)(v + u) * cpad + t] = to_elem<T>(q[u]);
@@ -460,14 +500,29 @@ __global__ void __launch_bounds__(kThreads, 1)
   typedef __attribute__((ext_vector_type(4))) int i32x4_t;
   typedef __attribute__((ext_vector_type(4))) short s16x4_t;
   typedef __attribute__((ext_vector_type(8))) short s16x8_t;
-  // 1. every entry as if it were not the target, in place: -c_t p
+  // 1. every entry as if it were not the target, in place: -c_t p f'(z)
+  if (SC) {
 #pragma unroll
-  for (int j = 0; j < kWN; ++j) {
-    const float nc = -ct[j];
+    for (int j = 0; j < kWN; ++j) {
+      const float nc = -ct[j] * xf.a * xf.b;
 #pragma unroll
-    for (int i = 0; i < kWM; ++i)
+      for (int i = 0; i < kWM; ++i)
 #pragma unroll
-      for (int e = 0; e < kAcc; ++e) acc[i][j][e] = nc * ex2(fmaf(acc[i][j][e], kLog2e, -lb[j]));
+        for (int e = 0; e < kAcc; ++e) {
+          const float t = tanh_fast(xf.a * acc[i][j][e]);
+          acc[i][j][e] = nc * (1.f - t * t) * ex2(fmaf(xf.b * t, kLog2e, -lb[j]));
+        }
+    }
+  } else {
+    const float kl = xf.k * kLog2e;
+#pragma unroll
+    for (int j = 0; j < kWN; ++j) {
+      const float nc = -ct[j] * xf.k;
+#pragma unroll
+      for (int i = 0; i < kWM; ++i)
+#pragma unroll
+        for (int e = 0; e < kAcc; ++e) acc[i][j][e] = nc * ex2(fmaf(acc[i][j][e], kl, -lb[j]));
+    }
   }
   if (m0 + kBM > vs_valid) {
     // ragged last vocabulary tile of the slab: rows past it hold zeros
@@ -495,7 +550,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
   }
   __syncthreads();
-  // 3. the target entry of each token, c_t (1 - p_y), if it falls in this tile
+  // 3. the target entry of each token, c_t (1 - p_y) f'(z_y), if it falls in this tile
   for (int tl = (int)threadIdx.x; tl < kBN; tl += kThreads) {
     const int64_t yr = (int64_t)y_c[n0 + tl] - v0 - m0;  // y_c = -1 for padding tokens
     if (yr >= 0 && yr < kBM && m0 + yr < vs_valid)
@@ -687,12 +742,16 @@ hipError_t launch_advantages(const float* rewards, int64_t groups, int64_t G, fl
 
 template <typename T>
 hipError_t launch_lse_partials(const T* W, const T* H, const int32_t* y, int64_t V, int64_t d,
-                               int n_tok, int cpad, float* part_m, float* part_s, float* zy,
-                               hipStream_t s) {
+                               int n_tok, int cpad, const LogitXform& xf, float* part_m,
+                               float* part_s, float* zy, hipStream_t s) {
   ScopedKernelTimer timer_(KK_LSE_PARTIALS, s);
   const int tm = cdiv(V, kBM), tn = cdiv(n_tok, kBN);
-  hipLaunchKernelGGL(k_lse_partials<T>, dim3(tm * tn), dim3(kThreads), 0, s, W, H, y, V, d, n_tok,
-                     cpad, tm, tn, part_m, part_s, zy);
+  if (xf.softcap)
+    hipLaunchKernelGGL((k_lse_partials<T, true>), dim3(tm * tn), dim3(kThreads), 0, s, W, H, y, V,
+                       d, n_tok, cpad, tm, tn, xf, part_m, part_s, zy);
+  else
+    hipLaunchKernelGGL((k_lse_partials<T, false>), dim3(tm * tn), dim3(kThreads), 0, s, W, H, y,
+                       V, d, n_tok, cpad, tm, tn, xf, part_m, part_s, zy);
   return hipGetLastError();
 }
 
@@ -735,25 +794,32 @@ template <typename T>
 hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int32_t* count,
                            int64_t c0, int C, int cpad, const int32_t* y, const uint8_t* mask,
                            const float* adv, const float* ref_lp, const float* lp,
-                           const float* lse, int64_t L, float beta, float grad_loss, T* H_act,
-                           float* coef, float* lse_c, int32_t* y_c, float* tgt_c, hipStream_t s) {
+                           const float* lse, int64_t L, float beta, float grad_loss,
+                           const LogitXform& xf, T* H_act, float* coef, float* lse_c,
+                           int32_t* y_c, float* tgt_c, hipStream_t s) {
   ScopedKernelTimer timer_(KK_BWD_PREP, s);
   (void)mask;
   hipLaunchKernelGGL(k_bwd_prep<T>, dim3(cpad), dim3(256), 0, s, H, d, idx, count, c0, C, y, adv,
-                     ref_lp, lp, lse, L, beta, grad_loss, H_act, coef, lse_c, y_c, tgt_c);
+                     ref_lp, lp, lse, L, beta, grad_loss, xf, H_act, coef, lse_c, y_c, tgt_c);
   return hipGetLastError();
 }
 
 template <typename T>
 hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,
-                     int vs, const int32_t* count, int64_t c0, int C, int cpad, const float* coef,
-                     const float* lse_c, const int32_t* y_c, const float* tgt_c, T* dZ, T* dZT,
-                     hipStream_t s) {
+                     int vs, const int32_t* count, int64_t c0, int C, int cpad,
+                     const LogitXform& xf, const float* coef, const float* lse_c,
+                     const int32_t* y_c, const float* tgt_c, T* dZ, T* dZT, hipStream_t s) {
   ScopedKernelTimer timer_(KK_DZ, s);
   (void)V;
   const int tm = cdiv(vs_valid, kBM), tn = cdiv(C, kBN);
-  hipLaunchKernelGGL(k_dz<T>, dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0, vs_valid, vs,
-                     count, c0, C, cpad, tm, tn, coef, lse_c, y_c, tgt_c, dZ, dZT);
+  if (xf.softcap)
+    hipLaunchKernelGGL((k_dz<T, true>), dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0,
+                       vs_valid, vs, count, c0, C, cpad, tm, tn, xf, coef, lse_c, y_c, tgt_c, dZ,
+                       dZT);
+  else
+    hipLaunchKernelGGL((k_dz<T, false>), dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0,
+                       vs_valid, vs, count, c0, C, cpad, tm, tn, xf, coef, lse_c, y_c, tgt_c, dZ,
+                       dZT);
   return hipGetLastError();
 }
 
@@ -817,17 +883,18 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
 
 #define GRPO_INSTANTIATE(T)                                                                       \
   template hipError_t launch_lse_partials<T>(const T*, const T*, const int32_t*, int64_t,         \
-                                             int64_t, int, int, float*, float*, float*,           \
-                                             hipStream_t);                                        \
+                                             int64_t, int, int, const LogitXform&, float*,        \
+                                             float*, float*, hipStream_t);                        \
   template hipError_t launch_transpose<T>(const T*, int64_t, int64_t, T*, int64_t, hipStream_t);  \
   template hipError_t launch_bwd_prep<T>(const T*, int64_t, const int32_t*, const int32_t*,       \
                                          int64_t, int, int, const int32_t*, const uint8_t*,        \
                                          const float*, const float*, const float*, const float*,  \
-                                         int64_t, float, float, T*, float*, float*, int32_t*,      \
-                                         float*, hipStream_t);                                    \
+                                         int64_t, float, float, const LogitXform&, T*, float*,     \
+                                         float*, int32_t*, float*, hipStream_t);                  \
   template hipError_t launch_dz<T>(const T*, const T*, int64_t, int64_t, int64_t, int, int,       \
-                                   const int32_t*, int64_t, int, int, const float*, const float*, \
-                                   const int32_t*, const float*, T*, T*, hipStream_t);            \
+                                   const int32_t*, int64_t, int, int, const LogitXform&,         \
+                                   const float*, const float*, const int32_t*, const float*, T*,  \
+                                   T*, hipStream_t);                                              \
   template hipError_t launch_dh_gemm<T>(const T*, int64_t, int64_t, int, const T*, int, int64_t,  \
                                         const int32_t*, int64_t, int, int, int, int, float*,      \
                                         hipStream_t);                                             \

@@ -9,6 +9,17 @@ namespace grpo {
 // Tokens per block of the forward merge kernel (one loss partial per block).
 constexpr int kMergeTokens = 32;
 
+// Logit transform applied to every z = h . w before the log-softmax:
+//   without a cap:  z' = k z                      (k = scale / temperature)
+//   with a cap:     z' = b tanh(a z)              (a = scale / cap, b = cap / temperature)
+// with scale = multiply / divide.  k, a, b > 0.  The identity is k = 1, no cap.
+struct LogitXform {
+  float k;
+  float a;
+  float b;
+  int softcap;
+};
+
 // Logical tile grid of one GEMM-shaped launch.
 struct Grid2 {
   int tm;  // tiles along M (A rows)
@@ -22,8 +33,8 @@ hipError_t launch_advantages(const float* rewards, int64_t groups, int64_t G, fl
 // for the tokens [0, n_tok) of one chunk whose hidden states start at H.
 template <typename T>
 hipError_t launch_lse_partials(const T* W, const T* H, const int32_t* y, int64_t V, int64_t d,
-                               int n_tok, int cpad, float* part_m, float* part_s, float* zy,
-                               hipStream_t s);
+                               int n_tok, int cpad, const LogitXform& xf, float* part_m,
+                               float* part_s, float* zy, hipStream_t s);
 
 // Merge the partials of one chunk (tokens c0 .. c0 + n_tok - 1).
 // mode 0: reference log-probs -> out_lp.  mode 1: loss forward.
@@ -48,14 +59,15 @@ template <typename T>
 hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int32_t* count,
                            int64_t c0, int C, int cpad, const int32_t* y, const uint8_t* mask,
                            const float* adv, const float* ref_lp, const float* lp,
-                           const float* lse, int64_t L, float beta, float grad_loss, T* H_act,
-                           float* coef, float* lse_c, int32_t* y_c, float* tgt_c, hipStream_t s);
+                           const float* lse, int64_t L, float beta, float grad_loss,
+                           const LogitXform& xf, T* H_act, float* coef, float* lse_c,
+                           int32_t* y_c, float* tgt_c, hipStream_t s);
 
 template <typename T>
 hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,
-                     int vs, const int32_t* count, int64_t c0, int C, int cpad, const float* coef,
-                     const float* lse_c, const int32_t* y_c, const float* tgt_c, T* dZ, T* dZT,
-                     hipStream_t s);
+                     int vs, const int32_t* count, int64_t c0, int C, int cpad,
+                     const LogitXform& xf, const float* coef, const float* lse_c,
+                     const int32_t* y_c, const float* tgt_c, T* dZ, T* dZT, hipStream_t s);
 
 // dH_acc holds nsplit partial buffers of [cpad, d] floats; split sp covers
 // one contiguous share of the slab's vocabulary columns.

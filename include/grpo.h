@@ -144,6 +144,47 @@ int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t*
                   size_t workspace_bytes, void* stream);
 
 /*
+ * Optional logit transform (Unsloth docs, "Flattened sequence length
+ * chunking": the chunked log-softmax takes logit_scale_multiply,
+ * logit_scale_divide, logit_softcapping and temperature, and supports
+ * softcapping and temperature).  The pages give no formulas; applied here in
+ * the order of those arguments to every logit z = h . w before the
+ * log-softmax:
+ *   z * multiply, / divide, cap * tanh(z / cap), / temperature.
+ * A zero multiply, divide or cap is "off"; a zero temperature means 1, so a
+ * zero-initialised struct is the identity.  Every field must be finite and
+ * >= 0 (GRPO_ERR_INVALID_ARG otherwise).  lp, lse, kl and the gradients are
+ * those of the transformed logits.
+ */
+typedef struct grpo_logit_opts {
+  float logit_scale_multiply;
+  float logit_scale_divide;
+  float logit_softcapping;
+  float temperature;
+} grpo_logit_opts;
+
+/*
+ * grpo_ref_logprobs, grpo_loss_fwd and grpo_loss_bwd with a logit transform
+ * (`opts` may be NULL: the identity, exactly the calls above).  Arguments and
+ * outputs are otherwise those of the plain calls; grpo_loss_bwd_ex must get
+ * the opts of the grpo_loss_fwd_ex call that produced lp and lse, and the
+ * reference log-probs are taken with the same opts.
+ */
+int grpo_ref_logprobs_ex(const void* H_ref, const void* W, const int32_t* y, int64_t N, int64_t d,
+                         int64_t V, int dtype, int64_t chunk, const grpo_logit_opts* opts,
+                         float* ref_lp, void* workspace, size_t workspace_bytes, void* stream);
+int grpo_loss_fwd_ex(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                     const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
+                     int64_t V, int dtype, float beta, int64_t chunk, const grpo_logit_opts* opts,
+                     float* loss, float* lp, float* kl, float* lse, void* workspace,
+                     size_t workspace_bytes, void* stream);
+int grpo_loss_bwd_ex(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                     const float* adv, const float* ref_lp, const float* lp, const float* lse,
+                     int64_t B, int64_t L, int64_t d, int64_t V, int dtype, float beta,
+                     float grad_loss, int64_t chunk, const grpo_logit_opts* opts, void* dH,
+                     float* dW, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Diagnostic: C[M, N] (float32, row-major, written) = A[M, K] . B[N, K]^T,
  * through the same MFMA tile main loop the loss kernels use (A, B dtype
  * elements, both rows contiguous along K).  K times the element size must be

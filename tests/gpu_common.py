@@ -17,32 +17,32 @@ def to64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def gpu_chain(inp, w, beta=BETA, chunk=None, grad_loss=1.0, ref_from=None):
+def gpu_chain(inp, w, beta=BETA, chunk=None, grad_loss=1.0, ref_from=None, opts=None):
     """All outputs of the HIP path for inputs `inp` (tensors on the GPU)."""
     chunk = w.chunk if chunk is None else chunk
     adv = gp.grpo_advantages(inp["rewards"], w.G, EPS)
     H_ref = inp["H_ref"] if ref_from is None else ref_from
-    ref = gp.grpo_ref_logprobs(H_ref, inp["W"], inp["y"], chunk)
+    ref = gp.grpo_ref_logprobs(H_ref, inp["W"], inp["y"], chunk, logit_opts=opts)
     loss, lp, kl, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref,
-                                         w.B, w.L, beta, chunk)
+                                         w.B, w.L, beta, chunk, logit_opts=opts)
     dH, dW = gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp, lse,
-                              w.B, w.L, beta, grad_loss, chunk)
+                              w.B, w.L, beta, grad_loss, chunk, logit_opts=opts)
     torch.cuda.synchronize()
     return dict(adv=adv, ref=ref, loss=loss, lp=lp, kl=kl, lse=lse, dH=dH, dW=dW)
 
 
-def oracle_chain(inp, w, beta=BETA, grad_loss=1.0, backward=True, ref_from=None):
+def oracle_chain(inp, w, beta=BETA, grad_loss=1.0, backward=True, ref_from=None, opts=None):
     """Float64 oracle outputs for the same inputs (copied to the host)."""
     H, W = to64(inp["H"]), to64(inp["W"])
     H_ref = to64(inp["H_ref"] if ref_from is None else ref_from)
     y = inp["y"].cpu().numpy().astype(np.int64)
     mask = inp["mask"].cpu().numpy()
     adv = oracle.group_advantages(inp["rewards"].cpu().numpy(), w.G, EPS)
-    ref, _ = oracle.token_logprobs(H_ref, W, y)
-    out = oracle.loss_forward(H, W, y, mask, adv, ref, w.L, beta)
+    ref, _ = oracle.token_logprobs(H_ref, W, y, opts=opts)
+    out = oracle.loss_forward(H, W, y, mask, adv, ref, w.L, beta, opts=opts)
     out.update(adv=adv, ref=ref)
     if backward:
-        dH, dW = oracle.loss_backward(H, W, y, mask, adv, ref, w.L, beta, grad_loss)
+        dH, dW = oracle.loss_backward(H, W, y, mask, adv, ref, w.L, beta, grad_loss, opts=opts)
         out.update(dH=dH, dW=dW)
     return out
 

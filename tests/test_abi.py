@@ -143,3 +143,16 @@ def test_binding_refuses_cpu_tensors():
     H = torch.zeros(4, 8)
     with pytest.raises(ValueError):
         gp.grpo_ref_logprobs(H, torch.zeros(16, 8), torch.zeros(4, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("field,value", [("temperature", -1.0), ("logit_softcapping", -30.0),
+                                         ("logit_scale_multiply", float("nan")),
+                                         ("logit_scale_divide", float("inf"))])
+def test_logit_opts_rejected_before_any_launch(field, value):
+    import ctypes
+    opts = _lib.LogitOpts(**{field: value})
+    one = ctypes.c_void_p(16)        # never dereferenced: the options are checked first
+    st = L.grpo_ref_logprobs_ex(one, one, one, 8, 16, 32, 0, 8, ctypes.pointer(opts), one, one,
+                                1 << 20, None)
+    assert st == -1
+    assert b"logit opts" in L.grpo_last_error()

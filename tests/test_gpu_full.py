@@ -152,3 +152,52 @@ def test_full_size_exact_dW_with_sparse_mask(name):
     others = torch.ones(w.N, dtype=torch.bool, device="cuda")
     others[torch.as_tensor(keep, device="cuda")] = False
     assert torch.all(dH[others] == 0)
+
+
+def test_full_size_logit_transform_sampled_parity():
+    """Qwen2.5-1.5B shape with softcap 30 and temperature 0.9 (the launch
+    configuration the benchmark times, plus the transform): lp/ref/lse of sampled
+    tokens and dH of sampled active rows against the oracle's transformed logits."""
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    w = workloads.BY_NAME["qwen2.5-1.5b-bf16"]
+    opts = {"logit_softcapping": 30.0, "temperature": 0.9}
+    print(f"[full-xform] {w.name} {opts}", flush=True)
+    inp = workloads.generate(w, seed=13, device="cuda")
+    adv = gp.grpo_advantages(inp["rewards"], w.G, EPS)
+    ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, logit_opts=opts)
+    loss, lp, kl, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref,
+                                         w.B, w.L, BETA, w.chunk, logit_opts=opts)
+    dH, dW = gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp, lse,
+                              w.B, w.L, BETA, 1.0, w.chunk, logit_opts=opts)
+    torch.cuda.synchronize()
+    y = inp["y"].cpu().numpy().astype(np.int64)
+    mask = inp["mask"].cpu().numpy()
+    A = oracle.group_advantages(inp["rewards"].cpu().numpy(), w.G, EPS)
+    W64 = to64(inp["W"])
+    rng = np.random.default_rng(17)
+    rows = _sample_rows(w.N, w.L, 256, rng, [0, w.N - 1])
+    o_lp, o_lse = oracle.token_logprobs(to64(inp["H"][torch.as_tensor(rows, device="cuda")]), W64,
+                                        y[rows], opts=opts)
+    o_ref, _ = oracle.token_logprobs(to64(inp["H_ref"][torch.as_tensor(rows, device="cuda")]), W64,
+                                     y[rows], opts=opts)
+    g_lp, g_ref, g_lse = (to64(t)[rows] for t in (lp, ref, lse))
+    print(f"[full-xform] max|dlp| {np.abs(g_lp - o_lp).max():.2e} "
+          f"max|dlse| {np.abs(g_lse - o_lse).max():.2e}", flush=True)
+    assert np.abs(g_lp - o_lp).max() <= 2e-4
+    assert np.abs(g_ref - o_ref).max() <= 2e-4
+    assert np.abs(g_lse - o_lse).max() <= 2e-4
+    act = np.nonzero(mask)[0]
+    drows = np.array(sorted(set(rng.choice(act, size=256, replace=False).tolist())))
+    H64 = np.zeros((w.N, w.d))
+    H64[drows] = to64(inp["H"][torch.as_tensor(drows, device="cuda")])
+    ref64 = np.zeros(w.N)
+    ref64[drows], _ = oracle.token_logprobs(to64(inp["H_ref"][torch.as_tensor(drows, device="cuda")]),
+                                            W64, y[drows], opts=opts)
+    o_dH, _ = oracle.loss_backward(H64, W64, y, mask, A, ref64, w.L, BETA, dh_rows=drows,
+                                   want_dW=False, opts=opts)
+    g_dH = to64(dH[torch.as_tensor(drows, device="cuda")])
+    print(f"[full-xform] dH rows cos {cosine(g_dH, o_dH):.6f} maxrel {max_abs_rel(g_dH, o_dH):.2e}",
+          flush=True)
+    assert cosine(g_dH, o_dH) >= 0.999
+    assert max_abs_rel(g_dH, o_dH) <= 1e-2

@@ -213,3 +213,45 @@ def test_degenerate_shapes_pure_kl(N, d, V):
     else:
         assert max_abs_rel(to64(g["dW"]), o["dW"]) <= 1e-4
         assert max_abs_rel(to64(g["dH"]), o["dH"]) <= 1e-4
+
+
+XFORMS = [
+    {"temperature": 0.7},
+    {"logit_softcapping": 3.0},
+    {"logit_scale_multiply": 1.3, "logit_scale_divide": 0.8, "logit_softcapping": 2.5,
+     "temperature": 1.25},
+]
+
+
+@pytest.mark.parametrize("opts", XFORMS, ids=["temperature", "softcap", "all"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chain_with_logit_transform_matches_oracle(dtype, opts):
+    """Scale, softcap and temperature through the whole chain (ragged V = 1000,
+    chunks of 256 over 600 tokens) against the oracle's transformed logits."""
+    _need_gpu()
+    w = small(dtype)
+    inp = inputs(w, seed=8)
+    g = gpu_chain(inp, w, opts=opts)
+    o = oracle_chain(inp, w, opts=opts)
+    if dtype == "f32":
+        np.testing.assert_allclose(to64(g["ref"]), o["ref"], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(to64(g["lp"]), o["lp"], rtol=1e-5, atol=1e-6)
+        assert abs(g["loss"].item() - o["loss"]) <= 1e-5 * abs(o["loss"])
+        for k in ("dH", "dW"):
+            assert max_abs_rel(to64(g[k]), o[k]) <= 1e-4, k
+    else:
+        assert np.abs(to64(g["lp"]) - o["lp"]).max() <= 1e-4
+        assert abs(g["loss"].item() - o["loss"]) <= 2e-3 * abs(o["loss"])
+        for k in ("dH", "dW"):
+            assert cosine(to64(g[k]), o[k]) >= 0.999, k
+            assert max_abs_rel(to64(g[k]), o[k]) <= 1e-2, k
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_logit_transform_keeps_kl_exactly_zero_for_policy_equal_reference(dtype):
+    _need_gpu()
+    w = small(dtype)
+    inp = inputs(w, seed=9)
+    g = gpu_chain(inp, w, ref_from=inp["H"], opts=XFORMS[2])
+    assert torch.equal(g["ref"], g["lp"])
+    assert torch.all(g["kl"] == 0)
