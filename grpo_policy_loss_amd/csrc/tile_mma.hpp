@@ -18,10 +18,17 @@
 //  * Every instruction of a k-step is placed by hand (scheduling fences): the
 //    64 MFMAs of the step, one LDS fragment read for the next k-step after each
 //    even MFMA of its first half, and -- in the step after the slice barrier --
-//    one slice copy after every fourth MFMA.  Left to itself the compiler
-//    clusters the copies (each needs its own M0 write) and the matrix core
-//    idles; the fixed order measured +8 points of bf16 peak over the
+//    one slice copy after every third MFMA from the first.  Left to itself the
+//    compiler clusters the copies (each needs its own M0 write) and the matrix
+//    core idles; the fixed order measured +8 points of bf16 peak over the
 //    compiler's schedule of the same loop.
+//  * With one wave per SIMD, whatever sits between two MFMAs must issue within
+//    the 16 cycles of the first one.  A copy of a slice that lies wholly inside
+//    k therefore costs no vector instruction: each lane's row-and-chunk offset
+//    is computed once, the slice offset rides in the scalar offset, and only
+//    M0 changes per copy.  The per-lane k-bound check (three VALU operations
+//    per copy, measured 3 to 5 points of peak) is left to the slices at and
+//    past the k tail.
 //  * Slice barrier after the first k-step: every wave then holds the slice's
 //    last fragments, so the stage is free for the copy of slice kt + 2, and
 //    (after each wave's own vmcnt wait) slice kt + 1 is visible.  Copies of
@@ -106,6 +113,7 @@ struct Loader {
   uint32_t chunk_bytes;     // logical 16-byte chunk this lane copies, even 8-row groups
   uint32_t chunk_bytes_odd; // the same for odd 8-row groups (f(r) flips bit 0)
   uint32_t k_bytes;
+  uint32_t voff[8];         // rowoff[j] + this lane's chunk (kOOB if the row is absent)
 
   __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
     int rv = op.rows_valid < 0 ? 0 : (op.rows_valid > kBM ? kBM : op.rows_valid);
@@ -119,6 +127,9 @@ struct Loader {
       rowoff[j] = r < rv ? (uint32_t)r * op.ld_bytes : kOOB;
     }
     k_bytes = op.k_bytes;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      voff[j] = rowoff[j] == kOOB ? kOOB : rowoff[j] + ((j & 1) ? chunk_bytes_odd : chunk_bytes);
   }
 
   // Copy instruction j (rows 8 j .. 8 j + 7 of this wave's 64) of slice `kt`.
@@ -128,6 +139,15 @@ struct Loader {
     const uint32_t off = kb < k_bytes ? rowoff[j] + kb : kOOB;
     char GRPO_LDS* dst = tile + (wave * 64 + j * 8) * kBKB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, off, 0, 0, kCopyPolicy);
+  }
+  // The same copy for a slice with kt * 128 + 128 <= k_bytes: the slice offset
+  // travels in the scalar offset.  A present row stays inside its own bytes and
+  // an absent one (voff = kOOB) stays past the range, whether or not the range
+  // check counts the scalar offset.
+  __device__ __forceinline__ void issue1_full(int kt, int j, char GRPO_LDS* tile, int wave) const {
+    char GRPO_LDS* dst = tile + (wave * 64 + j * 8) * kBKB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, voff[j], kt * kBKB, 0,
+                                             kCopyPolicy);
   }
   __device__ __forceinline__ void issue(int kt, char GRPO_LDS* tile, int wave) const {
 #pragma unroll
@@ -160,9 +180,9 @@ __device__ __forceinline__ f32x4_t mfma_block(f32x4_t c, const f32x4_t& a, const
 // One 64-byte k-step of the wave's 8 x 8 blocks, in a fixed order.  After
 // block q: for READ and even q < 32, LDS read q / 2 of the next k-step's
 // fragments (a0..a7, then b0..b7) from stage `rst` at chunk offset `sw`; for
-// COPY and q % 4 == 3, copy instruction q / 4 of slice `ckt` into stage `cst`
-// (A rows for q / 4 < 8, then B rows).
-template <typename T, bool READ, bool COPY>
+// COPY and q % 3 == 0, q < 48, copy instruction q / 3 of slice `ckt` into
+// stage `cst` (A rows for q / 3 < 8, then B rows), unchecked when FULL.
+template <typename T, bool READ, bool COPY, bool FULL = false>
 __device__ __forceinline__ void kstep(Acc& acc, const typename Frag<T>::type (&a)[kWM],
                                       const typename Frag<T>::type (&b)[kWN],
                                       typename Frag<T>::type (&na)[kWM], typename Frag<T>::type (&nb)[kWN],
@@ -181,10 +201,15 @@ __device__ __forceinline__ void kstep(Acc& acc, const typename Frag<T>::type (&a
       else nb[f - kWM] = *(const F GRPO_LDS*)(rst + kTileBytes + bbase + (f - kWM) * 16 * kBKB + sw);
       GRPO_FENCE();
     }
-    if (COPY && (q & 3) == 3) {
-      const int c = q >> 2;
-      if (c < 8) la.issue1(ckt, c, cst, wave);
-      else lb.issue1(ckt, c - 8, cst + kTileBytes, wave);
+    if (COPY && q % 3 == 0 && q < 48) {
+      const int c = q / 3;
+      if (FULL) {
+        if (c < 8) la.issue1_full(ckt, c, cst, wave);
+        else lb.issue1_full(ckt, c - 8, cst + kTileBytes, wave);
+      } else {
+        if (c < 8) la.issue1(ckt, c, cst, wave);
+        else lb.issue1(ckt, c - 8, cst + kTileBytes, wave);
+      }
       GRPO_FENCE();
     }
   }
@@ -230,7 +255,11 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
     fb0[f] = *(const F GRPO_LDS*)(lds + kTileBytes + bbase + f * 16 * kBKB + sw0);
 
   int kt = 0;
-  for (; kt + 1 < k_slices; ++kt) {
+  // Slices wholly inside k in both operands take unchecked copies; the k tail
+  // and the zero slices past it take the checked ones.
+  const int full_a = (int)(A.k_bytes / kBKB), full_b = (int)(B.k_bytes / kBKB);
+  const int full = full_a < full_b ? full_a : full_b;
+  for (; kt + 2 < full; ++kt) {
     char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
     char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
     // k-step 0: read k-step 1's fragments of this slice
@@ -240,7 +269,18 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
     __builtin_amdgcn_s_barrier();
     GRPO_FENCE();
     // k-step 1: read slice kt + 1's first fragments; copy slice kt + 2 into this
-    // slice's stage (zeros past the end, drained below)
+    // slice's stage
+    kstep<T, true, true, true>(acc, fa1, fb1, fa0, fb0, nxt, abase, bbase, sw0, la, lb, kt + 2, cur, wave);
+  }
+  for (; kt + 1 < k_slices; ++kt) {
+    char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
+    char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
+    kstep<T, true, false>(acc, fa0, fb0, fa1, fb1, cur, abase, bbase, sw1, la, lb, 0, cur, wave);
+    wait_vmem_all();
+    wait_lds_all();
+    __builtin_amdgcn_s_barrier();
+    GRPO_FENCE();
+    // as above, checked (zeros past the end, drained below)
     kstep<T, true, true>(acc, fa1, fb1, fa0, fb0, nxt, abase, bbase, sw0, la, lb, kt + 2, cur, wave);
   }
   {
