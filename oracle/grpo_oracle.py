@@ -35,6 +35,13 @@ prose fixes the pieces used here:
 Readings where the pages are silent (aggregation, std estimator, masked-token
 outputs, empty mask) are listed in the module-level notes of each function.
 
+The pages' four-run ablation [P-blog, GRPO maths] also trains with the detach
+removed, with a "full" reverse KL carrying the extra factor of Q, and with a
+forward KL; the formulas are lost, and the readings taken here are stated
+with each function (token_kl, token_kl_slope, loss_forward).  A per-sequence
+mean aggregation (mean over each completion's tokens, then over completions)
+is offered beside the global token mean.
+
 Parity unpinned: nothing.  Every function is pinned by the CPU tests against
 closed forms, invariants, library routines (scipy log_softmax, numpy std,
 torch float64 autograd of the literal policy-term expression) and central
@@ -170,6 +177,85 @@ def reverse_kl_k3(ref_lp, lp):
     return np.exp(x) - x - 1.0
 
 
+def forward_kl(ref_lp, lp):
+    """kl = r log r - (r - 1) with r = exp(ref_lp - lp) (unscaled, every token).
+
+    [P-blog, GRPO maths]: the ablation's forward-KL run, KL(P || Q) with P the
+    reference.  The tokens are drawn from Q, so the estimator weights by
+    r = P / Q: r log r - (r - 1) has expectation KL(P || Q) under Q (the r - 1
+    term has mean zero) and is >= 0 pointwise, the forward-direction
+    counterpart of k3 in the estimator family of Schulman's note that the
+    pages cite.
+    """
+    x = _f64(ref_lp) - _f64(lp)
+    r = np.exp(x)
+    return r * x - (r - 1.0)
+
+
+def reverse_kl_q(ref_lp, lp):
+    """kl = q (exp(x) - x - 1), x = ref_lp - lp, q = exp(lp) (every token).
+
+    [P-blog, GRPO maths]: the ablation's "full reverse KL", the k3 term with
+    the extra factor of Q (the trained policy's probability of the sampled
+    token) that the pages' derivation found missing.  Plainest reading: the
+    factor multiplies the per-token term and is differentiated with it.
+    """
+    return np.exp(_f64(lp)) * reverse_kl_k3(ref_lp, lp)
+
+
+KL_ESTIMATORS = ("reverse", "forward", "reverse_q")
+
+
+def _variant(opts):
+    """(kl estimator index, detach removed, per-sequence mean) of an options dict."""
+    o = opts or {}
+    return int(o.get("kl_estimator", 0)), bool(o.get("no_detach", 0)), int(o.get("aggregation", 0))
+
+
+def token_kl(ref_lp, lp, opts=None):
+    """Per-token KL of the estimator that `opts["kl_estimator"]` names:
+    0 reverse k3 (the default), 1 forward, 2 reverse with the factor Q."""
+    k = _variant(opts)[0]
+    if k == 0:
+        return reverse_kl_k3(ref_lp, lp)
+    if k == 1:
+        return forward_kl(ref_lp, lp)
+    if k == 2:
+        return reverse_kl_q(ref_lp, lp)
+    raise ValueError(f"unknown kl_estimator {k}")
+
+
+def token_kl_slope(ref_lp, lp, opts=None):
+    """d token_kl / d lp, elementwise (x = ref_lp - lp, so dx/dlp = -1):
+    k3: 1 - exp(x);  forward: -x exp(x);  reverse with Q: q (k3 + 1 - exp(x)) = -x q."""
+    k = _variant(opts)[0]
+    x = _f64(ref_lp) - _f64(lp)
+    if k == 0:
+        return 1.0 - np.exp(x)
+    if k == 1:
+        return -x * np.exp(x)
+    if k == 2:
+        return -x * np.exp(_f64(lp))
+    raise ValueError(f"unknown kl_estimator {k}")
+
+
+def token_weights(mask, seq_len, opts=None):
+    """w_t with loss = sum_t w_t l_t.
+
+    Global token mean (the default): w_t = m_t / max(sum m, 1), one mean over
+    all unmasked flattened tokens.  Per-sequence mean (`aggregation` 1):
+    w_t = m_t / (B max(n_b, 1)) with n_b the unmasked tokens of t's sequence,
+    i.e. each completion's masked mean, then the plain mean over all B
+    completions (an empty completion contributes 0 and still counts in B).
+    """
+    m = _f64(mask)
+    if _variant(opts)[2] == 1:
+        mb = m.reshape(-1, seq_len)
+        n = mb.sum(axis=1, keepdims=True)
+        return (mb / (mb.shape[0] * np.maximum(n, 1.0))).reshape(-1)
+    return m / max(m.sum(), 1.0)
+
+
 def token_advantages(adv, seq_len):
     """A per flattened token: sequence b's advantage on its seq_len tokens.
 
@@ -180,35 +266,39 @@ def token_advantages(adv, seq_len):
 
 
 def loss_forward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04, opts=None):
-    """Masked token-mean GRPO loss plus the per-token outputs.
+    """Masked GRPO loss plus the per-token outputs.
 
     l_t = -(R_t * A_t - beta * kl_t), with R_t = exp(lp_t - stopgrad(lp_t)),
-    whose value is exactly 1 [P-blog, GRPO maths].
-    loss = sum_t m_t l_t / max(sum_t m_t, 1): one mean over all unmasked
-    flattened tokens (an empty mask gives 0).
+    whose value is exactly 1 [P-blog, GRPO maths]; with the detach removed
+    (`no_detach`) R_t = exp(lp_t - lp_t), still 1 in value.
+    kl_t is token_kl (reverse k3 unless `kl_estimator` says otherwise).
+    loss = sum_t w_t l_t with w from token_weights: by default the mean over
+    all unmasked flattened tokens (an empty mask gives 0).
     lp, kl and lse are reported for every token, masked or not.
     """
     lp, lse = token_logprobs(H, W, y, opts=opts)
-    kl = reverse_kl_k3(ref_lp, lp)
+    kl = token_kl(ref_lp, lp, opts)
     A_t = token_advantages(adv, seq_len)
     R = 1.0
     ell = -(R * A_t - beta * kl)
-    m = _f64(mask)
-    loss = (m * ell).sum() / max(m.sum(), 1.0)
+    loss = (token_weights(mask, seq_len, opts) * ell).sum()
     return dict(loss=float(loss), lp=lp, kl=kl, lse=lse, ell=ell)
 
 
-def loss_coefficients(mask, adv, ref_lp, lp, seq_len, beta=0.04, grad_loss=1.0):
+def loss_coefficients(mask, adv, ref_lp, lp, seq_len, beta=0.04, grad_loss=1.0, opts=None):
     """c_t = d loss / d lp_t.
 
-    From l_t = -(R_t A_t - beta kl_t): dR/dlp = R = 1 and
-    dkl/dlp = 1 - exp(x), so dl_t/dlp_t = -A_t + beta (1 - exp(x_t)).
-    The mean contributes m_t / max(sum m, 1); grad_loss is the upstream scalar.
+    From l_t = -(R_t A_t - beta kl_t): with the detach, dR/dlp = R = 1; with
+    it removed, R = exp(lp - lp) is constant and dR/dlp = 0, so the advantage
+    term carries no gradient [P-blog, GRPO maths: removing the detach broke
+    training].  dkl/dlp is token_kl_slope (1 - exp(x) for k3).  The
+    aggregation contributes w_t (token_weights); grad_loss is the upstream
+    scalar.
     """
-    m = _f64(mask)
     A_t = token_advantages(adv, seq_len)
-    x = _f64(ref_lp) - _f64(lp)
-    return grad_loss * m / max(m.sum(), 1.0) * (-A_t + beta * (1.0 - np.exp(x)))
+    dR = 0.0 if _variant(opts)[1] else 1.0
+    w = token_weights(mask, seq_len, opts)
+    return grad_loss * w * (-dR * A_t + beta * token_kl_slope(ref_lp, lp, opts))
 
 
 def loss_backward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04, grad_loss=1.0,
@@ -237,7 +327,7 @@ def loss_backward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04, grad_loss=1.0,
     # per-token coefficient needs lp of the token: recompute from full logits
     lp_need, _ = token_logprobs(H, W, y, rows=need, block=block, opts=opts)
     lp_all[need] = lp_need
-    c = loss_coefficients(mask, adv, ref_lp, lp_all, seq_len, beta, grad_loss)
+    c = loss_coefficients(mask, adv, ref_lp, lp_all, seq_len, beta, grad_loss, opts)
     dW = np.zeros_like(Wf)
     dH = np.zeros((len(rows), Wf.shape[1]))
     pos = {int(t): i for i, t in enumerate(rows)}
@@ -245,15 +335,14 @@ def loss_backward(H, W, y, mask, adv, ref_lp, seq_len, beta=0.04, grad_loss=1.0,
         sel = need[b0:b0 + block]
         Hs = _f64(H[sel])
         Z = Hs @ Wf.T
-        Zf = logit_transform(Z, opts) if opts else Z
+        Zf = logit_transform(Z, opts)
         M = Zf.max(axis=1, keepdims=True)
         P = np.exp(Zf - M)
         P /= P.sum(axis=1, keepdims=True)
         dZ = -P
         dZ[np.arange(len(sel)), y[sel].astype(np.int64)] += 1.0
         dZ *= c[sel][:, None]
-        if opts:
-            dZ *= logit_transform_slope(Z, opts)
+        dZ *= logit_transform_slope(Z, opts)
         if want_dW:
             dW += dZ.T @ Hs
         g = dZ @ Wf

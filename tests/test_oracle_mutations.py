@@ -51,17 +51,17 @@ MUTATIONS = [
     ("token advantages tiled instead of repeated",
      [("return np.repeat(_f64(adv), seq_len)", "return np.tile(_f64(adv), seq_len)")]),
     ("loss: mean over every token, not the unmasked ones",
-     [("loss = (m * ell).sum() / max(m.sum(), 1.0)", "loss = (m * ell).sum() / len(m)")]),
+     [("    return m / max(m.sum(), 1.0)", "    return m / len(m)")]),
     ("loss: KL penalty added instead of subtracted",
      [("ell = -(R * A_t - beta * kl)", "ell = -(R * A_t + beta * kl)")]),
     ("gradient: KL derivative sign",
-     [("(-A_t + beta * (1.0 - np.exp(x)))", "(-A_t + beta * (np.exp(x) - 1.0))")]),
+     [("        return 1.0 - np.exp(x)", "        return np.exp(x) - 1.0")]),
     ("gradient: advantage sign",
-     [("(-A_t + beta * (1.0 - np.exp(x)))", "(A_t + beta * (1.0 - np.exp(x)))")]),
+     [("(-dR * A_t + beta *", "(dR * A_t + beta *")]),
     ("gradient: mean normalisation dropped",
-     [("return grad_loss * m / max(m.sum(), 1.0) *", "return grad_loss * m *")]),
+     [("return grad_loss * w * (", "return grad_loss * _f64(mask) * (")]),
     ("gradient: grad_loss ignored",
-     [("return grad_loss * m / max(m.sum(), 1.0) *", "return 1.0 * m / max(m.sum(), 1.0) *")]),
+     [("return grad_loss * w * (", "return 1.0 * w * (")]),
     ("dZ: p - onehot instead of onehot - p",
      [("dZ = -P\n", "dZ = P.copy()\n"),
       ("dZ[np.arange(len(sel)), y[sel].astype(np.int64)] += 1.0",
@@ -89,6 +89,32 @@ MUTATIONS = [
     ("backward: softmax of the raw logits, not the transformed ones",
      [("M = Zf.max(axis=1, keepdims=True)\n        P = np.exp(Zf - M)",
        "M = Z.max(axis=1, keepdims=True)\n        P = np.exp(Z - M)")]),
+    ("forward kl: the r - 1 term dropped",
+     [("return r * x - (r - 1.0)", "return r * x")]),
+    ("forward kl: k3 in its place",
+     [("return r * x - (r - 1.0)", "return r - x - 1.0")]),
+    ("forward kl: the ratio inverted",
+     [("    r = np.exp(x)\n    return r * x - (r - 1.0)", "    r = np.exp(-x)\n    return -r * x - (r - 1.0)")]),
+    ("full reverse kl: the factor Q dropped",
+     [("return np.exp(_f64(lp)) * reverse_kl_k3(ref_lp, lp)", "return reverse_kl_k3(ref_lp, lp)")]),
+    ("full reverse kl: the reference's probability as the factor",
+     [("return np.exp(_f64(lp)) * reverse_kl_k3(ref_lp, lp)",
+       "return np.exp(_f64(ref_lp)) * reverse_kl_k3(ref_lp, lp)")]),
+    ("forward kl slope: sign",
+     [("        return -x * np.exp(x)", "        return x * np.exp(x)")]),
+    ("full reverse kl slope: the factor Q held constant",
+     [("        return -x * np.exp(_f64(lp))", "        return np.exp(_f64(lp)) * (1.0 - np.exp(x))")]),
+    ("no-detach switch ignored",
+     [("dR = 0.0 if _variant(opts)[1] else 1.0", "dR = 1.0")]),
+    ("sequence mean: divided by all unmasked tokens",
+     [("return (mb / (mb.shape[0] * np.maximum(n, 1.0))).reshape(-1)",
+       "return (mb / max(mb.sum(), 1.0)).reshape(-1)")]),
+    ("sequence mean: the 1 / B dropped",
+     [("return (mb / (mb.shape[0] * np.maximum(n, 1.0))).reshape(-1)",
+       "return (mb / np.maximum(n, 1.0)).reshape(-1)")]),
+    ("sequence mean: empty completions left out of B",
+     [("return (mb / (mb.shape[0] * np.maximum(n, 1.0))).reshape(-1)",
+       "return (mb / (max(int((n > 0).sum()), 1) * np.maximum(n, 1.0))).reshape(-1)")]),
     ("backward: recomputed logits against the transposed head",
      [("Z = Hs @ Wf.T", "Z = Hs @ Wf[::-1].T")]),
 ]

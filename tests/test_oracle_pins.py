@@ -402,6 +402,125 @@ def test_transform_gradients_match_torch_autograd(opts):
     np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-10, atol=1e-15)
 
 
+# --------------------------------------------------------------------------- ablation variants
+VARIANTS = [
+    {"kl_estimator": 1},
+    {"kl_estimator": 2},
+    {"no_detach": 1},
+    {"aggregation": 1},
+    {"kl_estimator": 1, "no_detach": 1, "aggregation": 1},
+    {"kl_estimator": 2, "temperature": 0.8},
+]
+
+
+def test_kl_estimators_are_unbiased_on_a_small_vocabulary():
+    """Averaged over the trained policy Q on a 9-token vocabulary, k3 is exactly
+    KL(Q || P) and the forward estimator exactly KL(P || Q) (scipy rel_entr)."""
+    rng = np.random.default_rng(40)
+    for _ in range(5):
+        q = scipy.special.softmax(rng.standard_normal(9) * 1.5)
+        p = scipy.special.softmax(rng.standard_normal(9) * 1.5)
+        lp, ref = np.log(q), np.log(p)
+        rev = (q * oracle.token_kl(ref, lp, {"kl_estimator": 0})).sum()
+        fwd = (q * oracle.token_kl(ref, lp, {"kl_estimator": 1})).sum()
+        assert rev == pytest.approx(scipy.special.rel_entr(q, p).sum(), rel=1e-12)
+        assert fwd == pytest.approx(scipy.special.rel_entr(p, q).sum(), rel=1e-12)
+        assert abs(fwd - rev) > 1e-6          # the two directions differ here
+
+
+def test_kl_variant_closed_forms_golden():
+    names = {"forward": 1, "reverse_q": 2}
+    for est, q, pr, want in _table("kl_variants_closed_form.txt"):
+        lp, ref = np.log([float(q)]), np.log([float(pr)])
+        got = oracle.token_kl(ref, lp, {"kl_estimator": names[est]})[0]
+        assert got == pytest.approx(float(want), rel=1e-15, abs=1e-16), (est, q, pr)
+
+
+def test_kl_variants_nonnegative_and_zero_at_equality():
+    rng = np.random.default_rng(41)
+    ref, lp = -rng.random(1000) * 10, -rng.random(1000) * 10
+    for k in (1, 2):
+        assert np.all(oracle.token_kl(ref, lp, {"kl_estimator": k}) > 0)
+        assert np.all(oracle.token_kl(lp, lp, {"kl_estimator": k}) == 0.0)
+
+
+def test_token_weights_hand_example():
+    # B = 3 completions of L = 3: lengths 2, 1, 0
+    mask = np.array([1, 1, 0, 1, 0, 0, 0, 0, 0], dtype=np.uint8)
+    np.testing.assert_allclose(oracle.token_weights(mask, 3),
+                               [1 / 3, 1 / 3, 0, 1 / 3, 0, 0, 0, 0, 0], rtol=0, atol=1e-16)
+    np.testing.assert_allclose(oracle.token_weights(mask, 3, {"aggregation": 1}),
+                               [1 / 6, 1 / 6, 0, 1 / 3, 0, 0, 0, 0, 0], rtol=0, atol=1e-16)
+
+
+def test_sequence_mean_policy_equals_reference_gives_zero_loss():
+    """With kl = 0, the per-sequence mean is -mean_b(A_b), which vanishes because
+    each group's advantages sum to zero; the token mean weights sequences by
+    length and does not vanish for unequal lengths."""
+    p = _problem(42, lo=1, hi=5)
+    ref_lp, _ = oracle.token_logprobs(p["H"], p["W"], p["y"])
+    for k in (0, 1, 2):
+        seq = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], p["adv"], ref_lp, p["L"], BETA,
+                                  opts={"kl_estimator": k, "aggregation": 1})
+        tok = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], p["adv"], ref_lp, p["L"], BETA,
+                                  opts={"kl_estimator": k})
+        assert np.all(seq["kl"] == 0.0)
+        assert abs(seq["loss"]) < 1e-15
+        assert abs(tok["loss"]) > 1e-3
+
+
+def test_no_detach_gradient_is_the_pure_kl_gradient():
+    p = _problem(43, ref_sigma=0.5)
+    nd = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"],
+                              BETA, opts={"no_detach": 1})
+    a0 = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], np.zeros_like(p["adv"]),
+                              p["ref_lp"], p["L"], BETA)
+    np.testing.assert_allclose(nd[0], a0[0], rtol=1e-13, atol=1e-18)
+    np.testing.assert_allclose(nd[1], a0[1], rtol=1e-13, atol=1e-18)
+    # the value is that of the detached loss
+    f = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"], BETA)
+    g = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"], BETA,
+                            opts={"no_detach": 1})
+    assert f["loss"] == g["loss"]
+
+
+@pytest.mark.parametrize("opts", VARIANTS)
+def test_variant_gradients_match_torch_autograd(opts):
+    """Torch float64 autograd of each variant written out literally: the ratio
+    with or without detach, the estimator's expression, the aggregation."""
+    p = _problem(44, ref_sigma=0.5, lo=0, hi=5)
+    H = torch.tensor(p["H"], requires_grad=True)
+    W = torch.tensor(p["W"], requires_grad=True)
+    T = opts.get("temperature", 0.0) or 1.0
+    B, L = len(p["adv"]), p["L"]
+    logp = torch.log_softmax((H @ W.T) / T, dim=1)
+    lp = logp[torch.arange(logp.shape[0]), torch.as_tensor(p["y"]).long()].reshape(B, L)
+    ratio = (lp - lp).exp() if opts.get("no_detach") else (lp - lp.detach()).exp()
+    x = torch.as_tensor(p["ref_lp"]).reshape(B, L) - lp
+    k = opts.get("kl_estimator", 0)
+    if k == 0:
+        kl = x.exp() - x - 1.0
+    elif k == 1:
+        kl = x.exp() * x - (x.exp() - 1.0)
+    else:
+        kl = lp.exp() * (x.exp() - x - 1.0)
+    m = torch.as_tensor(p["mask"]).double().reshape(B, L)
+    per_token = BETA * kl - ratio * torch.as_tensor(p["adv"]).reshape(B, 1)
+    if opts.get("aggregation"):
+        loss = ((per_token * m).sum(dim=1) / torch.clamp(m.sum(dim=1), min=1.0)).mean()
+    else:
+        loss = (per_token * m).sum() / torch.clamp(m.sum(), min=1.0)
+    loss.backward()
+    out = oracle.loss_forward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"],
+                              BETA, opts=opts)
+    assert out["loss"] == pytest.approx(loss.item(), rel=1e-13)
+    np.testing.assert_allclose(out["kl"], kl.detach().numpy().reshape(-1), rtol=1e-12, atol=1e-15)
+    dH, dW = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                  p["L"], BETA, opts=opts)
+    np.testing.assert_allclose(dH, H.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-10, atol=1e-15)
+
+
 # --------------------------------------------------------------------------- workload shapes
 def test_long_context_workload_reproduces_pages_logit_memory():
     """8 x 20480 tokens x 128256 vocab x 4 B is the pages' 78.3 GB of logits;
