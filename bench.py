@@ -192,6 +192,12 @@ def main():
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcapping (0: off)")
     ap.add_argument("--scale-multiply", type=float, default=0.0, help="logit scale multiply (0: off)")
     ap.add_argument("--scale-divide", type=float, default=0.0, help="logit scale divide (0: off)")
+    ap.add_argument("--kl-estimator", type=int, default=0, choices=(0, 1, 2),
+                    help="0 reverse k3 (default), 1 forward, 2 reverse with the factor q")
+    ap.add_argument("--no-detach", action="store_true",
+                    help="ratio without the detach (the advantage term has no gradient)")
+    ap.add_argument("--sequence-mean", action="store_true",
+                    help="per-sequence mean aggregation instead of the token mean")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a 1 GiB calibration copy and one reference pass, then exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -200,7 +206,10 @@ def main():
     xopts = {k: v for k, v in (("logit_scale_multiply", args.scale_multiply),
                                ("logit_scale_divide", args.scale_divide),
                                ("logit_softcapping", args.softcap),
-                               ("temperature", args.temperature)) if v} or None
+                               ("temperature", args.temperature),
+                               ("kl_estimator", args.kl_estimator),
+                               ("no_detach", int(args.no_detach)),
+                               ("aggregation", int(args.sequence_mean))) if v} or None
 
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload)
@@ -243,7 +252,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
         gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, workspace=ws_f,
-                             logit_opts=xopts)
+                             opts=xopts)
         torch.cuda.synchronize()
         log("[bench] traffic probe done")
         return
@@ -253,18 +262,18 @@ def main():
             ev[0].record(stream)
         adv = gp.grpo_advantages(inp["rewards"], w.G, workloads.EPS)
         ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, workspace=ws_f,
-                                   logit_opts=xopts)
+                                   opts=xopts)
         if ev is not None:
             ev[1].record(stream)
         loss, lp, kl, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref,
                                              B, L, workloads.BETA, w.chunk, workspace=ws_f,
-                                             logit_opts=xopts)
+                                             opts=xopts)
         if ev is not None:
             ev[2].record(stream)
         dW.zero_()
         gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp, lse, B, L,
                          workloads.BETA, 1.0, w.chunk, dW=dW, dH=dH, workspace=ws_b,
-                         logit_opts=xopts)
+                         opts=xopts)
         if ev is not None:
             ev[3].record(stream)
         return loss
@@ -330,7 +339,7 @@ def main():
         "config": {"workload": w.name, "tokens": N, "active_tokens": N_act, "d": d, "V": V,
                    "chunk": w.chunk, "beta": workloads.BETA,
                    "step": "advantages + reference log-probs + loss fwd + loss bwd",
-                   **({"logit_opts": xopts} if xopts else {})},
+                   **({"opts": xopts} if xopts else {})},
         "fwd_bwd_tokens_per_s": round(N / ((ms_fwd + ms_bwd) * 1e-3), 1),
         "fwd_bwd_mfma_frac": round(fb_flops / ((ms_fwd + ms_bwd) * 1e-3) / peak, 4),
         "ms": {"advantages+ref": round(ms_ref, 3), "fwd": round(ms_fwd, 3),

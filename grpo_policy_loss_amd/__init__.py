@@ -9,6 +9,11 @@ from ._lib import (  # noqa: F401
     GRPO_OP_BWD,
     GRPO_OP_FWD,
     GRPO_OP_REF,
+    AGG_SEQUENCE_MEAN,
+    AGG_TOKEN_MEAN,
+    KL_FORWARD,
+    KL_REVERSE,
+    KL_REVERSE_Q,
     GrpoError,
     grpo_advantages,
     grpo_gemm_nt,

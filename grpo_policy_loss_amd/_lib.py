@@ -23,13 +23,20 @@ _i64, _f32, _vp, _sz, _int = ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ct
 
 
 
-class LogitOpts(ctypes.Structure):
-    """grpo_logit_opts: zero fields are off (temperature 0 means 1)."""
+class Opts(ctypes.Structure):
+    """grpo_opts: zero fields give the plain loss (temperature 0 means 1)."""
     _fields_ = [("logit_scale_multiply", ctypes.c_float), ("logit_scale_divide", ctypes.c_float),
-                ("logit_softcapping", ctypes.c_float), ("temperature", ctypes.c_float)]
+                ("logit_softcapping", ctypes.c_float), ("temperature", ctypes.c_float),
+                ("kl_estimator", ctypes.c_int32), ("no_detach", ctypes.c_int32),
+                ("aggregation", ctypes.c_int32)]
 
 
-_OPTS_P = ctypes.POINTER(LogitOpts)
+# grpo_kl_estimator and grpo_aggregation
+KL_REVERSE, KL_FORWARD, KL_REVERSE_Q = 0, 1, 2
+AGG_TOKEN_MEAN, AGG_SEQUENCE_MEAN = 0, 1
+
+
+_OPTS_P = ctypes.POINTER(Opts)
 
 # name -> (restype, argtypes); mirrors include/grpo.h
 SIGNATURES = {
@@ -108,14 +115,16 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
-def _opts(logit_opts):
-    """A grpo_logit_opts pointer from a dict of its fields (None: the identity)."""
-    if logit_opts is None:
+def _opts(opts):
+    """A grpo_opts pointer from a dict of its fields (None: the plain loss)."""
+    if opts is None:
         return None
-    unknown = set(logit_opts) - {f for f, _ in LogitOpts._fields_}
+    kinds = dict(Opts._fields_)
+    unknown = set(opts) - set(kinds)
     if unknown:
-        raise ValueError(f"unknown logit options: {sorted(unknown)}")
-    return ctypes.pointer(LogitOpts(**{k: float(v) for k, v in logit_opts.items()}))
+        raise ValueError(f"unknown options: {sorted(unknown)}")
+    return ctypes.pointer(Opts(**{k: (float(v) if kinds[k] is ctypes.c_float else int(v))
+                                  for k, v in opts.items()}))
 
 
 def _want(t: torch.Tensor, dtype, name):
@@ -148,7 +157,7 @@ def grpo_advantages(rewards: torch.Tensor, group_size: int, eps: float = 1e-4, o
 
 
 def grpo_ref_logprobs(H_ref, W, y, chunk: int = 4096, out=None, workspace=None,
-                      logit_opts=None):
+                      opts=None):
     _dev(H_ref, W, y)
     _want(y, torch.int32, "y")
     N, d = H_ref.shape
@@ -159,16 +168,16 @@ def grpo_ref_logprobs(H_ref, W, y, chunk: int = 4096, out=None, workspace=None,
     out = torch.empty(N, dtype=torch.float32, device=H_ref.device) if out is None else out
     ws = _workspace(GRPO_OP_REF, N, d, V, dt, chunk, H_ref.device, workspace)
     _check("grpo_ref_logprobs_ex", lib().grpo_ref_logprobs_ex(
-        _ptr(H_ref), _ptr(W), _ptr(y), N, d, V, dt, chunk, _opts(logit_opts), _ptr(out), _ptr(ws),
+        _ptr(H_ref), _ptr(W), _ptr(y), N, d, V, dt, chunk, _opts(opts), _ptr(out), _ptr(ws),
         ws.numel(), _stream()))
     return out
 
 
 def grpo_loss_fwd(H, W, y, mask, adv, ref_lp, B: int, L: int, beta: float = 0.04,
-                  chunk: int = 4096, workspace=None, logit_opts=None):
-    """Returns (loss[1], lp[N], kl[N], lse[N]), all float32 on the GPU.  `logit_opts`:
-    dict of grpo_logit_opts fields (logit_scale_multiply, logit_scale_divide,
-    logit_softcapping, temperature), or None for the identity."""
+                  chunk: int = 4096, workspace=None, opts=None):
+    """Returns (loss[1], lp[N], kl[N], lse[N]), all float32 on the GPU.  `opts`: dict
+    of grpo_opts fields (logit_scale_multiply, logit_scale_divide, logit_softcapping,
+    temperature, kl_estimator, no_detach, aggregation), or None for the plain loss."""
     _dev(H, W, y, mask, adv, ref_lp)
     _want(y, torch.int32, "y")
     _want(mask, torch.uint8, "mask")
@@ -188,17 +197,17 @@ def grpo_loss_fwd(H, W, y, mask, adv, ref_lp, B: int, L: int, beta: float = 0.04
     ws = _workspace(GRPO_OP_FWD, N, d, V, dt, chunk, dev, workspace)
     _check("grpo_loss_fwd_ex", lib().grpo_loss_fwd_ex(
         _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(adv), _ptr(ref_lp), B, L, d, V, dt, beta,
-        chunk, _opts(logit_opts), _ptr(loss), _ptr(lp), _ptr(kl), _ptr(lse), _ptr(ws),
+        chunk, _opts(opts), _ptr(loss), _ptr(lp), _ptr(kl), _ptr(lse), _ptr(ws),
         ws.numel(), _stream()))
     return loss, lp, kl, lse
 
 
 def grpo_loss_bwd(H, W, y, mask, adv, ref_lp, lp, lse, B: int, L: int, beta: float = 0.04,
                   grad_loss: float = 1.0, chunk: int = 4096, dW=None, dH=None, workspace=None,
-                  logit_opts=None):
+                  opts=None):
     """Returns (dH[N, d] in H's dtype, dW[V, d] float32).  dW is accumulated into
-    when given (zeros are allocated otherwise).  `logit_opts` must be those of
-    the forward that produced lp and lse."""
+    when given (zeros are allocated otherwise).  `opts` must be those of the
+    forward that produced lp and lse."""
     _dev(H, W, y, mask, adv, ref_lp, lp, lse)
     N, d = H.shape
     V = W.shape[0]
@@ -213,7 +222,7 @@ def grpo_loss_bwd(H, W, y, mask, adv, ref_lp, lp, lse, B: int, L: int, beta: flo
     ws = _workspace(GRPO_OP_BWD, N, d, V, dt, chunk, dev, workspace)
     _check("grpo_loss_bwd_ex", lib().grpo_loss_bwd_ex(
         _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(adv), _ptr(ref_lp), _ptr(lp), _ptr(lse),
-        B, L, d, V, dt, beta, grad_loss, chunk, _opts(logit_opts), _ptr(dH), _ptr(dW), _ptr(ws),
+        B, L, d, V, dt, beta, grad_loss, chunk, _opts(opts), _ptr(dH), _ptr(dW), _ptr(ws),
         ws.numel(), _stream()))
     return dH, dW
 

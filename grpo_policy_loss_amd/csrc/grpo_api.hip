@@ -51,7 +51,7 @@ struct Carve {
 // one chunk, the chunk's target logits, and the per-block loss sums.
 struct FwdPlan {
   int64_t C, cpad, S, nchunks, parts_per_chunk;
-  size_t o_pm, o_ps, o_zy, o_lpart, o_cpart, total;
+  size_t o_pm, o_ps, o_zy, o_lpart, o_cpart, o_seq, total;
 };
 
 FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
@@ -67,6 +67,7 @@ FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
   p.o_zy = c.take((size_t)p.cpad * 4);
   p.o_lpart = c.take((size_t)(p.nchunks * p.parts_per_chunk) * 8);
   p.o_cpart = c.take((size_t)(p.nchunks * p.parts_per_chunk) * 4);
+  p.o_seq = c.take((size_t)N * 4);   // per-sequence counts: B <= N sequences
   p.total = c.off;
   return p;
 }
@@ -90,7 +91,8 @@ constexpr int64_t kCUs = 256;  // MI355X compute units (one GEMM workgroup each:
 
 struct BwdPlan {
   int64_t C, cpad, vpad, vs, nslabs, nchunks, nsplit;
-  size_t o_idx, o_cnt, o_wt, o_hact, o_ht, o_coef, o_lse, o_y, o_tgt, o_dz, o_dzt, o_dhacc, total;
+  size_t o_idx, o_cnt, o_wt, o_hact, o_ht, o_coef, o_lse, o_y, o_tgt, o_dz, o_dzt, o_dhacc, o_seq,
+      total;
 };
 
 BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
@@ -157,6 +159,7 @@ BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
   p.o_dz = c.take((size_t)(p.cpad * p.vs) * es);
   p.o_dzt = c.take((size_t)(p.vs * p.cpad) * es);
   p.o_dhacc = c.take((size_t)(p.nsplit * p.cpad * d) * 4);
+  p.o_seq = c.take((size_t)N * 4);   // per-sequence counts: B <= N sequences
   p.total = c.off;
   return p;
 }
@@ -194,8 +197,8 @@ int check_shape(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
     if (e_ != hipSuccess) return hip_fail(e_, #call);     \
   } while (0)
 
-// The kernels' form of a grpo_logit_opts (NULL: identity).
-int make_xform(const grpo_logit_opts* o, grpo::LogitXform* xf) {
+// The kernels' form of the logit transform of a grpo_opts (NULL: identity).
+int make_xform(const grpo_opts* o, grpo::LogitXform* xf) {
   *xf = grpo::LogitXform{1.f, 1.f, 1.f, 0};
   if (o == nullptr) return GRPO_OK;
   const float v[4] = {o->logit_scale_multiply, o->logit_scale_divide, o->logit_softcapping,
@@ -219,25 +222,43 @@ int make_xform(const grpo_logit_opts* o, grpo::LogitXform* xf) {
   return GRPO_OK;
 }
 
+// The kernels' form of the loss variant of a grpo_opts (NULL: the default loss).
+int make_variant(const grpo_opts* o, grpo::LossVariant* lv) {
+  *lv = grpo::LossVariant{0, 0, 0};
+  if (o == nullptr) return GRPO_OK;
+  if (o->kl_estimator < GRPO_KL_REVERSE || o->kl_estimator > GRPO_KL_REVERSE_Q)
+    return fail(GRPO_ERR_INVALID_ARG, "kl_estimator %d is not 0, 1 or 2", (int)o->kl_estimator);
+  if (o->no_detach != 0 && o->no_detach != 1)
+    return fail(GRPO_ERR_INVALID_ARG, "no_detach %d is not 0 or 1", (int)o->no_detach);
+  if (o->aggregation != GRPO_AGG_TOKEN_MEAN && o->aggregation != GRPO_AGG_SEQUENCE_MEAN)
+    return fail(GRPO_ERR_INVALID_ARG, "aggregation %d is not 0 or 1", (int)o->aggregation);
+  *lv = grpo::LossVariant{(int)o->kl_estimator, (int)o->no_detach,
+                          o->aggregation == GRPO_AGG_SEQUENCE_MEAN ? 1 : 0};
+  return GRPO_OK;
+}
+
 template <typename T>
 int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* mask,
              const float* adv, const float* ref_lp, int64_t N, int64_t L, int64_t d, int64_t V,
-             float beta, int64_t chunk, const grpo::LogitXform& xf, float* loss,
-             float* out_lp, float* out_kl, float* out_lse, char* ws, hipStream_t s) {
+             float beta, int64_t chunk, const grpo::LogitXform& xf, const grpo::LossVariant& lv,
+             float* loss, float* out_lp, float* out_kl, float* out_lse, char* ws, hipStream_t s) {
   const FwdPlan p = plan_fwd(N, V, chunk);
   float* pm = (float*)(ws + p.o_pm);
   float* ps = (float*)(ws + p.o_ps);
   float* zy = (float*)(ws + p.o_zy);
   double* lpart = (double*)(ws + p.o_lpart);
   int* cpart = (int*)(ws + p.o_cpart);
+  const bool seq_mean = mode == 1 && lv.seq_mean;
+  int32_t* seq_n = seq_mean ? (int32_t*)(ws + p.o_seq) : nullptr;
+  if (seq_mean) GRPO_HIP(grpo::launch_seq_counts(mask, N / L, L, seq_n, s));
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const int64_t c0 = c * p.C;
     const int n_tok = (int)std::min<int64_t>(p.C, N - c0);
     GRPO_HIP(grpo::launch_lse_partials<T>(W, H + c0 * d, y + c0, V, d, n_tok, (int)p.cpad, xf, pm,
                                           ps, zy, s));
     GRPO_HIP(grpo::launch_lse_merge(mode, pm, ps, zy, (int)p.S, (int)p.cpad, n_tok, c0, y, V,
-                                    out_lp, out_lse, out_kl, ref_lp, mask, adv, L, beta, lpart,
-                                    cpart, (int)(c * p.parts_per_chunk), s));
+                                    out_lp, out_lse, out_kl, ref_lp, mask, adv, L, beta, lv, seq_n,
+                                    lpart, cpart, (int)(c * p.parts_per_chunk), s));
   }
   if (mode == 1) {
     // every full chunk writes all of its slots; a short last chunk
@@ -246,7 +267,7 @@ int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* 
     const int64_t last_blocks =
         (std::min<int64_t>(p.C, N - last_c0) + grpo::kMergeTokens - 1) / grpo::kMergeTokens;
     const int64_t nparts = (p.nchunks - 1) * p.parts_per_chunk + last_blocks;
-    GRPO_HIP(grpo::launch_loss_final(lpart, cpart, (int)nparts, loss, s));
+    GRPO_HIP(grpo::launch_loss_final(lpart, cpart, (int)nparts, seq_mean ? N / L : 0, loss, s));
   }
   return GRPO_OK;
 }
@@ -255,7 +276,8 @@ template <typename T>
 int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, const float* adv,
              const float* ref_lp, const float* lp, const float* lse, int64_t N, int64_t L,
              int64_t d, int64_t V, float beta, float grad_loss, int64_t chunk,
-             const grpo::LogitXform& xf, T* dH, float* dW, char* ws, int dtype, hipStream_t s) {
+             const grpo::LogitXform& xf, const grpo::LossVariant& lv, T* dH, float* dW, char* ws,
+             int dtype, hipStream_t s) {
   const BwdPlan p = plan_bwd(N, d, V, dtype, chunk);
   int32_t* idx = (int32_t*)(ws + p.o_idx);
   int32_t* cnt = (int32_t*)(ws + p.o_cnt);
@@ -269,9 +291,12 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
   T* dZ = (T*)(ws + p.o_dz);
   T* dZT = (T*)(ws + p.o_dzt);
   float* dH_acc = (float*)(ws + p.o_dhacc);
+  int32_t* seq_n = lv.seq_mean ? (int32_t*)(ws + p.o_seq) : nullptr;
+  const int64_t B = N / L;
 
   GRPO_HIP(grpo::launch_zero(dH, (size_t)(N * d) * sizeof(T), s));
   GRPO_HIP(grpo::launch_active_scan(mask, N, idx, cnt, s));
+  if (seq_n != nullptr) GRPO_HIP(grpo::launch_seq_counts(mask, B, L, seq_n, s));
   GRPO_HIP(grpo::launch_transpose<T>(W, V, d, WT, p.vpad, s));
   // Chunks are planned for the worst case (every token active); chunks past
   // the device-side active count exit at once, so no host sync is needed.
@@ -279,8 +304,8 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
     const int64_t c0 = c * p.C;
     const int C = (int)p.C;
     GRPO_HIP(grpo::launch_bwd_prep<T>(H, d, idx, cnt, c0, C, (int)p.cpad, y, mask, adv, ref_lp, lp,
-                                      lse, L, beta, grad_loss, xf, H_act, coef, lse_c, y_c, tgt_c,
-                                      s));
+                                      lse, L, beta, grad_loss, xf, lv, seq_n, B, H_act, coef,
+                                      lse_c, y_c, tgt_c, s));
     GRPO_HIP(grpo::launch_transpose<T>(H_act, p.cpad, d, HT, p.cpad, s));
     for (int64_t sl = 0; sl < p.nslabs; ++sl) {
       const int64_t v0 = sl * p.vs;
@@ -340,11 +365,13 @@ int grpo_advantages(const float* rewards, int64_t num_groups, int64_t group_size
 }
 
 int grpo_ref_logprobs_ex(const void* H_ref, const void* W, const int32_t* y, int64_t N, int64_t d,
-                         int64_t V, int dtype, int64_t chunk, const grpo_logit_opts* opts,
+                         int64_t V, int dtype, int64_t chunk, const grpo_opts* opts,
                          float* ref_lp, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   grpo::LogitXform xf;
-  if (make_xform(opts, &xf) != GRPO_OK) return GRPO_ERR_INVALID_ARG;
+  grpo::LossVariant lv;
+  if (make_xform(opts, &xf) != GRPO_OK || make_variant(opts, &lv) != GRPO_OK)
+    return GRPO_ERR_INVALID_ARG;
   GRPO_CHECK_PTR(H_ref);
   GRPO_CHECK_PTR(W);
   GRPO_CHECK_PTR(y);
@@ -358,10 +385,10 @@ int grpo_ref_logprobs_ex(const void* H_ref, const void* W, const int32_t* y, int
   hipStream_t s = (hipStream_t)stream;
   if (dtype == GRPO_BF16)
     return lse_pass<__bf16>(0, (const __bf16*)H_ref, (const __bf16*)W, y, nullptr, nullptr,
-                            nullptr, N, 1, d, V, 0.f, chunk, xf, nullptr, ref_lp, nullptr,
+                            nullptr, N, 1, d, V, 0.f, chunk, xf, lv, nullptr, ref_lp, nullptr,
                             nullptr, (char*)workspace, s);
   return lse_pass<float>(0, (const float*)H_ref, (const float*)W, y, nullptr, nullptr, nullptr, N,
-                         1, d, V, 0.f, chunk, xf, nullptr, ref_lp, nullptr, nullptr,
+                         1, d, V, 0.f, chunk, xf, lv, nullptr, ref_lp, nullptr, nullptr,
                          (char*)workspace, s);
 }
 
@@ -374,12 +401,14 @@ int grpo_ref_logprobs(const void* H_ref, const void* W, const int32_t* y, int64_
 
 int grpo_loss_fwd_ex(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
                      const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
-                     int64_t V, int dtype, float beta, int64_t chunk, const grpo_logit_opts* opts,
+                     int64_t V, int dtype, float beta, int64_t chunk, const grpo_opts* opts,
                      float* loss, float* lp, float* kl, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   grpo::LogitXform xf;
-  if (make_xform(opts, &xf) != GRPO_OK) return GRPO_ERR_INVALID_ARG;
+  grpo::LossVariant lv;
+  if (make_xform(opts, &xf) != GRPO_OK || make_variant(opts, &lv) != GRPO_OK)
+    return GRPO_ERR_INVALID_ARG;
   GRPO_CHECK_PTR(H);
   GRPO_CHECK_PTR(W);
   GRPO_CHECK_PTR(y);
@@ -403,9 +432,9 @@ int grpo_loss_fwd_ex(const void* H, const void* W, const int32_t* y, const uint8
   hipStream_t s = (hipStream_t)stream;
   if (dtype == GRPO_BF16)
     return lse_pass<__bf16>(1, (const __bf16*)H, (const __bf16*)W, y, mask, adv, ref_lp, N, L, d,
-                            V, beta, chunk, xf, loss, lp, kl, lse, (char*)workspace, s);
+                            V, beta, chunk, xf, lv, loss, lp, kl, lse, (char*)workspace, s);
   return lse_pass<float>(1, (const float*)H, (const float*)W, y, mask, adv, ref_lp, N, L, d, V,
-                         beta, chunk, xf, loss, lp, kl, lse, (char*)workspace, s);
+                         beta, chunk, xf, lv, loss, lp, kl, lse, (char*)workspace, s);
 }
 
 int grpo_loss_fwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
@@ -419,11 +448,13 @@ int grpo_loss_fwd(const void* H, const void* W, const int32_t* y, const uint8_t*
 int grpo_loss_bwd_ex(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
                      const float* adv, const float* ref_lp, const float* lp, const float* lse,
                      int64_t B, int64_t L, int64_t d, int64_t V, int dtype, float beta,
-                     float grad_loss, int64_t chunk, const grpo_logit_opts* opts, void* dH,
+                     float grad_loss, int64_t chunk, const grpo_opts* opts, void* dH,
                      float* dW, void* workspace, size_t workspace_bytes, void* stream) {
   g_last_error[0] = 0;
   grpo::LogitXform xf;
-  if (make_xform(opts, &xf) != GRPO_OK) return GRPO_ERR_INVALID_ARG;
+  grpo::LossVariant lv;
+  if (make_xform(opts, &xf) != GRPO_OK || make_variant(opts, &lv) != GRPO_OK)
+    return GRPO_ERR_INVALID_ARG;
   GRPO_CHECK_PTR(H);
   GRPO_CHECK_PTR(W);
   GRPO_CHECK_PTR(y);
@@ -448,11 +479,11 @@ int grpo_loss_bwd_ex(const void* H, const void* W, const int32_t* y, const uint8
   hipStream_t s = (hipStream_t)stream;
   if (dtype == GRPO_BF16)
     return bwd_pass<__bf16>((const __bf16*)H, (const __bf16*)W, y, mask, adv, ref_lp, lp, lse, N,
-                            L, d, V, beta, grad_loss, chunk, xf, (__bf16*)dH, dW,
+                            L, d, V, beta, grad_loss, chunk, xf, lv, (__bf16*)dH, dW,
                             (char*)workspace, dtype, s);
   return bwd_pass<float>((const float*)H, (const float*)W, y, mask, adv, ref_lp, lp, lse, N, L, d,
-                         V, beta, grad_loss, chunk, xf, (float*)dH, dW, (char*)workspace, dtype,
-                         s);
+                         V, beta, grad_loss, chunk, xf, lv, (float*)dH, dW, (char*)workspace,
+                         dtype, s);
 }
 
 int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,

@@ -9,6 +9,7 @@
 //   k_lse_merge: fixed-order merge of the per-tile pairs into lse and lp; in
 //     loss mode also kl and the masked per-block loss sums.
 //   k_loss_final: fixed-order sum of the block sums -> loss.
+//   (k_seq_counts: unmasked tokens per sequence, for the per-sequence mean.)
 // Backward (per chunk of ACTIVE tokens, per vocabulary slab):
 //   k_dz: the same tile recomputed; the epilogue forms
 //     dZ = c_t (onehot(y_t) - exp(z - lse_t)) in registers and stores it in
@@ -239,6 +240,26 @@ __global__ void __launch_bounds__(kThreads, 1)
   }
 }
 
+// ---------------------------------------------------------------- per-token KL
+// The KL estimators of the blog's ablation (GRPO maths), x = ref_lp - lp:
+//   reverse k3:      e^x - x - 1                      (the default)
+//   forward:         r ln r - (r - 1), r = e^x, written x (e^x - 1) - (e^x - 1 - x):
+//                    both terms are O(x^2), so nothing cancels near x = 0
+//   reverse with q:  e^lp (e^x - x - 1), q the policy's probability of the token
+__device__ __forceinline__ float kl_value(int kl, float x, float lp) {
+  const float em = expm1f(x);
+  const float k3 = em - x;
+  if (kl == 1) return fmaf(x, em, -k3);
+  if (kl == 2) return expf(lp) * k3;
+  return k3;
+}
+// d kl / d lp (dx / dlp = -1): -(e^x - 1), -x e^x and -x e^lp.
+__device__ __forceinline__ float kl_slope(int kl, float x, float lp) {
+  if (kl == 1) return -x * expf(x);
+  if (kl == 2) return -x * expf(lp);
+  return -expm1f(x);
+}
+
 // ---------------------------------------------------------------- forward merge
 // 256 threads = 32 tokens x 8 splits of the vocabulary-tile partials.  Split q
 // folds partials q, q + 8, ... of its token in order; the 8 split results are
@@ -252,8 +273,8 @@ __global__ void __launch_bounds__(256)
                 const int32_t* __restrict__ y, int64_t V, float* __restrict__ out_lp,
                 float* __restrict__ out_lse, float* __restrict__ out_kl,
                 const float* __restrict__ ref_lp, const uint8_t* __restrict__ mask,
-                const float* __restrict__ adv, int64_t L, float beta, double* loss_part,
-                int* cnt_part, int part0) {
+                const float* __restrict__ adv, int64_t L, float beta, LossVariant lv,
+                const int32_t* __restrict__ seq_n, double* loss_part, int* cnt_part, int part0) {
   __shared__ float sm_m[kMergeSplit][kMergeTok], sm_s[kMergeSplit][kMergeTok];
   const int tt = threadIdx.x % kMergeTok, q = threadIdx.x / kMergeTok;
   const int t = blockIdx.x * kMergeTok + tt;
@@ -289,10 +310,12 @@ __global__ void __launch_bounds__(256)
     if (mode == 1) {
       out_lse[tg] = lse;
       const float x = ref_lp[tg] - lp;
-      const float kl = expm1f(x) - x;
+      const float kl = kl_value(lv.kl, x, lp);
       out_kl[tg] = kl;
       if (mask[tg] != 0) {
+        // the ratio exp(lp - sg(lp)) (or exp(lp - lp)) is exactly 1 in value
         ml = (double)(-(adv[tg / L] - beta * kl));
+        if (seq_n != nullptr) ml /= (double)(seq_n[tg / L] > 0 ? seq_n[tg / L] : 1);
         cnt = 1;
       }
     }
@@ -310,7 +333,7 @@ __global__ void __launch_bounds__(256)
 
 __global__ void __launch_bounds__(256)
     k_loss_final(const double* __restrict__ loss_part, const int* __restrict__ cnt_part,
-                 int nparts, float* __restrict__ loss) {
+                 int nparts, int64_t seq_B, float* __restrict__ loss) {
   double s = 0.0;
   long long c = 0;
   for (int i = threadIdx.x; i < nparts; i += 256) {
@@ -329,7 +352,22 @@ __global__ void __launch_bounds__(256)
     }
     __syncthreads();
   }
-  if (threadIdx.x == 0) loss[0] = (float)(ss[0] / (double)(sc[0] > 0 ? sc[0] : 1));
+  // token mean: over the unmasked tokens; per-sequence mean: the block sums
+  // already hold each sequence's mean share, so divide by the sequence count
+  const double den = seq_B > 0 ? (double)seq_B : (double)(sc[0] > 0 ? sc[0] : 1);
+  if (threadIdx.x == 0) loss[0] = (float)(ss[0] / den);
+}
+
+__global__ void __launch_bounds__(256)
+    k_seq_counts(const uint8_t* __restrict__ mask, int64_t L, int32_t* __restrict__ n) {
+  const int64_t b = blockIdx.x;
+  int c = 0;
+  for (int64_t j = threadIdx.x; j < L; j += 256) c += mask[b * L + j] != 0;
+  c = wave_sum(c);
+  __shared__ int sc[4];
+  if ((threadIdx.x & 63) == 0) sc[threadIdx.x >> 6] = c;
+  __syncthreads();
+  if (threadIdx.x == 0) n[b] = sc[0] + sc[1] + sc[2] + sc[3];
 }
 
 // ---------------------------------------------------------------- backward helpers
@@ -386,7 +424,8 @@ __global__ void __launch_bounds__(256)
                const int32_t* __restrict__ y, const float* __restrict__ adv,
                const float* __restrict__ ref_lp, const float* __restrict__ lp,
                const float* __restrict__ lse, int64_t L, float beta, float grad_loss,
-               LogitXform xf, T* __restrict__ H_act, float* __restrict__ coef,
+               LogitXform xf, LossVariant lv, const int32_t* __restrict__ seq_n, int64_t B,
+               T* __restrict__ H_act, float* __restrict__ coef,
                float* __restrict__ lse_c, int32_t* __restrict__ y_c, float* __restrict__ tgt_c) {
   const int cnt = count[0];
   if (c0 >= cnt) return;
@@ -399,9 +438,16 @@ __global__ void __launch_bounds__(256)
   for (int v = threadIdx.x; v < nvec; v += 256) dst[v] = valid ? src[v] : int4{0, 0, 0, 0};
   if (threadIdx.x == 0) {
     if (valid) {
+      // c_t = d loss / d lp_t = w_t (-[detached] A + beta d kl / d lp), w_t the
+      // aggregation weight of an unmasked token
       const float x = ref_lp[t] - lp[t];
-      const float scale = grad_loss / (float)(cnt > 0 ? cnt : 1);
-      const float c = scale * (-adv[t / L] - beta * expm1f(x));
+      const int64_t b = t / L;
+      const float scale =
+          seq_n != nullptr
+              ? grad_loss / ((float)B * (float)(seq_n[b] > 0 ? seq_n[b] : 1))
+              : grad_loss / (float)(cnt > 0 ? cnt : 1);
+      const float a_term = lv.no_detach ? 0.f : -adv[b];
+      const float c = scale * (a_term + beta * kl_slope(lv.kl, x, lp[t]));
       coef[j] = c;
       lse_c[j] = lse[t];
       y_c[j] = y[t];
@@ -759,18 +805,26 @@ hipError_t launch_lse_merge(int mode, const float* part_m, const float* part_s, 
                             int S, int cpad, int n_tok, int64_t c0, const int32_t* y, int64_t V,
                             float* out_lp, float* out_lse, float* out_kl, const float* ref_lp,
                             const uint8_t* mask, const float* adv, int64_t L, float beta,
-                            double* loss_part, int* cnt_part, int part0, hipStream_t s) {
+                            const LossVariant& lv, const int32_t* seq_n, double* loss_part,
+                            int* cnt_part, int part0, hipStream_t s) {
   ScopedKernelTimer timer_(KK_LSE_MERGE, s);
   hipLaunchKernelGGL(k_lse_merge, dim3(cdiv(n_tok, kMergeTok)), dim3(256), 0, s, mode, part_m, part_s,
                      zy, S, cpad, n_tok, c0, y, V, out_lp, out_lse, out_kl, ref_lp, mask, adv, L,
-                     beta, loss_part, cnt_part, part0);
+                     beta, lv, seq_n, loss_part, cnt_part, part0);
   return hipGetLastError();
 }
 
-hipError_t launch_loss_final(const double* loss_part, const int* cnt_part, int nparts, float* loss,
-                             hipStream_t s) {
+hipError_t launch_loss_final(const double* loss_part, const int* cnt_part, int nparts,
+                             int64_t seq_B, float* loss, hipStream_t s) {
   ScopedKernelTimer timer_(KK_LOSS_FINAL, s);
-  hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, s, loss_part, cnt_part, nparts, loss);
+  hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, s, loss_part, cnt_part, nparts, seq_B,
+                     loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_seq_counts(const uint8_t* mask, int64_t B, int64_t L, int32_t* n, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_SEQ_COUNTS, s);
+  hipLaunchKernelGGL(k_seq_counts, dim3((unsigned)B), dim3(256), 0, s, mask, L, n);
   return hipGetLastError();
 }
 
@@ -795,12 +849,14 @@ hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int3
                            int64_t c0, int C, int cpad, const int32_t* y, const uint8_t* mask,
                            const float* adv, const float* ref_lp, const float* lp,
                            const float* lse, int64_t L, float beta, float grad_loss,
-                           const LogitXform& xf, T* H_act, float* coef, float* lse_c,
-                           int32_t* y_c, float* tgt_c, hipStream_t s) {
+                           const LogitXform& xf, const LossVariant& lv, const int32_t* seq_n,
+                           int64_t B, T* H_act, float* coef, float* lse_c, int32_t* y_c,
+                           float* tgt_c, hipStream_t s) {
   ScopedKernelTimer timer_(KK_BWD_PREP, s);
   (void)mask;
   hipLaunchKernelGGL(k_bwd_prep<T>, dim3(cpad), dim3(256), 0, s, H, d, idx, count, c0, C, y, adv,
-                     ref_lp, lp, lse, L, beta, grad_loss, xf, H_act, coef, lse_c, y_c, tgt_c);
+                     ref_lp, lp, lse, L, beta, grad_loss, xf, lv, seq_n, B, H_act, coef, lse_c,
+                     y_c, tgt_c);
   return hipGetLastError();
 }
 
@@ -889,7 +945,8 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
   template hipError_t launch_bwd_prep<T>(const T*, int64_t, const int32_t*, const int32_t*,       \
                                          int64_t, int, int, const int32_t*, const uint8_t*,        \
                                          const float*, const float*, const float*, const float*,  \
-                                         int64_t, float, float, const LogitXform&, T*, float*,     \
+                                         int64_t, float, float, const LogitXform&,                \
+                                         const LossVariant&, const int32_t*, int64_t, T*, float*,  \
                                          float*, int32_t*, float*, hipStream_t);                  \
   template hipError_t launch_dz<T>(const T*, const T*, int64_t, int64_t, int64_t, int, int,       \
                                    const int32_t*, int64_t, int, int, const LogitXform&,         \

@@ -20,6 +20,13 @@ struct LogitXform {
   int softcap;
 };
 
+// The loss variant: KL estimator, detach and aggregation.
+struct LossVariant {
+  int kl;         // 0 reverse k3, 1 forward r log r - (r - 1), 2 reverse k3 times q = exp(lp)
+  int no_detach;  // 1: exp(lp - lp) in place of exp(lp - stopgrad(lp)): no advantage gradient
+  int seq_mean;   // 1: per-sequence masked mean, then the mean over sequences
+};
+
 // Logical tile grid of one GEMM-shaped launch.
 struct Grid2 {
   int tm;  // tiles along M (A rows)
@@ -38,14 +45,20 @@ hipError_t launch_lse_partials(const T* W, const T* H, const int32_t* y, int64_t
 
 // Merge the partials of one chunk (tokens c0 .. c0 + n_tok - 1).
 // mode 0: reference log-probs -> out_lp.  mode 1: loss forward.
+// seq_n (per-sequence unmasked counts) is null for the token mean.
 hipError_t launch_lse_merge(int mode, const float* part_m, const float* part_s, const float* zy,
                             int S, int cpad, int n_tok, int64_t c0, const int32_t* y, int64_t V,
                             float* out_lp, float* out_lse, float* out_kl, const float* ref_lp,
                             const uint8_t* mask, const float* adv, int64_t L, float beta,
-                            double* loss_part, int* cnt_part, int part0, hipStream_t s);
+                            const LossVariant& lv, const int32_t* seq_n, double* loss_part,
+                            int* cnt_part, int part0, hipStream_t s);
 
-hipError_t launch_loss_final(const double* loss_part, const int* cnt_part, int nparts, float* loss,
-                             hipStream_t s);
+// seq_B: the number of sequences for the per-sequence mean, 0 for the token mean.
+hipError_t launch_loss_final(const double* loss_part, const int* cnt_part, int nparts,
+                             int64_t seq_B, float* loss, hipStream_t s);
+
+// n[b] = unmasked tokens of sequence b (B sequences of L tokens).
+hipError_t launch_seq_counts(const uint8_t* mask, int64_t B, int64_t L, int32_t* n, hipStream_t s);
 
 // Backward helpers.
 hipError_t launch_active_scan(const uint8_t* mask, int64_t N, int32_t* idx, int32_t* count,
@@ -60,8 +73,9 @@ hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int3
                            int64_t c0, int C, int cpad, const int32_t* y, const uint8_t* mask,
                            const float* adv, const float* ref_lp, const float* lp,
                            const float* lse, int64_t L, float beta, float grad_loss,
-                           const LogitXform& xf, T* H_act, float* coef, float* lse_c,
-                           int32_t* y_c, float* tgt_c, hipStream_t s);
+                           const LogitXform& xf, const LossVariant& lv, const int32_t* seq_n,
+                           int64_t B, T* H_act, float* coef, float* lse_c, int32_t* y_c,
+                           float* tgt_c, hipStream_t s);
 
 template <typename T>
 hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,

@@ -24,6 +24,7 @@ enum KernelKind {
   KK_DH_SCATTER,
   KK_ZERO,
   KK_GEMM_NT,
+  KK_SEQ_COUNTS,
   KK_COUNT
 };
 

@@ -74,7 +74,8 @@ typedef enum { GRPO_OP_REF = 0, GRPO_OP_FWD = 1, GRPO_OP_BWD = 2 } grpo_op;
  * arguments.  It never scales with N*V: the forward keeps only per-token
  * split partials of one chunk, the backward one bounded [chunk x V_s] slab
  * of dZ (and its transpose), a transposed copy of W and one chunk of hidden
- * states.  Each dZ slab is at most 2 GiB (V_s <= V), or at most
+ * states, plus 4 bytes per token for the per-sequence counts that the
+ * per-sequence mean aggregation uses.  Each dZ slab is at most 2 GiB (V_s <= V), or at most
  * GRPO_SLAB_MIB MiB when that environment variable is set; a smaller budget
  * trades speed for memory.  The variable is read at every call: query the
  * workspace and run the backward under the same setting.
@@ -144,44 +145,72 @@ int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t*
                   size_t workspace_bytes, void* stream);
 
 /*
- * Optional logit transform (Unsloth docs, "Flattened sequence length
- * chunking": the chunked log-softmax takes logit_scale_multiply,
- * logit_scale_divide, logit_softcapping and temperature, and supports
- * softcapping and temperature).  The pages give no formulas; applied here in
- * the order of those arguments to every logit z = h . w before the
- * log-softmax:
+ * Options of the _ex calls.  A zero-initialised struct (or a NULL pointer)
+ * gives exactly the plain calls.
+ *
+ * Logit transform (Unsloth docs, "Flattened sequence length chunking": the
+ * chunked log-softmax takes logit_scale_multiply, logit_scale_divide,
+ * logit_softcapping and temperature, and supports softcapping and
+ * temperature).  The pages give no formulas; applied here in the order of
+ * those arguments to every logit z = h . w before the log-softmax:
  *   z * multiply, / divide, cap * tanh(z / cap), / temperature.
- * A zero multiply, divide or cap is "off"; a zero temperature means 1, so a
- * zero-initialised struct is the identity.  Every field must be finite and
- * >= 0 (GRPO_ERR_INVALID_ARG otherwise).  lp, lse, kl and the gradients are
- * those of the transformed logits.
+ * A zero multiply, divide or cap is "off"; a zero temperature means 1.  Every
+ * float field must be finite and >= 0 (GRPO_ERR_INVALID_ARG otherwise).  lp,
+ * lse, kl and the gradients are those of the transformed logits.
+ *
+ * Loss variants (Unsloth blog, GRPO maths: the four-run ablation trains the
+ * reference loss, the loss with the detach removed, a "full" reverse KL with
+ * the extra factor Q and a forward KL; the formulas are lost, so these are
+ * the plainest readings), with x = ref_lp - lp and r = exp(x):
+ *   kl_estimator  GRPO_KL_REVERSE    kl = r - x - 1 (k3; the default)
+ *                 GRPO_KL_FORWARD    kl = r x - (r - 1), the estimator of
+ *                                    KL(ref || policy) from policy samples
+ *                 GRPO_KL_REVERSE_Q  kl = exp(lp) (r - x - 1), the factor
+ *                                    differentiated with the term
+ *   no_detach     1: the ratio is exp(lp - lp) -- still 1 in value, but the
+ *                 advantage term then carries no gradient
+ *   aggregation   GRPO_AGG_TOKEN_MEAN     sum_t m_t l_t / max(sum m, 1)
+ *                 GRPO_AGG_SEQUENCE_MEAN  (1/B) sum_b sum_j m l / max(n_b, 1),
+ *                                         n_b = sum_j m_{b,j}; an empty
+ *                                         sequence adds 0 and counts in B
+ * The backward coefficient follows: c_t = g w_t (-[no_detach = 0] A +
+ * beta dkl/dlp) with w_t the aggregation weight and dkl/dlp = 1 - r, -x r,
+ * -x exp(lp) for the three estimators.  Values outside these sets:
+ * GRPO_ERR_INVALID_ARG.  grpo_ref_logprobs_ex uses only the logit transform.
  */
-typedef struct grpo_logit_opts {
+typedef enum { GRPO_KL_REVERSE = 0, GRPO_KL_FORWARD = 1, GRPO_KL_REVERSE_Q = 2 } grpo_kl_estimator;
+typedef enum { GRPO_AGG_TOKEN_MEAN = 0, GRPO_AGG_SEQUENCE_MEAN = 1 } grpo_aggregation;
+
+typedef struct grpo_opts {
   float logit_scale_multiply;
   float logit_scale_divide;
   float logit_softcapping;
   float temperature;
-} grpo_logit_opts;
+  int32_t kl_estimator;   /* grpo_kl_estimator */
+  int32_t no_detach;      /* 0 or 1 */
+  int32_t aggregation;    /* grpo_aggregation */
+} grpo_opts;
 
 /*
- * grpo_ref_logprobs, grpo_loss_fwd and grpo_loss_bwd with a logit transform
- * (`opts` may be NULL: the identity, exactly the calls above).  Arguments and
- * outputs are otherwise those of the plain calls; grpo_loss_bwd_ex must get
- * the opts of the grpo_loss_fwd_ex call that produced lp and lse, and the
- * reference log-probs are taken with the same opts.
+ * grpo_ref_logprobs, grpo_loss_fwd and grpo_loss_bwd with options (`opts`
+ * may be NULL: exactly the calls above).  Arguments and outputs are otherwise
+ * those of the plain calls; grpo_loss_bwd_ex must get the opts of the
+ * grpo_loss_fwd_ex call that produced lp and lse, and the reference
+ * log-probs are taken with the same logit transform.  kl holds the selected
+ * estimator's per-token value.
  */
 int grpo_ref_logprobs_ex(const void* H_ref, const void* W, const int32_t* y, int64_t N, int64_t d,
-                         int64_t V, int dtype, int64_t chunk, const grpo_logit_opts* opts,
+                         int64_t V, int dtype, int64_t chunk, const grpo_opts* opts,
                          float* ref_lp, void* workspace, size_t workspace_bytes, void* stream);
 int grpo_loss_fwd_ex(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
                      const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
-                     int64_t V, int dtype, float beta, int64_t chunk, const grpo_logit_opts* opts,
+                     int64_t V, int dtype, float beta, int64_t chunk, const grpo_opts* opts,
                      float* loss, float* lp, float* kl, float* lse, void* workspace,
                      size_t workspace_bytes, void* stream);
 int grpo_loss_bwd_ex(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
                      const float* adv, const float* ref_lp, const float* lp, const float* lse,
                      int64_t B, int64_t L, int64_t d, int64_t V, int dtype, float beta,
-                     float grad_loss, int64_t chunk, const grpo_logit_opts* opts, void* dH,
+                     float grad_loss, int64_t chunk, const grpo_opts* opts, void* dH,
                      float* dW, void* workspace, size_t workspace_bytes, void* stream);
 
 /*

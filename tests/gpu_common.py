@@ -22,11 +22,11 @@ def gpu_chain(inp, w, beta=BETA, chunk=None, grad_loss=1.0, ref_from=None, opts=
     chunk = w.chunk if chunk is None else chunk
     adv = gp.grpo_advantages(inp["rewards"], w.G, EPS)
     H_ref = inp["H_ref"] if ref_from is None else ref_from
-    ref = gp.grpo_ref_logprobs(H_ref, inp["W"], inp["y"], chunk, logit_opts=opts)
+    ref = gp.grpo_ref_logprobs(H_ref, inp["W"], inp["y"], chunk, opts=opts)
     loss, lp, kl, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref,
-                                         w.B, w.L, beta, chunk, logit_opts=opts)
+                                         w.B, w.L, beta, chunk, opts=opts)
     dH, dW = gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp, lse,
-                              w.B, w.L, beta, grad_loss, chunk, logit_opts=opts)
+                              w.B, w.L, beta, grad_loss, chunk, opts=opts)
     torch.cuda.synchronize()
     return dict(adv=adv, ref=ref, loss=loss, lp=lp, kl=kl, lse=lse, dH=dH, dW=dW)
 

@@ -56,13 +56,14 @@ def test_workspace_bytes_bounded_and_independent_of_N_times_V(op):
     if op == 2:
         # dZ and its transpose hold at most one chunk's float32 logits; the rest is
         # W transposed (bf16), per-chunk hidden-state copies and dH split partials
-        # (at most 8 float32 copies of a chunk), and the 4 B/token index list
+        # (at most 8 float32 copies of a chunk), the 4 B/token index list and the
+        # 4 B/token room for per-sequence counts
         Vp = -(-V // 256) * 256
         assert ws <= chunk * Vp * 4 + d * Vp * 2 + 2 * chunk * d * 2 + 8 * chunk * d * 4 \
-            + 4 * N + (1 << 20)
-        # grows with N only through the active-index list (4 B per token)
+            + 8 * N + (1 << 20)
+        # grows with N only through the index list and the counts (8 B per token)
         ws2 = L.grpo_workspace_bytes(op, 2 * N, d, V, 1, chunk)
-        assert ws2 - ws <= 4 * N + 512
+        assert ws2 - ws <= 8 * N + 1024
 
 
 def test_slab_budget_variable_bounds_the_backward_workspace(monkeypatch):
@@ -145,14 +146,33 @@ def test_binding_refuses_cpu_tensors():
         gp.grpo_ref_logprobs(H, torch.zeros(16, 8), torch.zeros(4, dtype=torch.int32))
 
 
-@pytest.mark.parametrize("field,value", [("temperature", -1.0), ("logit_softcapping", -30.0),
-                                         ("logit_scale_multiply", float("nan")),
-                                         ("logit_scale_divide", float("inf"))])
-def test_logit_opts_rejected_before_any_launch(field, value):
+@pytest.mark.parametrize("field,value,msg", [
+    ("temperature", -1.0, b"logit opts"), ("logit_softcapping", -30.0, b"logit opts"),
+    ("logit_scale_multiply", float("nan"), b"logit opts"),
+    ("logit_scale_divide", float("inf"), b"logit opts"),
+    ("kl_estimator", 3, b"kl_estimator"), ("kl_estimator", -1, b"kl_estimator"),
+    ("no_detach", 2, b"no_detach"), ("aggregation", 2, b"aggregation")])
+def test_opts_rejected_before_any_launch(field, value, msg):
     import ctypes
-    opts = _lib.LogitOpts(**{field: value})
+    opts = _lib.Opts(**{field: value})
     one = ctypes.c_void_p(16)        # never dereferenced: the options are checked first
     st = L.grpo_ref_logprobs_ex(one, one, one, 8, 16, 32, 0, 8, ctypes.pointer(opts), one, one,
                                 1 << 20, None)
     assert st == -1
-    assert b"logit opts" in L.grpo_last_error()
+    assert msg in L.grpo_last_error()
+    st = L.grpo_loss_fwd_ex(one, one, one, one, one, one, 2, 4, 16, 32, 0, 0.04, 8,
+                            ctypes.pointer(opts), one, one, one, one, one, 1 << 20, None)
+    assert st == -1
+    st = L.grpo_loss_bwd_ex(one, one, one, one, one, one, one, one, 2, 4, 16, 32, 0, 0.04, 1.0, 8,
+                            ctypes.pointer(opts), one, one, one, 1 << 20, None)
+    assert st == -1
+
+
+def test_opts_struct_matches_the_header():
+    """Field order and types of grpo_opts as the header declares them."""
+    import ctypes
+    hdr = open(os.path.join(os.path.dirname(__file__), "..", "include", "grpo.h")).read()
+    body = hdr[hdr.index("typedef struct grpo_opts {"):hdr.index("} grpo_opts;")]
+    decl = [ln.split(";")[0].split() for ln in body.splitlines()[1:] if ";" in ln]
+    want = [(name, {"float": ctypes.c_float, "int32_t": ctypes.c_int32}[ty]) for ty, name in decl]
+    assert list(_lib.Opts._fields_) == want

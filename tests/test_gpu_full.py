@@ -154,22 +154,26 @@ def test_full_size_exact_dW_with_sparse_mask(name):
     assert torch.all(dH[others] == 0)
 
 
-def test_full_size_logit_transform_sampled_parity():
+@pytest.mark.parametrize("opts", [
+    {"logit_softcapping": 30.0, "temperature": 0.9},
+    {"logit_softcapping": 30.0, "temperature": 0.9, "kl_estimator": 1, "aggregation": 1}],
+    ids=["transform", "transform+forward-kl+sequence-mean"])
+def test_full_size_logit_transform_sampled_parity(opts):
     """Qwen2.5-1.5B shape with softcap 30 and temperature 0.9 (the launch
-    configuration the benchmark times, plus the transform): lp/ref/lse of sampled
-    tokens and dH of sampled active rows against the oracle's transformed logits."""
+    configuration the benchmark times, plus the transform), also with the forward
+    KL and the per-sequence mean: lp/ref/lse/kl of sampled tokens and dH of
+    sampled active rows against the oracle's transformed logits."""
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     w = workloads.BY_NAME["qwen2.5-1.5b-bf16"]
-    opts = {"logit_softcapping": 30.0, "temperature": 0.9}
     print(f"[full-xform] {w.name} {opts}", flush=True)
     inp = workloads.generate(w, seed=13, device="cuda")
     adv = gp.grpo_advantages(inp["rewards"], w.G, EPS)
-    ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, logit_opts=opts)
+    ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, opts=opts)
     loss, lp, kl, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref,
-                                         w.B, w.L, BETA, w.chunk, logit_opts=opts)
+                                         w.B, w.L, BETA, w.chunk, opts=opts)
     dH, dW = gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp, lse,
-                              w.B, w.L, BETA, 1.0, w.chunk, logit_opts=opts)
+                              w.B, w.L, BETA, 1.0, w.chunk, opts=opts)
     torch.cuda.synchronize()
     y = inp["y"].cpu().numpy().astype(np.int64)
     mask = inp["mask"].cpu().numpy()
@@ -187,6 +191,9 @@ def test_full_size_logit_transform_sampled_parity():
     assert np.abs(g_lp - o_lp).max() <= 2e-4
     assert np.abs(g_ref - o_ref).max() <= 2e-4
     assert np.abs(g_lse - o_lse).max() <= 2e-4
+    # the GPU's kl against the estimator evaluated in float64 on its own lp and ref
+    g_kl = to64(kl)[rows]
+    np.testing.assert_allclose(g_kl, oracle.token_kl(g_ref, g_lp, opts), rtol=1e-4, atol=1e-6)
     act = np.nonzero(mask)[0]
     drows = np.array(sorted(set(rng.choice(act, size=256, replace=False).tolist())))
     H64 = np.zeros((w.N, w.d))

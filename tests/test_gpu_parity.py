@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from tests.gpu_common import BETA, cosine, gpu_chain, max_abs_rel, oracle_chain, to64
 
@@ -255,3 +256,81 @@ def test_logit_transform_keeps_kl_exactly_zero_for_policy_equal_reference(dtype)
     g = gpu_chain(inp, w, ref_from=inp["H"], opts=XFORMS[2])
     assert torch.equal(g["ref"], g["lp"])
     assert torch.all(g["kl"] == 0)
+
+
+VARIANTS = [
+    {"kl_estimator": 1},
+    {"kl_estimator": 2},
+    {"no_detach": 1},
+    {"aggregation": 1},
+    {"kl_estimator": 1, "no_detach": 1, "aggregation": 1, "temperature": 0.9},
+]
+VARIANT_IDS = ["forward-kl", "reverse-kl-q", "no-detach", "sequence-mean", "combined"]
+
+
+@pytest.mark.parametrize("opts", VARIANTS, ids=VARIANT_IDS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chain_with_loss_variant_matches_oracle(dtype, opts):
+    """The ablation's estimator, detach and aggregation variants through the
+    whole chain (ragged tiles, 3 chunks); sequence 2 has an empty mask, so the
+    per-sequence mean counts it in B with a zero contribution.  The reference
+    hidden states are drawn independently, as in the pure-KL test above: x =
+    ref_lp - lp is then O(1), so the KL terms (all of the no-detach gradient)
+    are well conditioned in fp32 and every estimator is exercised away from 0."""
+    _need_gpu()
+    w = small(dtype)
+    inp = inputs(w, seed=10)
+    inp["mask"][2 * w.L:3 * w.L] = 0
+    ref_h = workloads.draw_hidden(w.N, w.d, inp["H"].dtype, 98, "cuda")
+    g = gpu_chain(inp, w, ref_from=ref_h, opts=opts)
+    o = oracle_chain(inp, w, ref_from=ref_h, opts=opts)
+    print(f"[variant] {dtype} {opts} loss gpu {g['loss'].item():.7g} oracle {o['loss']:.7g}",
+          flush=True)
+    # the kernel's estimator arithmetic (fp32) against the same estimator in float64
+    # on the GPU's own lp and ref; lp itself is checked against the oracle below
+    np.testing.assert_allclose(to64(g["kl"]), oracle.token_kl(to64(g["ref"]), to64(g["lp"]), opts),
+                               rtol=1e-5, atol=1e-7)
+    if dtype == "f32":
+        np.testing.assert_allclose(to64(g["lp"]), o["lp"], rtol=1e-5, atol=1e-6)
+        np.testing.assert_allclose(to64(g["kl"]), o["kl"], rtol=1e-3, atol=1e-6)
+        assert abs(g["loss"].item() - o["loss"]) <= 1e-5 * abs(o["loss"])
+        for k in ("dH", "dW"):
+            assert max_abs_rel(to64(g[k]), o[k]) <= 1e-4, k
+    else:
+        assert np.abs(to64(g["lp"]) - o["lp"]).max() <= 1e-4
+        assert abs(g["loss"].item() - o["loss"]) <= 2e-3 * abs(o["loss"])
+        for k in ("dH", "dW"):
+            assert cosine(to64(g[k]), o[k]) >= 0.999, k
+            assert max_abs_rel(to64(g[k]), o[k]) <= 1e-2, k
+    m = inp["mask"].cpu().numpy().astype(bool)
+    assert np.all(to64(g["dH"])[~m] == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_no_detach_gradient_is_bitwise_the_zero_advantage_gradient(dtype):
+    """Without the detach the advantage term has no gradient: the backward equals,
+    bit for bit, the detached backward with every advantage zero."""
+    _need_gpu()
+    w = small(dtype)
+    inp = inputs(w, seed=11)
+    g = gpu_chain(inp, w, opts={"no_detach": 1})
+    adv0 = torch.zeros_like(g["adv"])
+    dH0, dW0 = gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv0, g["ref"],
+                                g["lp"], g["lse"], w.B, w.L, BETA, 1.0, w.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dH"], dH0)
+    assert torch.equal(g["dW"], dW0)
+
+
+@pytest.mark.parametrize("kl_estimator", [0, 1, 2])
+def test_sequence_mean_policy_equals_reference_gives_zero_loss(kl_estimator):
+    """With kl = 0 the per-sequence mean is -mean_b(A_b), zero up to the rounding
+    of the group advantages; the token mean of the same inputs is not."""
+    _need_gpu()
+    w = small("f32")
+    inp = inputs(w, seed=12)
+    g = gpu_chain(inp, w, ref_from=inp["H"], opts={"kl_estimator": kl_estimator, "aggregation": 1})
+    t = gpu_chain(inp, w, ref_from=inp["H"], opts={"kl_estimator": kl_estimator})
+    assert torch.all(g["kl"] == 0)
+    assert abs(g["loss"].item()) <= 1e-6
+    assert abs(t["loss"].item()) > 1e-3
