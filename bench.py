@@ -192,6 +192,9 @@ def main():
     ap.add_argument("--softcap", type=float, default=0.0, help="logit softcapping (0: off)")
     ap.add_argument("--scale-multiply", type=float, default=0.0, help="logit scale multiply (0: off)")
     ap.add_argument("--scale-divide", type=float, default=0.0, help="logit scale divide (0: off)")
+    ap.add_argument("--chunk", type=int, default=-1,
+                    help="tokens per chunk: -1 the workload's own, 0 automatic (grpo_auto_chunk "
+                         "with half of the free HBM as the budget)")
     ap.add_argument("--kl-estimator", type=int, default=0, choices=(0, 1, 2),
                     help="0 reverse k3 (default), 1 forward, 2 reverse with the factor q")
     ap.add_argument("--no-detach", action="store_true",
@@ -228,6 +231,11 @@ def main():
     w = workloads.BY_NAME[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.chunk > 0:
+        w = w.scaled(chunk=args.chunk)
+    elif args.chunk == 0:
+        w = w.scaled(chunk=gp.auto_chunk(w.B, w.L, w.d, w.V,
+                                         gp.GRPO_BF16 if w.dtype == "bf16" else gp.GRPO_F32))
     log(f"[bench] workload {w.name}: N={w.N} d={w.d} V={w.V} {w.dtype} chunk={w.chunk}")
     t0 = time.time()
     inp = workloads.generate(w, seed=args.seed, device=dev)

@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     KL_REVERSE,
     KL_REVERSE_Q,
     GrpoError,
+    auto_chunk,
     grpo_advantages,
     grpo_gemm_nt,
     grpo_loss_bwd,

@@ -54,6 +54,7 @@ SIGNATURES = {
     "grpo_loss_bwd_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                 _int, _f32, _f32, _i64, _OPTS_P, _vp, _vp, _vp, _sz, _vp]),
     "grpo_gemm_nt": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
+    "grpo_auto_chunk": (_i64, [_i64, _i64, _i64, _i64, _int, _sz]),
     "grpo_timing_begin": (_int, []),
     "grpo_timing_end": (_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_int),
                                ctypes.POINTER(ctypes.c_double), _int]),
@@ -136,6 +137,17 @@ def grpo_workspace_bytes(op: int, N: int, d: int, V: int, dtype: int, chunk: int
     return int(lib().grpo_workspace_bytes(op, N, d, V, dtype, chunk))
 
 
+def auto_chunk(B: int, L: int, d: int, V: int, dtype: int, budget_bytes=None) -> int:
+    """grpo_auto_chunk: tokens per chunk for B sequences of L tokens.  budget_bytes
+    None: half of the current device's free HBM (torch.cuda.mem_get_info)."""
+    if budget_bytes is None:
+        budget_bytes = torch.cuda.mem_get_info()[0] // 2
+    c = int(lib().grpo_auto_chunk(B, L, d, V, dtype, int(budget_bytes)))
+    if c <= 0:
+        _check("grpo_auto_chunk", -1)
+    return c
+
+
 def _workspace(op, N, d, V, dt, chunk, device, workspace):
     need = grpo_workspace_bytes(op, N, d, V, dt, chunk)
     if need == 0:
@@ -166,6 +178,8 @@ def grpo_ref_logprobs(H_ref, W, y, chunk: int = 4096, out=None, workspace=None,
     if W.dtype != H_ref.dtype or W.shape[1] != d or y.numel() != N:
         raise ValueError("shape/dtype mismatch between H_ref, W, y")
     out = torch.empty(N, dtype=torch.float32, device=H_ref.device) if out is None else out
+    if chunk == 0:
+        chunk = auto_chunk(1, N, d, V, dt)
     ws = _workspace(GRPO_OP_REF, N, d, V, dt, chunk, H_ref.device, workspace)
     _check("grpo_ref_logprobs_ex", lib().grpo_ref_logprobs_ex(
         _ptr(H_ref), _ptr(W), _ptr(y), N, d, V, dt, chunk, _opts(opts), _ptr(out), _ptr(ws),
@@ -177,7 +191,8 @@ def grpo_loss_fwd(H, W, y, mask, adv, ref_lp, B: int, L: int, beta: float = 0.04
                   chunk: int = 4096, workspace=None, opts=None):
     """Returns (loss[1], lp[N], kl[N], lse[N]), all float32 on the GPU.  `opts`: dict
     of grpo_opts fields (logit_scale_multiply, logit_scale_divide, logit_softcapping,
-    temperature, kl_estimator, no_detach, aggregation), or None for the plain loss."""
+    temperature, kl_estimator, no_detach, aggregation), or None for the plain loss.
+    chunk 0 (here and in the other calls): auto_chunk with half the free HBM."""
     _dev(H, W, y, mask, adv, ref_lp)
     _want(y, torch.int32, "y")
     _want(mask, torch.uint8, "mask")
@@ -194,6 +209,8 @@ def grpo_loss_fwd(H, W, y, mask, adv, ref_lp, B: int, L: int, beta: float = 0.04
     lp = torch.empty(N, dtype=torch.float32, device=dev)
     kl = torch.empty(N, dtype=torch.float32, device=dev)
     lse = torch.empty(N, dtype=torch.float32, device=dev)
+    if chunk == 0:
+        chunk = auto_chunk(B, L, d, V, dt)
     ws = _workspace(GRPO_OP_FWD, N, d, V, dt, chunk, dev, workspace)
     _check("grpo_loss_fwd_ex", lib().grpo_loss_fwd_ex(
         _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(adv), _ptr(ref_lp), B, L, d, V, dt, beta,
@@ -219,6 +236,8 @@ def grpo_loss_bwd(H, W, y, mask, adv, ref_lp, lp, lse, B: int, L: int, beta: flo
     dW = torch.zeros(V, d, dtype=torch.float32, device=dev) if dW is None else dW
     _dev(dH, dW)
     _want(dW, torch.float32, "dW")
+    if chunk == 0:
+        chunk = auto_chunk(B, L, d, V, dt)
     ws = _workspace(GRPO_OP_BWD, N, d, V, dt, chunk, dev, workspace)
     _check("grpo_loss_bwd_ex", lib().grpo_loss_bwd_ex(
         _ptr(H), _ptr(W), _ptr(y), _ptr(mask), _ptr(adv), _ptr(ref_lp), _ptr(lp), _ptr(lse),

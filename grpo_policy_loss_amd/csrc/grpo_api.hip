@@ -350,6 +350,26 @@ size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, 
   }
 }
 
+int64_t grpo_auto_chunk(int64_t B, int64_t L, int64_t d, int64_t V, int dtype,
+                        size_t budget_bytes) {
+  g_last_error[0] = 0;
+  if (B <= 0 || L <= 0) {
+    fail(GRPO_ERR_INVALID_ARG, "B and L must be positive");
+    return 0;
+  }
+  if (B > INT32_MAX / L) {
+    fail(GRPO_ERR_UNSUPPORTED, "B*L exceeds int32");
+    return 0;
+  }
+  const int64_t N = B * L;
+  if (check_shape(N, d, V, dtype, 1) != GRPO_OK) return 0;
+  constexpr int64_t kStep = 256, kCap = 8192;  // best measured chunk at d = 1536 and 4096
+  const int64_t top = std::min<int64_t>(kCap, round_up(N, kStep));
+  for (int64_t c = top; c > kStep; c -= kStep)
+    if (plan_fwd(N, V, c).total + plan_bwd(N, d, V, dtype, c).total <= budget_bytes) return c;
+  return kStep;
+}
+
 int grpo_advantages(const float* rewards, int64_t num_groups, int64_t group_size, float eps,
                     float* adv, void* stream) {
   g_last_error[0] = 0;

@@ -83,6 +83,26 @@ typedef enum { GRPO_OP_REF = 0, GRPO_OP_FWD = 1, GRPO_OP_BWD = 2 } grpo_op;
 size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk);
 
 /*
+ * Automatic chunk size (Unsloth docs, "Flattened sequence length chunking"
+ * and "Configuring the parameters": left unset, the chunk multiplier and the
+ * hidden-state mini-batch are tuned from the free VRAM and the context
+ * length; the multiplier defaults to max(4, context_length // 4096)).  There
+ * the chunk's float32 logits are materialised, so memory sets the chunk; here
+ * the forward never holds chunk x V logits and the backward's dZ slab has its
+ * own bound, so the chunk is chosen for speed within the memory given.
+ * Returns the largest multiple of 256 tokens that is at most 8192 (the best
+ * measured size at d = 1536 and d = 4096; at 16384 the backward slows down)
+ * and at most N = B * L rounded up to 256, for which
+ *   grpo_workspace_bytes(GRPO_OP_FWD, ...) + grpo_workspace_bytes(GRPO_OP_BWD, ...)
+ * is at most budget_bytes; 256 if no candidate fits.  Pure host arithmetic:
+ * no device call, deterministic for given arguments (and GRPO_SLAB_MIB).
+ * The caller passes its own budget (for example part of the free HBM) and
+ * then uses the result for the workspace query and every call.  Returns 0
+ * for invalid arguments.
+ */
+int64_t grpo_auto_chunk(int64_t B, int64_t L, int64_t d, int64_t V, int dtype, size_t budget_bytes);
+
+/*
  * Group-relative advantages (aibit.im "Mastering GRPO", section "From RLHF
  * and PPO to the efficiency of GRPO": several completions per prompt are
  * scored and the advantage is derived from the group's rewards).

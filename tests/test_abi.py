@@ -176,3 +176,30 @@ def test_opts_struct_matches_the_header():
     decl = [ln.split(";")[0].split() for ln in body.splitlines()[1:] if ";" in ln]
     want = [(name, {"float": ctypes.c_float, "int32_t": ctypes.c_int32}[ty]) for ty, name in decl]
     assert list(_lib.Opts._fields_) == want
+
+
+def test_auto_chunk_is_the_largest_fitting_multiple_of_256():
+    """grpo_auto_chunk (pure host arithmetic): a multiple of 256 up to 8192 and up to N,
+    whose forward + backward workspace fits the budget, and the largest such."""
+    def ws(N, d, V, c):
+        return L.grpo_workspace_bytes(1, N, d, V, 1, c) + L.grpo_workspace_bytes(2, N, d, V, 1, c)
+    for (B, Lq, d, V) in [(32, 1024, 1536, 151936), (8, 4096, 4096, 128256),
+                          (8, 20480, 4096, 128256), (4, 16384, 2880, 201088)]:
+        N = B * Lq
+        # unlimited memory: the speed cap
+        assert L.grpo_auto_chunk(B, Lq, d, V, 1, 1 << 62) == 8192
+        for budget in (ws(N, d, V, 256) + 1, ws(N, d, V, 3000), ws(N, d, V, 8192) - 1, 12 << 30):
+            c = L.grpo_auto_chunk(B, Lq, d, V, 1, budget)
+            assert c % 256 == 0 and 256 <= c <= 8192
+            assert ws(N, d, V, c) <= budget
+            if c < 8192:
+                assert ws(N, d, V, c + 256) > budget
+    # nothing fits: the smallest candidate
+    assert L.grpo_auto_chunk(32, 1024, 1536, 151936, 1, 1024) == 256
+    # short inputs: capped at N rounded up to 256
+    assert L.grpo_auto_chunk(3, 100, 64, 500, 0, 1 << 62) == 512
+    assert L.grpo_auto_chunk(1, 7, 16, 3, 0, 1 << 62) == 256
+    # invalid arguments
+    assert L.grpo_auto_chunk(0, 8, 16, 32, 1, 1 << 30) == 0
+    assert L.grpo_auto_chunk(2, 8, 16, 32, 7, 1 << 30) == 0
+    assert L.grpo_auto_chunk(2, 8, 0, 32, 1, 1 << 30) == 0

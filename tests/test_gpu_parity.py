@@ -334,3 +334,22 @@ def test_sequence_mean_policy_equals_reference_gives_zero_loss(kl_estimator):
     assert torch.all(g["kl"] == 0)
     assert abs(g["loss"].item()) <= 1e-6
     assert abs(t["loss"].item()) > 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_chain_with_automatic_chunk_matches_fixed_chunk_bitwise(dtype):
+    """chunk = 0 resolves through grpo_auto_chunk (half the free HBM); lp and lse
+    do not depend on the chunk, so they equal a fixed-chunk run bit for bit, and
+    the whole chain still matches the oracle."""
+    _need_gpu()
+    w = small(dtype)
+    inp = inputs(w, seed=13)
+    a = gpu_chain(inp, w, chunk=0)
+    f = gpu_chain(inp, w, chunk=256)
+    assert torch.equal(a["lp"], f["lp"]) and torch.equal(a["lse"], f["lse"])
+    assert torch.equal(a["ref"], f["ref"])
+    o = oracle_chain(inp, w)
+    tol = 1e-5 if dtype == "f32" else 2e-3
+    assert abs(a["loss"].item() - o["loss"]) <= tol * abs(o["loss"])
+    for k in ("dH", "dW"):
+        assert cosine(to64(a[k]), o[k]) >= 0.999, k
