@@ -165,6 +165,89 @@ def token_logprobs(H, W, y, rows=None, block=ROW_BLOCK, opts=None):
 
 
 # ---------------------------------------------------------------------------
+# fp8 (e4m3) inputs
+# ---------------------------------------------------------------------------
+# [P-docs, introduction and "Getting started"]: FP8 RL training is offered
+# (an FP8 GRPO notebook), and [P-blog, Unsloth efficient GRPO algorithm] warns
+# that a naive linear cross-entropy under float8 mixed precision breaks loss
+# scaling.  No recipe is given.  Reading: the LM-head GEMM takes float8 e4m3
+# operands (the OCP "fn" variant: 4 exponent bits with bias 7, 3 mantissa
+# bits, no infinities, S.1111.111 is NaN, largest finite 448) with float32
+# accumulation and float32 log-sum-exp; each hidden-state row (token) has its
+# own scale and the head one scale; scales are powers of two, so dequantised
+# values are exact and only the e4m3 rounding decides a code.
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes):
+    """Value of each e4m3fn code, float64 (NaN for the two NaN codes)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & ((c & 7) == 7), np.nan, mag)
+    return sign * mag
+
+
+def _fp8_positive_table():
+    """The 127 finite non-negative e4m3fn values, ascending, and their codes."""
+    codes = np.arange(0, 127, dtype=np.uint8)
+    return fp8_e4m3_decode(codes), codes
+
+
+def fp8_e4m3_encode(x):
+    """Nearest e4m3fn code to each float64 x with |x| <= 448, ties to the even
+    code (even mantissa); the sign bit follows the sign of x, zero included."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~np.isfinite(x)) or np.any(np.abs(x) > FP8_MAX):
+        raise ValueError("fp8_e4m3_encode needs finite |x| <= 448")
+    vals, codes = _fp8_positive_table()
+    a = np.abs(x).reshape(-1)
+    hi = np.clip(np.searchsorted(vals, a, side="left"), 0, len(vals) - 1)
+    lo = np.clip(hi - 1, 0, len(vals) - 1)
+    dlo, dhi = a - vals[lo], vals[hi] - a
+    pick = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(codes[lo] % 2 == 0, lo, hi)))
+    out = codes[pick].astype(np.uint8)
+    neg = np.signbit(x.reshape(-1))
+    out = np.where(neg, out | 0x80, out).astype(np.uint8)
+    return out.reshape(x.shape)
+
+
+def fp8_scale_exponent(absmax):
+    """Smallest integer e with absmax <= 448 * 2**e (0 for absmax = 0)."""
+    a = float(absmax)
+    if a == 0.0:
+        return 0
+    f, k = np.frexp(a)           # a = f 2^k, 0.5 <= f < 1; 448 = 0.875 2^9
+    return int(k - 9) if f <= 0.875 else int(k - 8)
+
+
+def fp8_quantize(X, per_row=True):
+    """(codes uint8 [rows, cols], scales float64 [rows] or [1]): X ~ codes * scale.
+
+    The scale of a row (or of the whole tensor) is 2**e with e from
+    fp8_scale_exponent of its largest |x|; codes = e4m3 rounding of x / 2**e,
+    an exact division, so |x / scale| <= 448 and only the rounding is inexact.
+    """
+    X = _f64(X)
+    if per_row:
+        e = np.array([fp8_scale_exponent(np.abs(r).max() if r.size else 0.0) for r in X])
+    else:
+        e = np.array([fp8_scale_exponent(np.abs(X).max() if X.size else 0.0)])
+    sc = np.exp2(e.astype(np.float64))
+    codes = fp8_e4m3_encode(X / (sc[:, None] if per_row else sc[0]))
+    return codes, sc
+
+
+def fp8_dequantize(codes, scales):
+    """codes * scale per row (scales of length rows) or for the tensor (length 1)."""
+    v = fp8_e4m3_decode(codes)
+    s = _f64(scales)
+    return v * (s[:, None] if s.size > 1 or v.shape[0] == 1 else s[0])
+
+
+# ---------------------------------------------------------------------------
 # per-token KL and loss
 # ---------------------------------------------------------------------------
 def reverse_kl_k3(ref_lp, lp):

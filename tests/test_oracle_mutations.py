@@ -115,6 +115,19 @@ MUTATIONS = [
     ("sequence mean: empty completions left out of B",
      [("return (mb / (mb.shape[0] * np.maximum(n, 1.0))).reshape(-1)",
        "return (mb / (max(int((n > 0).sum()), 1) * np.maximum(n, 1.0))).reshape(-1)")]),
+    ("fp8 decode: exponent bias 8",
+     [("(1.0 + m / 8.0) * np.exp2(e - 7.0)", "(1.0 + m / 8.0) * np.exp2(e - 8.0)")]),
+    ("fp8 decode: subnormals on the normal scale",
+     [("np.where(e == 0, m / 8.0 * 2.0 ** -6,", "np.where(e == 0, m / 8.0 * 2.0 ** -7,")]),
+    ("fp8 encode: ties away from zero",
+     [("np.where(codes[lo] % 2 == 0, lo, hi)", "hi")]),
+    ("fp8 encode: sign dropped",
+     [("out = np.where(neg, out | 0x80, out).astype(np.uint8)", "out = out.astype(np.uint8)")]),
+    ("fp8 scale: one binade too large",
+     [("return int(k - 9) if f <= 0.875 else int(k - 8)", "return int(k - 8)")]),
+    ("fp8 quantize: tensor scale from the first row",
+     [("e = np.array([fp8_scale_exponent(np.abs(X).max() if X.size else 0.0)])",
+       "e = np.array([fp8_scale_exponent(np.abs(X[0]).max() if X.size else 0.0)])")]),
     ("backward: recomputed logits against the transposed head",
      [("Z = Hs @ Wf.T", "Z = Hs @ Wf[::-1].T")]),
 ]

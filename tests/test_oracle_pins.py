@@ -521,6 +521,67 @@ def test_variant_gradients_match_torch_autograd(opts):
     np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-10, atol=1e-15)
 
 
+# --------------------------------------------------------------------------- fp8 (e4m3) inputs
+def test_fp8_decode_matches_torch_float8_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.tensor(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = oracle.fp8_e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    ok = ~np.isnan(want)
+    assert np.array_equal(got[ok], want[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(want[ok]))
+    assert np.nanmax(got) == oracle.FP8_MAX
+
+
+def test_fp8_encode_matches_torch_rounding():
+    rng = np.random.default_rng(50)
+    x = np.concatenate([rng.uniform(-448, 448, 20000), rng.uniform(-0.05, 0.05, 20000),
+                        rng.uniform(-0.004, 0.004, 5000), [448.0, -448.0, 0.0, -0.0]])
+    want = torch.tensor(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.fp8_e4m3_encode(x), want)
+
+
+def test_fp8_encode_roundtrip_and_hand_worked_ties():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    assert np.array_equal(oracle.fp8_e4m3_encode(oracle.fp8_e4m3_decode(codes)), codes)
+    for x, c in _table("fp8_e4m3_ties.txt"):
+        assert int(oracle.fp8_e4m3_encode(np.array([float(x)]))[0]) == int(c, 16), x
+    with pytest.raises(ValueError):
+        oracle.fp8_e4m3_encode(np.array([448.5]))
+
+
+def test_fp8_scale_exponent_is_the_smallest_that_fits():
+    rng = np.random.default_rng(51)
+    for a in np.concatenate([rng.lognormal(0, 6, 2000), [1e-30, 3.0, 448.0, 449.0]]):
+        e = oracle.fp8_scale_exponent(a)
+        assert a <= 448.0 * 2.0 ** e and a > 448.0 * 2.0 ** (e - 1), a
+    for k in range(-20, 21):
+        assert oracle.fp8_scale_exponent(448.0 * 2.0 ** k) == k
+        assert oracle.fp8_scale_exponent(448.0 * 2.0 ** k * (1 + 2.0 ** -20)) == k + 1
+    assert oracle.fp8_scale_exponent(0.0) == 0
+
+
+def test_fp8_quantize_rows_bound_and_error():
+    rng = np.random.default_rng(52)
+    X = rng.standard_normal((40, 300)) * np.exp2(rng.integers(-12, 12, (40, 1)))
+    X[3] = 0.0
+    codes, sc = oracle.fp8_quantize(X, per_row=True)
+    assert np.all(np.log2(sc) == np.round(np.log2(sc)))          # powers of two
+    assert sc[3] == 1.0 and np.all(codes[3] == 0)
+    D = oracle.fp8_dequantize(codes, sc)
+    # 3 mantissa bits: half an ulp is 2^-4 of the value (normal) or 2^-10 of the scale
+    err = np.abs(D - X)
+    assert np.all(err <= np.maximum(2.0 ** -4 * np.abs(X), 2.0 ** -10 * sc[:, None]) * (1 + 1e-12))
+    # each row's largest magnitude lands in the top binade (>= 224 after scaling)
+    big = np.abs(X).max(axis=1)
+    assert np.all((big / sc >= 224.0) | (big == 0))
+    # one scale for the tensor
+    codes_t, sct = oracle.fp8_quantize(X, per_row=False)
+    assert sct.shape == (1,) and sct[0] == sc.max()
+    np.testing.assert_array_equal(oracle.fp8_dequantize(codes_t, sct),
+                                  oracle.fp8_e4m3_decode(codes_t) * sct[0])
+
+
 # --------------------------------------------------------------------------- workload shapes
 def test_long_context_workload_reproduces_pages_logit_memory():
     """8 x 20480 tokens x 128256 vocab x 4 B is the pages' 78.3 GB of logits;
