@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "flattened tokens/s GRPO loss fwd+bwd (1 GPU) + % bf16 MFMA peak + peak HBM"
-PEAK_FLOPS = {"bf16": 2.5e15, "f32": 157.3e12}   # MI355X dense MFMA peaks
+PEAK_FLOPS = {"bf16": 2.5e15, "f32": 157.3e12, "fp8": 5.0e15}   # MI355X dense MFMA peaks
 DEFAULT_WORKLOAD = "qwen2.5-1.5b-bf16"
 
 
@@ -195,6 +195,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=-1,
                     help="tokens per chunk: -1 the workload's own, 0 automatic (grpo_auto_chunk "
                          "with half of the free HBM as the budget)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="fp8 e4m3 forward (H, H_ref per-token scales, W one scale; quantised "
+                         "inside the timed step) with the bf16 backward on exact copies")
     ap.add_argument("--kl-estimator", type=int, default=0, choices=(0, 1, 2),
                     help="0 reverse k3 (default), 1 forward, 2 reverse with the factor q")
     ap.add_argument("--no-detach", action="store_true",
@@ -244,6 +247,10 @@ def main():
     N, d, V, B, L = w.N, w.d, w.V, w.B, w.L
     N_act = int(inp["mask"].sum().item())
     dt = gp.GRPO_BF16 if w.dtype == "bf16" else gp.GRPO_F32
+    if args.fp8:
+        if w.dtype != "bf16":
+            raise SystemExit("--fp8 quantises a bf16 workload")
+        dt = gp.GRPO_FP8_E4M3
     ws_f = torch.empty(gp.grpo_workspace_bytes(gp.GRPO_OP_FWD, N, d, V, dt, w.chunk),
                        dtype=torch.uint8, device=dev)
     ws_b = torch.empty(gp.grpo_workspace_bytes(gp.GRPO_OP_BWD, N, d, V, dt, w.chunk),
@@ -265,7 +272,32 @@ def main():
         log("[bench] traffic probe done")
         return
 
+    def step_fp8(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        adv = gp.grpo_advantages(inp["rewards"], w.G, workloads.EPS)
+        Wq = gp.quantize_fp8(inp["W"], per_row=False)
+        Rq = gp.quantize_fp8(inp["H_ref"], per_row=True)
+        ref = gp.grpo_ref_logprobs_fp8(Rq, Wq, inp["y"], w.chunk, workspace=ws_f, opts=xopts)
+        if ev is not None:
+            ev[1].record(stream)
+        Hq = gp.quantize_fp8(inp["H"], per_row=True)
+        loss, lp, kl, lse = gp.grpo_loss_fwd_fp8(Hq, Wq, inp["y"], inp["mask"], adv, ref, B, L,
+                                                 workloads.BETA, w.chunk, workspace=ws_f,
+                                                 opts=xopts)
+        if ev is not None:
+            ev[2].record(stream)
+        dW.zero_()
+        gp.grpo_loss_bwd_fp8(Hq, Wq, inp["y"], inp["mask"], adv, ref, lp, lse, B, L,
+                             workloads.BETA, 1.0, w.chunk, dW=dW, dH=dH, workspace=ws_b,
+                             opts=xopts)
+        if ev is not None:
+            ev[3].record(stream)
+        return loss
+
     def step(ev=None):
+        if args.fp8:
+            return step_fp8(ev)
         if ev is not None:
             ev[0].record(stream)
         adv = gp.grpo_advantages(inp["rewards"], w.G, workloads.EPS)
@@ -317,8 +349,11 @@ def main():
     dom_flops = alg_flops(dom_name, d, V, N, N_act)
     roof = None
     if dom_flops is not None:
+        # with --fp8 the lse pass runs fp8 MFMAs; the backward stays bf16
+        if args.fp8 and dom_name == "lse_partials":
+            peak = PEAK_FLOPS["fp8"]
         achieved = dom_flops * args.steps / (dom_ms * 1e-3) / 1e12
-        tb = read_traffic(dom_name, w.name)
+        tb = None if args.fp8 else read_traffic(dom_name, w.name)
         roof = {"kernel": dom_name, "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(achieved * 1e12 / peak, 4),
                 "traffic": tb, "traffic_unit": "bytes per launch (HBM, counters)",
@@ -342,14 +377,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "fp8-e4m3 fwd / bf16 bwd" if args.fp8 else w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "tokens": N, "active_tokens": N_act, "d": d, "V": V,
                    "chunk": w.chunk, "beta": workloads.BETA,
                    "step": "advantages + reference log-probs + loss fwd + loss bwd",
-                   **({"opts": xopts} if xopts else {})},
+                   **({"opts": xopts} if xopts else {}), **({"fp8": True} if args.fp8 else {})},
         "fwd_bwd_tokens_per_s": round(N / ((ms_fwd + ms_bwd) * 1e-3), 1),
-        "fwd_bwd_mfma_frac": round(fb_flops / ((ms_fwd + ms_bwd) * 1e-3) / peak, 4),
+        "fwd_bwd_mfma_frac": round(fb_flops / ((ms_fwd + ms_bwd) * 1e-3) / PEAK_FLOPS[w.dtype], 4),
         "ms": {"advantages+ref": round(ms_ref, 3), "fwd": round(ms_fwd, 3),
                "bwd": round(ms_bwd, 3)},
         "peak_hbm_gb": round(peak_bytes / 1e9, 3),

@@ -6,6 +6,13 @@ ABI declared in include/grpo.h; this package is its thin Python binding.
 from ._lib import (  # noqa: F401
     GRPO_BF16,
     GRPO_F32,
+    GRPO_FP8_E4M3,
+    Fp8,
+    dequantize_fp8,
+    quantize_fp8,
+    grpo_ref_logprobs_fp8,
+    grpo_loss_fwd_fp8,
+    grpo_loss_bwd_fp8,
     GRPO_OP_BWD,
     GRPO_OP_FWD,
     GRPO_OP_REF,

@@ -14,7 +14,7 @@ import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrpo.so")
 
-GRPO_F32, GRPO_BF16 = 0, 1
+GRPO_F32, GRPO_BF16, GRPO_FP8_E4M3 = 0, 1, 2
 GRPO_OP_REF, GRPO_OP_FWD, GRPO_OP_BWD = 0, 1, 2
 STATUS = {0: "GRPO_OK", -1: "GRPO_ERR_INVALID_ARG", -2: "GRPO_ERR_WORKSPACE",
           -3: "GRPO_ERR_UNSUPPORTED", -4: "GRPO_ERR_HIP"}
@@ -55,6 +55,15 @@ SIGNATURES = {
                                 _int, _f32, _f32, _i64, _OPTS_P, _vp, _vp, _vp, _sz, _vp]),
     "grpo_gemm_nt": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
     "grpo_auto_chunk": (_i64, [_i64, _i64, _i64, _i64, _int, _sz]),
+    "grpo_quantize_fp8_workspace_bytes": (_sz, []),
+    "grpo_quantize_fp8": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _sz, _vp]),
+    "grpo_dequantize_fp8": (_int, [_vp, _vp, _i64, _i64, _int, _vp, _vp]),
+    "grpo_ref_logprobs_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _OPTS_P,
+                                     _vp, _vp, _sz, _vp]),
+    "grpo_loss_fwd_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                 _f32, _i64, _OPTS_P, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "grpo_loss_bwd_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                 _i64, _i64, _f32, _f32, _i64, _OPTS_P, _vp, _vp, _vp, _sz, _vp]),
     "grpo_timing_begin": (_int, []),
     "grpo_timing_end": (_int, [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(_int),
                                ctypes.POINTER(ctypes.c_double), _int]),
@@ -270,3 +279,108 @@ def grpo_gemm_nt(A, B):
     C = torch.empty(M, N, dtype=torch.float32, device=A.device)
     _check("grpo_gemm_nt", lib().grpo_gemm_nt(_ptr(A), _ptr(B), M, N, K, _dt(A), _ptr(C), _stream()))
     return C
+
+
+# ---------------------------------------------------------------- fp8 e4m3 path
+class Fp8:
+    """Float8 e4m3 codes (uint8, [rows, cols]) and their power-of-two scales
+    (float32 on the GPU: one per row, or one for the tensor)."""
+
+    def __init__(self, codes, scales, per_row):
+        self.codes, self.scales, self.per_row = codes, scales, per_row
+
+    @property
+    def shape(self):
+        return self.codes.shape
+
+
+def quantize_fp8(X, per_row=True) -> Fp8:
+    """grpo_quantize_fp8 of a float32 or bfloat16 matrix on the GPU."""
+    _dev(X)
+    rows, cols = X.shape
+    codes = torch.empty(rows, cols, dtype=torch.uint8, device=X.device)
+    scales = torch.empty(rows if per_row else 1, dtype=torch.float32, device=X.device)
+    ws = None if per_row else torch.empty(int(lib().grpo_quantize_fp8_workspace_bytes()),
+                                          dtype=torch.uint8, device=X.device)
+    _check("grpo_quantize_fp8", lib().grpo_quantize_fp8(
+        _ptr(X), _dt(X), rows, cols, int(per_row), _ptr(codes), _ptr(scales), _ptr(ws),
+        0 if ws is None else ws.numel(), _stream()))
+    return Fp8(codes, scales, per_row)
+
+
+def dequantize_fp8(q: Fp8):
+    """grpo_dequantize_fp8: the exact bfloat16 values of q."""
+    rows, cols = q.codes.shape
+    out = torch.empty(rows, cols, dtype=torch.bfloat16, device=q.codes.device)
+    _check("grpo_dequantize_fp8", lib().grpo_dequantize_fp8(
+        _ptr(q.codes), _ptr(q.scales), rows, cols, int(q.per_row), _ptr(out), _stream()))
+    return out
+
+
+def _fp8_args(H: Fp8, W: Fp8):
+    if not H.per_row or W.per_row or W.scales.numel() != 1:
+        raise ValueError("fp8 loss takes per-row H scales and one W scale")
+    if H.codes.shape[1] != W.codes.shape[1]:
+        raise ValueError("H and W hidden sizes differ")
+    _dev(H.codes, H.scales, W.codes, W.scales)
+    return H.codes.shape[0], H.codes.shape[1], W.codes.shape[0]
+
+
+def grpo_ref_logprobs_fp8(H_ref: Fp8, W: Fp8, y, chunk: int = 4096, out=None, workspace=None,
+                          opts=None):
+    N, d, V = _fp8_args(H_ref, W)
+    _dev(y)
+    _want(y, torch.int32, "y")
+    out = torch.empty(N, dtype=torch.float32, device=y.device) if out is None else out
+    if chunk == 0:
+        chunk = auto_chunk(1, N, d, V, GRPO_FP8_E4M3)
+    ws = _workspace(GRPO_OP_REF, N, d, V, GRPO_FP8_E4M3, chunk, y.device, workspace)
+    _check("grpo_ref_logprobs_fp8", lib().grpo_ref_logprobs_fp8(
+        _ptr(H_ref.codes), _ptr(H_ref.scales), _ptr(W.codes), _ptr(W.scales), _ptr(y), N, d, V,
+        chunk, _opts(opts), _ptr(out), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def grpo_loss_fwd_fp8(H: Fp8, W: Fp8, y, mask, adv, ref_lp, B: int, L: int, beta: float = 0.04,
+                      chunk: int = 4096, workspace=None, opts=None):
+    """grpo_loss_fwd on fp8 operands: (loss[1], lp[N], kl[N], lse[N])."""
+    N, d, V = _fp8_args(H, W)
+    _dev(y, mask, adv, ref_lp)
+    _want(y, torch.int32, "y")
+    _want(mask, torch.uint8, "mask")
+    if N != B * L:
+        raise ValueError("N != B * L")
+    dev = y.device
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    lp, kl, lse = (torch.empty(N, dtype=torch.float32, device=dev) for _ in range(3))
+    if chunk == 0:
+        chunk = auto_chunk(B, L, d, V, GRPO_FP8_E4M3)
+    ws = _workspace(GRPO_OP_FWD, N, d, V, GRPO_FP8_E4M3, chunk, dev, workspace)
+    _check("grpo_loss_fwd_fp8", lib().grpo_loss_fwd_fp8(
+        _ptr(H.codes), _ptr(H.scales), _ptr(W.codes), _ptr(W.scales), _ptr(y), _ptr(mask),
+        _ptr(adv), _ptr(ref_lp), B, L, d, V, beta, chunk, _opts(opts), _ptr(loss), _ptr(lp),
+        _ptr(kl), _ptr(lse), _ptr(ws), ws.numel(), _stream()))
+    return loss, lp, kl, lse
+
+
+def grpo_loss_bwd_fp8(H: Fp8, W: Fp8, y, mask, adv, ref_lp, lp, lse, B: int, L: int,
+                      beta: float = 0.04, grad_loss: float = 1.0, chunk: int = 4096, dW=None,
+                      dH=None, workspace=None, opts=None):
+    """Backward of grpo_loss_fwd_fp8 with respect to the dequantised H and W:
+    (dH[N, d] bfloat16, dW[V, d] float32, accumulated into when given)."""
+    N, d, V = _fp8_args(H, W)
+    _dev(y, mask, adv, ref_lp, lp, lse)
+    if N != B * L:
+        raise ValueError("N != B * L")
+    dev = y.device
+    dH = torch.empty(N, d, dtype=torch.bfloat16, device=dev) if dH is None else dH
+    dW = torch.zeros(V, d, dtype=torch.float32, device=dev) if dW is None else dW
+    _want(dW, torch.float32, "dW")
+    if chunk == 0:
+        chunk = auto_chunk(B, L, d, V, GRPO_FP8_E4M3)
+    ws = _workspace(GRPO_OP_BWD, N, d, V, GRPO_FP8_E4M3, chunk, dev, workspace)
+    _check("grpo_loss_bwd_fp8", lib().grpo_loss_bwd_fp8(
+        _ptr(H.codes), _ptr(H.scales), _ptr(W.codes), _ptr(W.scales), _ptr(y), _ptr(mask),
+        _ptr(adv), _ptr(ref_lp), _ptr(lp), _ptr(lse), B, L, d, V, beta, grad_loss, chunk,
+        _opts(opts), _ptr(dH), _ptr(dW), _ptr(ws), ws.numel(), _stream()))
+    return dH, dW

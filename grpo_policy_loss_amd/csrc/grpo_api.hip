@@ -35,7 +35,7 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-inline size_t esize(int dtype) { return dtype == GRPO_F32 ? 4 : 2; }
+inline size_t esize(int dtype) { return dtype == GRPO_F32 ? 4 : dtype == GRPO_FP8_E4M3 ? 1 : 2; }
 
 // Bump allocator over the caller's workspace.
 struct Carve {
@@ -166,12 +166,13 @@ BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
 
 // Shape checks shared by all calls.  Operands are addressed per 256-row tile
 // with 32-bit offsets, so one tile's rows must span < 2 GiB.
-int check_shape(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
+// fp8_ok: GRPO_FP8_E4M3 is accepted (the fp8 calls and the size queries)
+int check_shape(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk, bool fp8_ok = false) {
   if (N <= 0 || d <= 0 || V <= 0 || chunk <= 0)
     return fail(GRPO_ERR_INVALID_ARG, "sizes must be positive (N=%lld d=%lld V=%lld chunk=%lld)",
                 (long long)N, (long long)d, (long long)V, (long long)chunk);
-  if (dtype != GRPO_F32 && dtype != GRPO_BF16)
-    return fail(GRPO_ERR_INVALID_ARG, "dtype %d is neither GRPO_F32 nor GRPO_BF16", dtype);
+  if (dtype != GRPO_F32 && dtype != GRPO_BF16 && !(fp8_ok && dtype == GRPO_FP8_E4M3))
+    return fail(GRPO_ERR_INVALID_ARG, "dtype %d is not accepted here", dtype);
   const int64_t vec = 16 / (int64_t)esize(dtype);
   if (d % vec != 0)
     return fail(GRPO_ERR_UNSUPPORTED, "d=%lld must be a multiple of %lld for this dtype",
@@ -241,7 +242,8 @@ template <typename T>
 int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* mask,
              const float* adv, const float* ref_lp, int64_t N, int64_t L, int64_t d, int64_t V,
              float beta, int64_t chunk, const grpo::LogitXform& xf, const grpo::LossVariant& lv,
-             float* loss, float* out_lp, float* out_kl, float* out_lse, char* ws, hipStream_t s) {
+             float* loss, float* out_lp, float* out_kl, float* out_lse, char* ws, hipStream_t s,
+             const float* w_scale = nullptr, const float* h_scale = nullptr) {
   const FwdPlan p = plan_fwd(N, V, chunk);
   float* pm = (float*)(ws + p.o_pm);
   float* ps = (float*)(ws + p.o_ps);
@@ -254,8 +256,9 @@ int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* 
   for (int64_t c = 0; c < p.nchunks; ++c) {
     const int64_t c0 = c * p.C;
     const int n_tok = (int)std::min<int64_t>(p.C, N - c0);
-    GRPO_HIP(grpo::launch_lse_partials<T>(W, H + c0 * d, y + c0, V, d, n_tok, (int)p.cpad, xf, pm,
-                                          ps, zy, s));
+    GRPO_HIP(grpo::launch_lse_partials<T>(W, H + c0 * d, y + c0, V, d, n_tok, (int)p.cpad, xf,
+                                          w_scale, h_scale ? h_scale + c0 : nullptr, pm, ps, zy,
+                                          s));
     GRPO_HIP(grpo::launch_lse_merge(mode, pm, ps, zy, (int)p.S, (int)p.cpad, n_tok, c0, y, V,
                                     out_lp, out_lse, out_kl, ref_lp, mask, adv, L, beta, lv, seq_n,
                                     lpart, cpart, (int)(c * p.parts_per_chunk), s));
@@ -340,12 +343,29 @@ const char* grpo_strerror(int code) {
 
 const char* grpo_last_error(void) { return g_last_error; }
 
+// The fp8 backward runs the bf16 backward on exact bf16 copies of H and W,
+// kept after the bf16 plan's workspace.
+struct Fp8BwdPlan {
+  size_t o_h, o_w, total;
+};
+Fp8BwdPlan plan_bwd_fp8(int64_t N, int64_t d, int64_t V, int64_t chunk) {
+  Fp8BwdPlan p{};
+  Carve c;
+  c.off = plan_bwd(N, d, V, GRPO_BF16, chunk).total;
+  p.o_h = c.take((size_t)(N * d) * 2);
+  p.o_w = c.take((size_t)(V * d) * 2);
+  p.total = c.off;
+  return p;
+}
+
 size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
-  if (check_shape(N, d, V, dtype, chunk) != GRPO_OK) return 0;
+  if (check_shape(N, d, V, dtype, chunk, true) != GRPO_OK) return 0;
   switch (op) {
     case GRPO_OP_REF:
     case GRPO_OP_FWD: return plan_fwd(N, V, chunk).total;
-    case GRPO_OP_BWD: return plan_bwd(N, d, V, dtype, chunk).total;
+    case GRPO_OP_BWD:
+      return dtype == GRPO_FP8_E4M3 ? plan_bwd_fp8(N, d, V, chunk).total
+                                    : plan_bwd(N, d, V, dtype, chunk).total;
     default: fail(GRPO_ERR_INVALID_ARG, "unknown op %d", op); return 0;
   }
 }
@@ -362,11 +382,13 @@ int64_t grpo_auto_chunk(int64_t B, int64_t L, int64_t d, int64_t V, int dtype,
     return 0;
   }
   const int64_t N = B * L;
-  if (check_shape(N, d, V, dtype, 1) != GRPO_OK) return 0;
+  if (check_shape(N, d, V, dtype, 1, true) != GRPO_OK) return 0;
   constexpr int64_t kStep = 256, kCap = 8192;  // best measured chunk at d = 1536 and 4096
   const int64_t top = std::min<int64_t>(kCap, round_up(N, kStep));
   for (int64_t c = top; c > kStep; c -= kStep)
-    if (plan_fwd(N, V, c).total + plan_bwd(N, d, V, dtype, c).total <= budget_bytes) return c;
+    if (grpo_workspace_bytes(GRPO_OP_FWD, N, d, V, dtype, c) +
+            grpo_workspace_bytes(GRPO_OP_BWD, N, d, V, dtype, c) <= budget_bytes)
+      return c;
   return kStep;
 }
 
@@ -513,6 +535,167 @@ int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t*
                   size_t workspace_bytes, void* stream) {
   return grpo_loss_bwd_ex(H, W, y, mask, adv, ref_lp, lp, lse, B, L, d, V, dtype, beta,
                           grad_loss, chunk, nullptr, dH, dW, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- fp8 e4m3 path
+namespace {
+constexpr int kQuantParts = 1024;   // partial maxima of a per-tensor scale
+}
+
+size_t grpo_quantize_fp8_workspace_bytes(void) { return kQuantParts * 4 + 256; }
+
+int grpo_quantize_fp8(const void* X, int dtype, int64_t rows, int64_t cols, int per_row,
+                      uint8_t* codes, float* scales, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_last_error[0] = 0;
+  GRPO_CHECK_PTR(X);
+  GRPO_CHECK_PTR(codes);
+  GRPO_CHECK_PTR(scales);
+  if (dtype != GRPO_F32 && dtype != GRPO_BF16)
+    return fail(GRPO_ERR_INVALID_ARG, "quantize takes GRPO_F32 or GRPO_BF16 input, not %d", dtype);
+  if (rows <= 0 || cols <= 0) return fail(GRPO_ERR_INVALID_ARG, "rows and cols must be positive");
+  if (per_row != 0 && per_row != 1) return fail(GRPO_ERR_INVALID_ARG, "per_row must be 0 or 1");
+  if (cols % 16 != 0) return fail(GRPO_ERR_UNSUPPORTED, "cols=%lld must be a multiple of 16",
+                                  (long long)cols);
+  if (rows > INT32_MAX) return fail(GRPO_ERR_UNSUPPORTED, "rows must fit int32");
+  if (!per_row && (workspace == nullptr || workspace_bytes < grpo_quantize_fp8_workspace_bytes()))
+    return fail(GRPO_ERR_WORKSPACE, "a per-tensor scale needs %zu bytes of workspace",
+                grpo_quantize_fp8_workspace_bytes());
+  const int64_t n = rows * cols;
+  const int nparts = (int)std::min<int64_t>(kQuantParts, (n + 4095) / 4096);
+  float* part = per_row ? nullptr : (float*)workspace;
+  int* e = per_row ? nullptr : (int*)((char*)workspace + kQuantParts * 4);
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == GRPO_BF16)
+    GRPO_HIP(grpo::launch_fp8_quantize<__bf16>((const __bf16*)X, rows, cols, per_row, part, nparts,
+                                               e, codes, scales, s));
+  else
+    GRPO_HIP(grpo::launch_fp8_quantize<float>((const float*)X, rows, cols, per_row, part, nparts, e,
+                                              codes, scales, s));
+  return GRPO_OK;
+}
+
+int grpo_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows, int64_t cols,
+                        int per_row, void* out, void* stream) {
+  g_last_error[0] = 0;
+  GRPO_CHECK_PTR(codes);
+  GRPO_CHECK_PTR(scales);
+  GRPO_CHECK_PTR(out);
+  if (rows <= 0 || cols <= 0) return fail(GRPO_ERR_INVALID_ARG, "rows and cols must be positive");
+  if (per_row != 0 && per_row != 1) return fail(GRPO_ERR_INVALID_ARG, "per_row must be 0 or 1");
+  if (cols % 16 != 0) return fail(GRPO_ERR_UNSUPPORTED, "cols=%lld must be a multiple of 16",
+                                  (long long)cols);
+  if (rows > INT32_MAX) return fail(GRPO_ERR_UNSUPPORTED, "rows must fit int32");
+  GRPO_HIP(grpo::launch_fp8_dequantize(codes, rows, cols, scales, per_row, (__bf16*)out,
+                                       (hipStream_t)stream));
+  return GRPO_OK;
+}
+
+int grpo_ref_logprobs_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8,
+                          const float* w_scale, const int32_t* y, int64_t N, int64_t d, int64_t V,
+                          int64_t chunk, const grpo_opts* opts, float* ref_lp, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  grpo::LogitXform xf;
+  grpo::LossVariant lv;
+  if (make_xform(opts, &xf) != GRPO_OK || make_variant(opts, &lv) != GRPO_OK)
+    return GRPO_ERR_INVALID_ARG;
+  GRPO_CHECK_PTR(H8);
+  GRPO_CHECK_PTR(h_scale);
+  GRPO_CHECK_PTR(W8);
+  GRPO_CHECK_PTR(w_scale);
+  GRPO_CHECK_PTR(y);
+  GRPO_CHECK_PTR(ref_lp);
+  int st = check_shape(N, d, V, GRPO_FP8_E4M3, chunk, true);
+  if (st != GRPO_OK) return st;
+  const size_t need = plan_fwd(N, V, chunk).total;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GRPO_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  return lse_pass<uint8_t>(0, H8, W8, y, nullptr, nullptr, nullptr, N, 1, d, V, 0.f, chunk, xf, lv,
+                           nullptr, ref_lp, nullptr, nullptr, (char*)workspace,
+                           (hipStream_t)stream, w_scale, h_scale);
+}
+
+int grpo_loss_fwd_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8,
+                      const float* w_scale, const int32_t* y, const uint8_t* mask,
+                      const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
+                      int64_t V, float beta, int64_t chunk, const grpo_opts* opts, float* loss,
+                      float* lp, float* kl, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  g_last_error[0] = 0;
+  grpo::LogitXform xf;
+  grpo::LossVariant lv;
+  if (make_xform(opts, &xf) != GRPO_OK || make_variant(opts, &lv) != GRPO_OK)
+    return GRPO_ERR_INVALID_ARG;
+  GRPO_CHECK_PTR(H8);
+  GRPO_CHECK_PTR(h_scale);
+  GRPO_CHECK_PTR(W8);
+  GRPO_CHECK_PTR(w_scale);
+  GRPO_CHECK_PTR(y);
+  GRPO_CHECK_PTR(mask);
+  GRPO_CHECK_PTR(adv);
+  GRPO_CHECK_PTR(ref_lp);
+  GRPO_CHECK_PTR(loss);
+  GRPO_CHECK_PTR(lp);
+  GRPO_CHECK_PTR(kl);
+  GRPO_CHECK_PTR(lse);
+  if (B <= 0 || L <= 0) return fail(GRPO_ERR_INVALID_ARG, "B and L must be positive");
+  if (B > INT32_MAX / L) return fail(GRPO_ERR_UNSUPPORTED, "B*L exceeds int32");
+  const int64_t N = B * L;
+  int st = check_shape(N, d, V, GRPO_FP8_E4M3, chunk, true);
+  if (st != GRPO_OK) return st;
+  if (!isfinite(beta)) return fail(GRPO_ERR_INVALID_ARG, "beta must be finite");
+  const size_t need = plan_fwd(N, V, chunk).total;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(GRPO_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  return lse_pass<uint8_t>(1, H8, W8, y, mask, adv, ref_lp, N, L, d, V, beta, chunk, xf, lv, loss,
+                           lp, kl, lse, (char*)workspace, (hipStream_t)stream, w_scale, h_scale);
+}
+
+int grpo_loss_bwd_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8,
+                      const float* w_scale, const int32_t* y, const uint8_t* mask,
+                      const float* adv, const float* ref_lp, const float* lp, const float* lse,
+                      int64_t B, int64_t L, int64_t d, int64_t V, float beta, float grad_loss,
+                      int64_t chunk, const grpo_opts* opts, void* dH, float* dW, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  g_last_error[0] = 0;
+  grpo::LogitXform xf;
+  grpo::LossVariant lv;
+  if (make_xform(opts, &xf) != GRPO_OK || make_variant(opts, &lv) != GRPO_OK)
+    return GRPO_ERR_INVALID_ARG;
+  GRPO_CHECK_PTR(H8);
+  GRPO_CHECK_PTR(h_scale);
+  GRPO_CHECK_PTR(W8);
+  GRPO_CHECK_PTR(w_scale);
+  GRPO_CHECK_PTR(y);
+  GRPO_CHECK_PTR(mask);
+  GRPO_CHECK_PTR(adv);
+  GRPO_CHECK_PTR(ref_lp);
+  GRPO_CHECK_PTR(lp);
+  GRPO_CHECK_PTR(lse);
+  GRPO_CHECK_PTR(dH);
+  GRPO_CHECK_PTR(dW);
+  if (B <= 0 || L <= 0) return fail(GRPO_ERR_INVALID_ARG, "B and L must be positive");
+  if (B > INT32_MAX / L) return fail(GRPO_ERR_UNSUPPORTED, "B*L exceeds int32");
+  const int64_t N = B * L;
+  int st = check_shape(N, d, V, GRPO_FP8_E4M3, chunk, true);
+  if (st != GRPO_OK) return st;
+  if (!isfinite(beta)) return fail(GRPO_ERR_INVALID_ARG, "beta must be finite");
+  if (!isfinite(grad_loss)) return fail(GRPO_ERR_INVALID_ARG, "grad_loss must be finite");
+  const Fp8BwdPlan p = plan_bwd_fp8(N, d, V, chunk);
+  if (workspace == nullptr || workspace_bytes < p.total)
+    return fail(GRPO_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", p.total,
+                workspace == nullptr ? (size_t)0 : workspace_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  __bf16* Hb = (__bf16*)(ws + p.o_h);
+  __bf16* Wb = (__bf16*)(ws + p.o_w);
+  GRPO_HIP(grpo::launch_fp8_dequantize(H8, N, d, h_scale, 1, Hb, s));
+  GRPO_HIP(grpo::launch_fp8_dequantize(W8, V, d, w_scale, 0, Wb, s));
+  return bwd_pass<__bf16>(Hb, Wb, y, mask, adv, ref_lp, lp, lse, N, L, d, V, beta, grad_loss, chunk,
+                          xf, lv, (__bf16*)dH, dW, ws, GRPO_BF16, s);
 }
 
 int grpo_gemm_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int dtype,

@@ -19,6 +19,8 @@
 // Every reduction runs in a fixed order, so results are bitwise reproducible.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "tile_mma.hpp"
 #include "timing.hpp"
@@ -127,12 +129,16 @@ __global__ void __launch_bounds__(64) k_advantages(const float* __restrict__ r, 
 }
 
 // ---------------------------------------------------------------- forward tile
+// T = uint8_t: float8 e4m3 codes, with w_scale[0] the head's scale and h_scale[t]
+// each token's (the logit is acc * w_scale * h_scale[t]); other T ignore both.
 template <typename T, bool SC>
 __global__ void __launch_bounds__(kThreads, 1)
     k_lse_partials(const T* __restrict__ W, const T* __restrict__ H, const int32_t* __restrict__ y,
                    int64_t V, int64_t d, int n_tok, int cpad, int tm, int tn, LogitXform xf,
+                   const float* __restrict__ w_scale, const float* __restrict__ h_scale,
                    float* __restrict__ part_m, float* __restrict__ part_s,
                    float* __restrict__ zy) {
+  constexpr bool kFp8 = std::is_same<T, uint8_t>::value;
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
   int mt, nt;
@@ -145,11 +151,25 @@ __global__ void __launch_bounds__(kThreads, 1)
   const Operand B{(const char*)(H + (int64_t)n0 * d), rowb, n_tok - n0, rowb};
 
   Acc acc;
-  tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+  if constexpr (kFp8)
+    tile_mainloop_fp8(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+  else
+    tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm0 = (wave >> 1) * 128;
   const bool full = mvalid >= wm0 + 128;
+  // per token column: the factor that turns the accumulator into the logit
+  // (the fp8 scales, powers of two; exactly 1 otherwise)
+  float cs[kWN];
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    cs[j] = 1.f;
+    if constexpr (kFp8) {
+      const int t = n0 + acc_col(wave, lane, j);
+      cs[j] = t < n_tok ? w_scale[0] * h_scale[t] : 1.f;
+    }
+  }
 
   // per token column j of this lane: (max, sum exp) of the transformed logits
   // over its 32 vocabulary rows.  The transform is increasing, so the max of
@@ -163,7 +183,7 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
       for (int e = 0; e < kAcc; ++e)
         if (full || acc_row(wave, lane, i, e) < mvalid) m = fmaxf(m, acc[i][j][e]);
-    const float mt = m == kNegInf ? kNegInf : xform<SC>(m, xf);
+    const float mt = m == kNegInf ? kNegInf : xform<SC>(m * cs[j], xf);
     const float mb = mt * kLog2e;
     float s = 0.f;
     if (SC) {
@@ -172,9 +192,9 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
         for (int e = 0; e < kAcc; ++e)
           if (full || acc_row(wave, lane, i, e) < mvalid)
-            s += ex2(fmaf(xform<true>(acc[i][j][e], xf), kLog2e, -mb));
+            s += ex2(fmaf(xform<true>(acc[i][j][e] * cs[j], xf), kLog2e, -mb));
     } else {
-      const float kl = xf.k * kLog2e;
+      const float kl = xf.k * kLog2e * cs[j];
 #pragma unroll
       for (int i = 0; i < kWM; ++i)
 #pragma unroll
@@ -209,7 +229,7 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
           for (int e = 0; e < kAcc; ++e)
             if (i == ti && e == te) v = acc[i][j][e];
-        zy[t] = xform<SC>(v, xf);
+        zy[t] = xform<SC>(v * cs[j], xf);
       }
     }
   }
@@ -774,6 +794,100 @@ __global__ void __launch_bounds__(kThreads, 1)
       }
 }
 
+// ---------------------------------------------------------------- fp8 quantisation
+// Scale exponent of a block of values: the smallest e with absmax <= 448 * 2^e
+// (0 for absmax = 0), decided by exact comparisons: absmax = f 2^k with
+// f in [0.5, 1) and 448 = 0.875 2^9.
+__device__ __forceinline__ int fp8_exponent(float absmax) {
+  if (!(absmax > 0.f)) return 0;
+  int k;
+  const float f = frexpf(absmax, &k);
+  return f <= 0.875f ? k - 9 : k - 8;
+}
+
+__device__ __forceinline__ float block_max256(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+template <typename T>
+__device__ __forceinline__ float to_float(T x) { return (float)x; }
+
+// Largest |x| of each block's share of X[0 .. n): part[blockIdx.x].
+template <typename T>
+__global__ void __launch_bounds__(256)
+    k_fp8_absmax_partial(const T* __restrict__ X, int64_t n, float* __restrict__ part) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, fabsf(to_float(X[i])));
+  m = block_max256(m, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+// The tensor's exponent and scale from the partial maxima.
+__global__ void __launch_bounds__(256)
+    k_fp8_tensor_exponent(const float* __restrict__ part, int nparts, int* __restrict__ e_out,
+                          float* __restrict__ scale_out) {
+  __shared__ float red[4];
+  float m = 0.f;
+  for (int i = threadIdx.x; i < nparts; i += 256) m = fmaxf(m, part[i]);
+  m = block_max256(m, red);
+  if (threadIdx.x == 0) {
+    const int e = fp8_exponent(m);
+    e_out[0] = e;
+    scale_out[0] = ldexpf(1.f, e);
+  }
+}
+
+// One block per row: the row's exponent (its own, or the tensor's from e_tensor),
+// its scale, and the e4m3 codes of x * 2^-e (an exact scaling; the conversion
+// rounds to nearest, ties to even).  cols is a multiple of 4.
+template <typename T>
+__global__ void __launch_bounds__(256)
+    k_fp8_quant_rows(const T* __restrict__ X, int64_t cols, const int* __restrict__ e_tensor,
+                     uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  __shared__ float red[4];
+  const int64_t r = blockIdx.x;
+  const T* x = X + r * cols;
+  int e;
+  if (e_tensor != nullptr) {
+    e = e_tensor[0];
+  } else {
+    float m = 0.f;
+    for (int64_t c = threadIdx.x; c < cols; c += 256) m = fmaxf(m, fabsf(to_float(x[c])));
+    e = fp8_exponent(block_max256(m, red));
+    if (threadIdx.x == 0) scales[r] = ldexpf(1.f, e);
+  }
+  uint32_t* out = (uint32_t*)(codes + r * cols);
+  for (int64_t w = threadIdx.x; w < cols / 4; w += 256) {
+    const float a = ldexpf(to_float(x[4 * w + 0]), -e), b = ldexpf(to_float(x[4 * w + 1]), -e);
+    const float c = ldexpf(to_float(x[4 * w + 2]), -e), dd = ldexpf(to_float(x[4 * w + 3]), -e);
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(c, dd, v, true);
+    out[w] = (uint32_t)v;
+  }
+}
+
+// bf16 copy of codes * scale (exact: 4 significant bits times a power of two).
+__global__ void __launch_bounds__(256)
+    k_fp8_dequant_rows(const uint8_t* __restrict__ codes, int64_t cols,
+                       const float* __restrict__ scales, int per_row, __bf16* __restrict__ out) {
+  const int64_t r = blockIdx.x;
+  const float sc = scales[per_row ? r : 0];
+  const uint32_t* in = (const uint32_t*)(codes + r * cols);
+  __bf16* o = out + r * cols;
+  for (int64_t w = threadIdx.x; w < cols / 4; w += 256) {
+    const int v = (int)in[w];
+    store4(o + 4 * w, __builtin_amdgcn_cvt_f32_fp8(v, 0) * sc, __builtin_amdgcn_cvt_f32_fp8(v, 1) * sc,
+           __builtin_amdgcn_cvt_f32_fp8(v, 2) * sc, __builtin_amdgcn_cvt_f32_fp8(v, 3) * sc);
+  }
+}
+
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
@@ -788,16 +902,17 @@ hipError_t launch_advantages(const float* rewards, int64_t groups, int64_t G, fl
 
 template <typename T>
 hipError_t launch_lse_partials(const T* W, const T* H, const int32_t* y, int64_t V, int64_t d,
-                               int n_tok, int cpad, const LogitXform& xf, float* part_m,
-                               float* part_s, float* zy, hipStream_t s) {
+                               int n_tok, int cpad, const LogitXform& xf, const float* w_scale,
+                               const float* h_scale, float* part_m, float* part_s, float* zy,
+                               hipStream_t s) {
   ScopedKernelTimer timer_(KK_LSE_PARTIALS, s);
   const int tm = cdiv(V, kBM), tn = cdiv(n_tok, kBN);
   if (xf.softcap)
     hipLaunchKernelGGL((k_lse_partials<T, true>), dim3(tm * tn), dim3(kThreads), 0, s, W, H, y, V,
-                       d, n_tok, cpad, tm, tn, xf, part_m, part_s, zy);
+                       d, n_tok, cpad, tm, tn, xf, w_scale, h_scale, part_m, part_s, zy);
   else
     hipLaunchKernelGGL((k_lse_partials<T, false>), dim3(tm * tn), dim3(kThreads), 0, s, W, H, y,
-                       V, d, n_tok, cpad, tm, tn, xf, part_m, part_s, zy);
+                       V, d, n_tok, cpad, tm, tn, xf, w_scale, h_scale, part_m, part_s, zy);
   return hipGetLastError();
 }
 
@@ -939,8 +1054,8 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
 
 #define GRPO_INSTANTIATE(T)                                                                       \
   template hipError_t launch_lse_partials<T>(const T*, const T*, const int32_t*, int64_t,         \
-                                             int64_t, int, int, const LogitXform&, float*,        \
-                                             float*, float*, hipStream_t);                        \
+                                             int64_t, int, int, const LogitXform&, const float*,  \
+                                             const float*, float*, float*, float*, hipStream_t);  \
   template hipError_t launch_transpose<T>(const T*, int64_t, int64_t, T*, int64_t, hipStream_t);  \
   template hipError_t launch_bwd_prep<T>(const T*, int64_t, const int32_t*, const int32_t*,       \
                                          int64_t, int, int, const int32_t*, const uint8_t*,        \
@@ -964,5 +1079,38 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
 
 GRPO_INSTANTIATE(float)
 GRPO_INSTANTIATE(__bf16)
+template hipError_t launch_lse_partials<uint8_t>(const uint8_t*, const uint8_t*, const int32_t*,
+                                                 int64_t, int64_t, int, int, const LogitXform&,
+                                                 const float*, const float*, float*, float*,
+                                                 float*, hipStream_t);
+
+
+// ---------------------------------------------------------------- fp8 launchers
+template <typename T>
+hipError_t launch_fp8_quantize(const T* X, int64_t rows, int64_t cols, int per_row, float* part,
+                               int nparts, int* e_tensor, uint8_t* codes, float* scales,
+                               hipStream_t s) {
+  ScopedKernelTimer timer_(KK_FP8_QUANT, s);
+  if (!per_row) {
+    hipLaunchKernelGGL(k_fp8_absmax_partial<T>, dim3(nparts), dim3(256), 0, s, X, rows * cols, part);
+    hipLaunchKernelGGL(k_fp8_tensor_exponent, dim3(1), dim3(256), 0, s, part, nparts, e_tensor,
+                       scales);
+  }
+  hipLaunchKernelGGL(k_fp8_quant_rows<T>, dim3((unsigned)rows), dim3(256), 0, s, X, cols,
+                     per_row ? nullptr : e_tensor, codes, scales);
+  return hipGetLastError();
+}
+template hipError_t launch_fp8_quantize<float>(const float*, int64_t, int64_t, int, float*, int,
+                                               int*, uint8_t*, float*, hipStream_t);
+template hipError_t launch_fp8_quantize<__bf16>(const __bf16*, int64_t, int64_t, int, float*, int,
+                                                int*, uint8_t*, float*, hipStream_t);
+
+hipError_t launch_fp8_dequantize(const uint8_t* codes, int64_t rows, int64_t cols,
+                                 const float* scales, int per_row, __bf16* out, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_FP8_DEQUANT, s);
+  hipLaunchKernelGGL(k_fp8_dequant_rows, dim3((unsigned)rows), dim3(256), 0, s, codes, cols,
+                     scales, per_row, out);
+  return hipGetLastError();
+}
 
 }  // namespace grpo

@@ -40,8 +40,20 @@ hipError_t launch_advantages(const float* rewards, int64_t groups, int64_t G, fl
 // for the tokens [0, n_tok) of one chunk whose hidden states start at H.
 template <typename T>
 hipError_t launch_lse_partials(const T* W, const T* H, const int32_t* y, int64_t V, int64_t d,
-                               int n_tok, int cpad, const LogitXform& xf, float* part_m,
-                               float* part_s, float* zy, hipStream_t s);
+                               int n_tok, int cpad, const LogitXform& xf, const float* w_scale,
+                               const float* h_scale, float* part_m, float* part_s, float* zy,
+                               hipStream_t s);
+
+// fp8 e4m3 codes of X (rows x cols, cols a multiple of 4) with power-of-two
+// scales, per row (scales[rows]) or for the tensor (scales[0]; part holds
+// nparts partial maxima and e_tensor the exponent).
+template <typename T>
+hipError_t launch_fp8_quantize(const T* X, int64_t rows, int64_t cols, int per_row, float* part,
+                               int nparts, int* e_tensor, uint8_t* codes, float* scales,
+                               hipStream_t s);
+// out (bf16, rows x cols) = codes * scale, exact.
+hipError_t launch_fp8_dequantize(const uint8_t* codes, int64_t rows, int64_t cols,
+                                 const float* scales, int per_row, __bf16* out, hipStream_t s);
 
 // Merge the partials of one chunk (tokens c0 .. c0 + n_tok - 1).
 // mode 0: reference log-probs -> out_lp.  mode 1: loss forward.

@@ -109,11 +109,10 @@ struct Operand {
 // moving 8 rows x 128 B (lane i fills slot i & 7 of row i >> 3 of the group).
 struct Loader {
   __amdgpu_buffer_rsrc_t rsrc;
-  uint32_t rowoff[8];       // byte offset of each of this lane's 8 rows (kOOB if absent)
   uint32_t chunk_bytes;     // logical 16-byte chunk this lane copies, even 8-row groups
   uint32_t chunk_bytes_odd; // the same for odd 8-row groups (f(r) flips bit 0)
   uint32_t k_bytes;
-  uint32_t voff[8];         // rowoff[j] + this lane's chunk (kOOB if the row is absent)
+  uint32_t voff[8];         // byte offset of this lane's row j plus its chunk (kOOB if absent)
 
   __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
     int rv = op.rows_valid < 0 ? 0 : (op.rows_valid > kBM ? kBM : op.rows_valid);
@@ -121,22 +120,20 @@ struct Loader {
     const int r_in = lane >> 3;                          // row within an 8-row group
     chunk_bytes = (uint32_t)(((lane & 7) ^ r_in) << 4);  // slot lane & 7 holds chunk slot ^ f(r)
     chunk_bytes_odd = chunk_bytes ^ 16u;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int r = wave * 64 + j * 8 + r_in;
-      rowoff[j] = r < rv ? (uint32_t)r * op.ld_bytes : kOOB;
-    }
     k_bytes = op.k_bytes;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      voff[j] = rowoff[j] == kOOB ? kOOB : rowoff[j] + ((j & 1) ? chunk_bytes_odd : chunk_bytes);
+    for (int j = 0; j < 8; ++j) {
+      const int r = wave * 64 + j * 8 + r_in;
+      voff[j] = r < rv ? (uint32_t)r * op.ld_bytes + ((j & 1) ? chunk_bytes_odd : chunk_bytes)
+                       : kOOB;
+    }
   }
 
   // Copy instruction j (rows 8 j .. 8 j + 7 of this wave's 64) of slice `kt`.
   // A slice past the end reads as zeros.
   __device__ __forceinline__ void issue1(int kt, int j, char GRPO_LDS* tile, int wave) const {
     const uint32_t kb = (uint32_t)kt * kBKB + ((j & 1) ? chunk_bytes_odd : chunk_bytes);
-    const uint32_t off = kb < k_bytes ? rowoff[j] + kb : kOOB;
+    const uint32_t off = kb < k_bytes ? voff[j] + (uint32_t)kt * kBKB : kOOB;
     char GRPO_LDS* dst = tile + (wave * 64 + j * 8) * kBKB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, off, 0, 0, kCopyPolicy);
   }
@@ -288,6 +285,159 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
     kstep<T, true, false>(acc, fa0, fb0, fa1, fb1, cur, abase, bbase, sw1, la, lb, 0, cur, wave);
     kstep<T, false, false>(acc, fa1, fb1, fa0, fb0, cur, abase, bbase, sw0, la, lb, 0, cur, wave);
   }
+  wait_vmem_all();
+}
+
+// ---------------------------------------------------------------- fp8 main loop
+// The same tile with float8 e4m3 operands (one byte per element):
+// v_mfma_f32_16x16x128_f8f6f4 takes a whole 128-byte slice row per k-step, so
+// a slice is one k-step of 64 MFMAs (32 cycles each, twice the bf16 rate).
+// A lane's 32-byte fragment is the two 16-byte chunks that the bf16 loop reads
+// for its two k-steps (chunks l/16 and 4 + l/16 of the row, same swizzle):
+// the instruction sums over k, so any k order that A and B share is exact.
+// Fragments are 8 VGPRs, so only B's are double buffered; A's rows 0..5 are
+// reloaded in place once their 8 MFMAs have issued, and rows 6 and 7 have two
+// buffers (fa[6..7] and fa[8..9]) that alternate between iterations, so no
+// LDS read is left in flight at the slice barrier.
+typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+
+__device__ __forceinline__ f32x4_t mfma_fp8(f32x4_t c, const i32x8_t& a, const i32x8_t& b) {
+  // zero scale operands: no block scaling
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ void read_frag_half(i32x8_t& f, int half, const char GRPO_LDS* p) {
+  const i32x4_t v = *(const i32x4_t GRPO_LDS*)p;
+  if (half == 0) f.lo = v;
+  else f.hi = v;
+}
+
+// One slice (k-step) of 64 MFMAs.  PAR selects the buffer of A rows 6..7 this
+// iteration uses (fa[6..7] or fa[8..9]); the next slice's fragments are read
+// from stage `rst`: fbn after even q < 32, A rows 6..7 into the other buffer
+// after q = 33..39 (odd), A row i < 6 after its last MFMA.  COPY: copy
+// instruction c of slice `ckt` into stage `cst` after MFMA 2c + 1.
+template <bool PAR, bool READ, bool COPY, bool FULL>
+__device__ __forceinline__ void kstep_fp8(Acc& acc, i32x8_t (&fa)[10], const i32x8_t (&fbc)[8],
+                                          i32x8_t (&fbn)[8], const char GRPO_LDS* rst,
+                                          uint32_t abase, uint32_t bbase, uint32_t sw0,
+                                          uint32_t sw1, const Loader& la, const Loader& lb,
+                                          int ckt, char GRPO_LDS* cst, int wave) {
+#pragma unroll
+  for (int q = 0; q < 64; ++q) {
+    const int i = q >> 3, j = q & 7;
+    const int ai = i < 6 ? i : (PAR ? i + 2 : i);
+    acc[i][j] = mfma_fp8(acc[i][j], fa[ai], fbc[j]);
+    GRPO_FENCE();
+    if (READ && (q & 1) == 0 && q < 32) {
+      const int f = q >> 2, h = (q >> 1) & 1;
+      read_frag_half(fbn[f], h, rst + kTileBytes + bbase + f * 16 * kBKB + (h ? sw1 : sw0));
+      GRPO_FENCE();
+    }
+    if (READ && (q & 1) == 1 && q >= 33 && q <= 39) {
+      const int k = (q - 33) >> 1, r = 6 + (k >> 1), h = k & 1;
+      read_frag_half(fa[PAR ? r : r + 2], h, rst + abase + r * 16 * kBKB + (h ? sw1 : sw0));
+      GRPO_FENCE();
+    }
+    if (READ && j == 7 && i < 6) {
+      read_frag_half(fa[i], 0, rst + abase + i * 16 * kBKB + sw0);
+      read_frag_half(fa[i], 1, rst + abase + i * 16 * kBKB + sw1);
+      GRPO_FENCE();
+    }
+    if (COPY && (q & 1) == 1 && q < 32) {
+      const int c = q >> 1;
+      if (FULL) {
+        if (c < 8) la.issue1_full(ckt, c, cst, wave);
+        else lb.issue1_full(ckt, c - 8, cst + kTileBytes, wave);
+      } else {
+        if (c < 8) la.issue1(ckt, c, cst, wave);
+        else lb.issue1(ckt, c - 8, cst + kTileBytes, wave);
+      }
+      GRPO_FENCE();
+    }
+  }
+}
+
+// Slice barrier: this wave's copies of the next slice have landed and its reads
+// of the current stage are done; after it every wave may read the next slice
+// and overwrite the current one.
+__device__ __forceinline__ void slice_barrier() {
+  wait_vmem_all();
+  wait_lds_all();
+  __builtin_amdgcn_s_barrier();
+  GRPO_FENCE();
+}
+
+template <bool PAR, bool FULL>
+__device__ __forceinline__ void fp8_iter(Acc& acc, i32x8_t (&fa)[10], i32x8_t (&fbA)[8],
+                                         i32x8_t (&fbB)[8], char GRPO_LDS* lds, int kt,
+                                         uint32_t abase, uint32_t bbase, uint32_t sw0,
+                                         uint32_t sw1, const Loader& la, const Loader& lb,
+                                         int wave) {
+  char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
+  char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
+  slice_barrier();
+  if (PAR)
+    kstep_fp8<true, true, true, FULL>(acc, fa, fbB, fbA, nxt, abase, bbase, sw0, sw1, la, lb,
+                                      kt + 2, cur, wave);
+  else
+    kstep_fp8<false, true, true, FULL>(acc, fa, fbA, fbB, nxt, abase, bbase, sw0, sw1, la, lb,
+                                       kt + 2, cur, wave);
+}
+
+// fp8 main loop: A and B rows of k_bytes e4m3 codes.  Same contract as
+// tile_mainloop.
+__device__ __forceinline__ void tile_mainloop_fp8(Acc& acc, const Operand& A, const Operand& B,
+                                                  int k_slices, char GRPO_LDS* lds) {
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+#pragma unroll
+  for (int i = 0; i < kWM; ++i)
+#pragma unroll
+    for (int j = 0; j < kWN; ++j)
+#pragma unroll
+      for (int e = 0; e < kAcc; ++e) acc[i][j][e] = 0.f;
+  if (k_slices <= 0) return;
+  Loader la, lb;
+  la.init(A, wave, lane);
+  lb.init(B, wave, lane);
+  const uint32_t abase = (uint32_t)((wave >> 1) * 128 + (lane & 15)) * kBKB;
+  const uint32_t bbase = (uint32_t)((wave & 1) * 128 + (lane & 15)) * kBKB;
+  const uint32_t fr = (uint32_t)((lane & 7) ^ ((lane >> 3) & 1));
+  const uint32_t sw0 = ((0u + (uint32_t)(lane >> 4)) ^ fr) << 4;
+  const uint32_t sw1 = ((4u + (uint32_t)(lane >> 4)) ^ fr) << 4;
+
+  la.issue(0, lds, wave);
+  lb.issue(0, lds + kTileBytes, wave);
+  la.issue(1, lds + kStageBytes, wave);
+  lb.issue(1, lds + kStageBytes + kTileBytes, wave);
+  wait_vmem_but_one_slice();
+  __builtin_amdgcn_s_barrier();
+  i32x8_t fa[10], fbA[8], fbB[8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    read_frag_half(fa[f], 0, lds + abase + f * 16 * kBKB + sw0);
+    read_frag_half(fa[f], 1, lds + abase + f * 16 * kBKB + sw1);
+    read_frag_half(fbA[f], 0, lds + kTileBytes + bbase + f * 16 * kBKB + sw0);
+    read_frag_half(fbA[f], 1, lds + kTileBytes + bbase + f * 16 * kBKB + sw1);
+  }
+  // Copies take the checked form throughout: with 32-cycle MFMAs the three
+  // VALU operations per copy fit in the issue shadow.  The slice count is
+  // rounded up to even (a zero slice past the end adds nothing), so every
+  // iteration's buffer parity is known at compile time.
+  const int k_even = (k_slices + 1) & ~1;
+  int kt = 0;
+  for (; kt + 2 < k_even; kt += 2) {
+    fp8_iter<false, false>(acc, fa, fbA, fbB, lds, kt, abase, bbase, sw0, sw1, la, lb, wave);
+    fp8_iter<true, false>(acc, fa, fbA, fbB, lds, kt + 1, abase, bbase, sw0, sw1, la, lb, wave);
+  }
+  // the last two slices: read the last one's fragments, copy nothing
+  slice_barrier();
+  kstep_fp8<false, true, false, false>(acc, fa, fbA, fbB, lds + ((kt + 1) & 1) * kStageBytes, abase,
+                                       bbase, sw0, sw1, la, lb, 0, lds, wave);
+  kstep_fp8<true, false, false, false>(acc, fa, fbB, fbA, lds, abase, bbase, sw0, sw1, la, lb, 0,
+                                       lds, wave);
   wait_vmem_all();
 }
 

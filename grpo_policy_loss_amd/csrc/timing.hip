@@ -21,7 +21,7 @@ thread_local State g_state;
 const char* const kNames[KK_COUNT] = {
     "advantages", "lse_partials", "lse_merge", "loss_final", "active_scan", "transpose",
     "bwd_prep",   "dz",           "dh_gemm",   "dw_gemm",    "dh_scatter",  "zero",
-    "gemm_nt",    "seq_counts"};
+    "gemm_nt",    "seq_counts", "fp8_quantize", "fp8_dequantize"};
 
 }  // namespace
 

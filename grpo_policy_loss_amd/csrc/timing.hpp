@@ -25,6 +25,8 @@ enum KernelKind {
   KK_ZERO,
   KK_GEMM_NT,
   KK_SEQ_COUNTS,
+  KK_FP8_QUANT,
+  KK_FP8_DEQUANT,
   KK_COUNT
 };
 

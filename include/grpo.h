@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-typedef enum { GRPO_F32 = 0, GRPO_BF16 = 1 } grpo_dtype;
+typedef enum { GRPO_F32 = 0, GRPO_BF16 = 1, GRPO_FP8_E4M3 = 2 } grpo_dtype;
 
 typedef enum {
   GRPO_OK = 0,
@@ -232,6 +232,59 @@ int grpo_loss_bwd_ex(const void* H, const void* W, const int32_t* y, const uint8
                      int64_t B, int64_t L, int64_t d, int64_t V, int dtype, float beta,
                      float grad_loss, int64_t chunk, const grpo_opts* opts, void* dH,
                      float* dW, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fp8 path (Unsloth docs: FP8 RL training is offered; Unsloth blog, "Unsloth
+ * efficient GRPO algorithm": a naive float8 linear cross-entropy breaks loss
+ * scaling).  The pages give no recipe; here the LM-head GEMM takes OCP float8
+ * e4m3 ("fn": bias 7, 3 mantissa bits, no infinities, largest 448) codes with
+ * float32 accumulation (v_mfma_f32_16x16x128_f8f6f4, twice the bf16 rate) and
+ * float32 log-sum-exp.  Each hidden-state row (token) has its own scale and
+ * the head one scale; the logit is z = (sum_k h8 w8) * w_scale * h_scale[t].
+ * Scales are powers of two, so dequantised values are exact.
+ *
+ * grpo_quantize_fp8: X [rows, cols] (GRPO_F32 or GRPO_BF16, device) ->
+ *   codes [rows, cols] uint8 and scales (float32, device): per_row = 1 gives
+ *   scales[rows], per_row = 0 one scales[0] for the tensor.  The scale of a
+ *   row (or tensor) is 2^e with e the smallest integer such that its largest
+ *   |x| <= 448 * 2^e (e = 0 for an all-zero block); codes are x / 2^e rounded
+ *   to the nearest e4m3 value, ties to even (the division is exact).  cols must
+ *   be a multiple of 16.  per_row = 0 needs grpo_quantize_fp8_workspace_bytes()
+ *   of workspace (partial maxima); per_row = 1 needs none (NULL allowed).
+ * grpo_dequantize_fp8: out [rows, cols] bfloat16 = codes * scale, exact.
+ * grpo_ref_logprobs_fp8, grpo_loss_fwd_fp8: grpo_ref_logprobs_ex and
+ *   grpo_loss_fwd_ex on fp8 codes H8 [N, d] (h_scale [N]) and W8 [V, d]
+ *   (w_scale [1]); outputs and workspace (grpo_workspace_bytes with dtype
+ *   GRPO_FP8_E4M3) as there.  d must be a multiple of 16.
+ * grpo_loss_bwd_fp8: the backward of that loss with respect to the dequantised
+ *   H and W: it writes exact bfloat16 copies of them into its workspace
+ *   (grpo_workspace_bytes(GRPO_OP_BWD, ..., GRPO_FP8_E4M3, chunk) includes
+ *   them) and runs the bfloat16 backward; dH [N, d] is bfloat16.  The
+ *   recomputed logits then differ from the forward's only by the order of
+ *   float32 summation.
+ */
+size_t grpo_quantize_fp8_workspace_bytes(void);
+int grpo_quantize_fp8(const void* X, int dtype, int64_t rows, int64_t cols, int per_row,
+                      uint8_t* codes, float* scales, void* workspace, size_t workspace_bytes,
+                      void* stream);
+int grpo_dequantize_fp8(const uint8_t* codes, const float* scales, int64_t rows, int64_t cols,
+                        int per_row, void* out, void* stream);
+int grpo_ref_logprobs_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8,
+                          const float* w_scale, const int32_t* y, int64_t N, int64_t d, int64_t V,
+                          int64_t chunk, const grpo_opts* opts, float* ref_lp, void* workspace,
+                          size_t workspace_bytes, void* stream);
+int grpo_loss_fwd_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8,
+                      const float* w_scale, const int32_t* y, const uint8_t* mask,
+                      const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
+                      int64_t V, float beta, int64_t chunk, const grpo_opts* opts, float* loss,
+                      float* lp, float* kl, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream);
+int grpo_loss_bwd_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8,
+                      const float* w_scale, const int32_t* y, const uint8_t* mask,
+                      const float* adv, const float* ref_lp, const float* lp, const float* lse,
+                      int64_t B, int64_t L, int64_t d, int64_t V, float beta, float grad_loss,
+                      int64_t chunk, const grpo_opts* opts, void* dH, float* dW, void* workspace,
+                      size_t workspace_bytes, void* stream);
 
 /*
  * Diagnostic: C[M, N] (float32, row-major, written) = A[M, K] . B[N, K]^T,
