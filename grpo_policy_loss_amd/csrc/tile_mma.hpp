@@ -295,10 +295,13 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
 // A lane's 32-byte fragment is the two 16-byte chunks that the bf16 loop reads
 // for its two k-steps (chunks l/16 and 4 + l/16 of the row, same swizzle):
 // the instruction sums over k, so any k order that A and B share is exact.
-// Fragments are 8 VGPRs, so only B's are double buffered; A's rows 0..5 are
-// reloaded in place once their 8 MFMAs have issued, and rows 6 and 7 have two
-// buffers (fa[6..7] and fa[8..9]) that alternate between iterations, so no
-// LDS read is left in flight at the slice barrier.
+// Fragments are 8 VGPRs, so only B's are double buffered; A's rows 0..6 are
+// reloaded in place once their 8 MFMAs have issued (row 6 nine MFMAs before
+// the slice barrier), and row 7 has two buffers (fa[7] and fa[8]) that
+// alternate between iterations, so no LDS read is left in flight at the
+// barrier.  Its LDS layout is [A stage 0 | A stage 1 | B stage 0 | B stage 1]
+// (32 KB each), so both stages of an operand sit within the 16-bit offset of
+// one ds_read base: two base registers per operand instead of four.
 typedef __attribute__((ext_vector_type(8))) int i32x8_t;
 typedef __attribute__((ext_vector_type(4))) int i32x4_t;
 
@@ -313,46 +316,51 @@ __device__ __forceinline__ void read_frag_half(i32x8_t& f, int half, const char 
   else f.hi = v;
 }
 
-// One slice (k-step) of 64 MFMAs.  PAR selects the buffer of A rows 6..7 this
-// iteration uses (fa[6..7] or fa[8..9]); the next slice's fragments are read
-// from stage `rst`: fbn after even q < 32, A rows 6..7 into the other buffer
-// after q = 33..39 (odd), A row i < 6 after its last MFMA.  COPY: copy
-// instruction c of slice `ckt` into stage `cst` after MFMA 2c + 1.
-template <bool PAR, bool READ, bool COPY, bool FULL>
-__device__ __forceinline__ void kstep_fp8(Acc& acc, i32x8_t (&fa)[10], const i32x8_t (&fbc)[8],
-                                          i32x8_t (&fbn)[8], const char GRPO_LDS* rst,
-                                          uint32_t abase, uint32_t bbase, uint32_t sw0,
-                                          uint32_t sw1, const Loader& la, const Loader& lb,
-                                          int ckt, char GRPO_LDS* cst, int wave) {
+// One slice (k-step) of 64 MFMAs.  PAR selects the buffer of A row 7 this
+// iteration uses (fa[7] or fa[8]); the next slice's fragments are read from
+// stage `rst`: fbn after even q < 32, A row 7 into the other buffer after
+// q = 33 and 35, A row i < 7 after its last MFMA.  COPY: copy instruction c of
+// slice `ckt` into stage `cst` after MFMA 2c + 1.
+// Fragment reads address lds + (lane base) + (compile-time offset): the lane
+// bases a0/a1 (A rows, chunks sw0/sw1) and b0/b1 (B rows) are loop invariant,
+// and RS (the stage read) and CS (the stage refilled) are template constants.
+template <bool PAR, bool READ, bool COPY, bool FULL, int RS, int CS>
+__device__ __forceinline__ void kstep_fp8(Acc& acc, i32x8_t (&fa)[9], const i32x8_t (&fbc)[8],
+                                          i32x8_t (&fbn)[8], const char GRPO_LDS* lds,
+                                          uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                          const Loader& la, const Loader& lb, int ckt, int wave) {
+  constexpr int kAoff = RS * kTileBytes, kBoff = (2 + RS) * kTileBytes;
+  char GRPO_LDS* cstA = (char GRPO_LDS*)lds + CS * kTileBytes;
+  char GRPO_LDS* cstB = (char GRPO_LDS*)lds + (2 + CS) * kTileBytes;
 #pragma unroll
   for (int q = 0; q < 64; ++q) {
     const int i = q >> 3, j = q & 7;
-    const int ai = i < 6 ? i : (PAR ? i + 2 : i);
+    const int ai = (i == 7 && PAR) ? 8 : i;
     acc[i][j] = mfma_fp8(acc[i][j], fa[ai], fbc[j]);
     GRPO_FENCE();
     if (READ && (q & 1) == 0 && q < 32) {
       const int f = q >> 2, h = (q >> 1) & 1;
-      read_frag_half(fbn[f], h, rst + kTileBytes + bbase + f * 16 * kBKB + (h ? sw1 : sw0));
+      read_frag_half(fbn[f], h, lds + (h ? b1 : b0) + (kBoff + f * 16 * kBKB));
       GRPO_FENCE();
     }
-    if (READ && (q & 1) == 1 && q >= 33 && q <= 39) {
-      const int k = (q - 33) >> 1, r = 6 + (k >> 1), h = k & 1;
-      read_frag_half(fa[PAR ? r : r + 2], h, rst + abase + r * 16 * kBKB + (h ? sw1 : sw0));
+    if (READ && (q == 33 || q == 35)) {
+      const int h = (q - 33) >> 1;
+      read_frag_half(fa[PAR ? 7 : 8], h, lds + (h ? a1 : a0) + (kAoff + 7 * 16 * kBKB));
       GRPO_FENCE();
     }
-    if (READ && j == 7 && i < 6) {
-      read_frag_half(fa[i], 0, rst + abase + i * 16 * kBKB + sw0);
-      read_frag_half(fa[i], 1, rst + abase + i * 16 * kBKB + sw1);
+    if (READ && j == 7 && i < 7) {
+      read_frag_half(fa[i], 0, lds + a0 + (kAoff + i * 16 * kBKB));
+      read_frag_half(fa[i], 1, lds + a1 + (kAoff + i * 16 * kBKB));
       GRPO_FENCE();
     }
     if (COPY && (q & 1) == 1 && q < 32) {
       const int c = q >> 1;
       if (FULL) {
-        if (c < 8) la.issue1_full(ckt, c, cst, wave);
-        else lb.issue1_full(ckt, c - 8, cst + kTileBytes, wave);
+        if (c < 8) la.issue1_full(ckt, c, cstA, wave);
+        else lb.issue1_full(ckt, c - 8, cstB, wave);
       } else {
-        if (c < 8) la.issue1(ckt, c, cst, wave);
-        else lb.issue1(ckt, c - 8, cst + kTileBytes, wave);
+        if (c < 8) la.issue1(ckt, c, cstA, wave);
+        else lb.issue1(ckt, c - 8, cstB, wave);
       }
       GRPO_FENCE();
     }
@@ -370,20 +378,18 @@ __device__ __forceinline__ void slice_barrier() {
 }
 
 template <bool PAR, bool FULL>
-__device__ __forceinline__ void fp8_iter(Acc& acc, i32x8_t (&fa)[10], i32x8_t (&fbA)[8],
+__device__ __forceinline__ void fp8_iter(Acc& acc, i32x8_t (&fa)[9], i32x8_t (&fbA)[8],
                                          i32x8_t (&fbB)[8], char GRPO_LDS* lds, int kt,
-                                         uint32_t abase, uint32_t bbase, uint32_t sw0,
-                                         uint32_t sw1, const Loader& la, const Loader& lb,
-                                         int wave) {
-  char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
-  char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
+                                         uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
+                                         const Loader& la, const Loader& lb, int wave) {
+  // this iteration's stage is PAR (= kt & 1): it reads the other and refills its own
   slice_barrier();
   if (PAR)
-    kstep_fp8<true, true, true, FULL>(acc, fa, fbB, fbA, nxt, abase, bbase, sw0, sw1, la, lb,
-                                      kt + 2, cur, wave);
+    kstep_fp8<true, true, true, FULL, 0, 1>(acc, fa, fbB, fbA, lds, a0, a1, b0, b1, la, lb,
+                                            kt + 2, wave);
   else
-    kstep_fp8<false, true, true, FULL>(acc, fa, fbA, fbB, nxt, abase, bbase, sw0, sw1, la, lb,
-                                       kt + 2, cur, wave);
+    kstep_fp8<false, true, true, FULL, 1, 0>(acc, fa, fbA, fbB, lds, a0, a1, b0, b1, la, lb,
+                                             kt + 2, wave);
 }
 
 // fp8 main loop: A and B rows of k_bytes e4m3 codes.  Same contract as
@@ -407,20 +413,21 @@ __device__ __forceinline__ void tile_mainloop_fp8(Acc& acc, const Operand& A, co
   const uint32_t fr = (uint32_t)((lane & 7) ^ ((lane >> 3) & 1));
   const uint32_t sw0 = ((0u + (uint32_t)(lane >> 4)) ^ fr) << 4;
   const uint32_t sw1 = ((4u + (uint32_t)(lane >> 4)) ^ fr) << 4;
+  const uint32_t a0 = abase + sw0, a1 = abase + sw1, b0 = bbase + sw0, b1 = bbase + sw1;
 
   la.issue(0, lds, wave);
-  lb.issue(0, lds + kTileBytes, wave);
-  la.issue(1, lds + kStageBytes, wave);
-  lb.issue(1, lds + kStageBytes + kTileBytes, wave);
+  lb.issue(0, lds + 2 * kTileBytes, wave);
+  la.issue(1, lds + kTileBytes, wave);
+  lb.issue(1, lds + 3 * kTileBytes, wave);
   wait_vmem_but_one_slice();
   __builtin_amdgcn_s_barrier();
-  i32x8_t fa[10], fbA[8], fbB[8];
+  i32x8_t fa[9], fbA[8], fbB[8];
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     read_frag_half(fa[f], 0, lds + abase + f * 16 * kBKB + sw0);
     read_frag_half(fa[f], 1, lds + abase + f * 16 * kBKB + sw1);
-    read_frag_half(fbA[f], 0, lds + kTileBytes + bbase + f * 16 * kBKB + sw0);
-    read_frag_half(fbA[f], 1, lds + kTileBytes + bbase + f * 16 * kBKB + sw1);
+    read_frag_half(fbA[f], 0, lds + 2 * kTileBytes + bbase + f * 16 * kBKB + sw0);
+    read_frag_half(fbA[f], 1, lds + 2 * kTileBytes + bbase + f * 16 * kBKB + sw1);
   }
   // Copies take the checked form throughout: with 32-cycle MFMAs the three
   // VALU operations per copy fit in the issue shadow.  The slice count is
@@ -429,15 +436,15 @@ __device__ __forceinline__ void tile_mainloop_fp8(Acc& acc, const Operand& A, co
   const int k_even = (k_slices + 1) & ~1;
   int kt = 0;
   for (; kt + 2 < k_even; kt += 2) {
-    fp8_iter<false, false>(acc, fa, fbA, fbB, lds, kt, abase, bbase, sw0, sw1, la, lb, wave);
-    fp8_iter<true, false>(acc, fa, fbA, fbB, lds, kt + 1, abase, bbase, sw0, sw1, la, lb, wave);
+    fp8_iter<false, false>(acc, fa, fbA, fbB, lds, kt, a0, a1, b0, b1, la, lb, wave);
+    fp8_iter<true, false>(acc, fa, fbA, fbB, lds, kt + 1, a0, a1, b0, b1, la, lb, wave);
   }
   // the last two slices: read the last one's fragments, copy nothing
   slice_barrier();
-  kstep_fp8<false, true, false, false>(acc, fa, fbA, fbB, lds + ((kt + 1) & 1) * kStageBytes, abase,
-                                       bbase, sw0, sw1, la, lb, 0, lds, wave);
-  kstep_fp8<true, false, false, false>(acc, fa, fbB, fbA, lds, abase, bbase, sw0, sw1, la, lb, 0,
-                                       lds, wave);
+  kstep_fp8<false, true, false, false, 1, 0>(acc, fa, fbA, fbB, lds, a0, a1, b0, b1, la, lb, 0,
+                                             wave);
+  kstep_fp8<true, false, false, false, 0, 0>(acc, fa, fbB, fbA, lds, a0, a1, b0, b1, la, lb, 0,
+                                             wave);
   wait_vmem_all();
 }
 
