@@ -275,12 +275,23 @@ int lse_pass(int mode, const T* H, const T* W, const int32_t* y, const uint8_t* 
   return GRPO_OK;
 }
 
+// fp8 operands of the backward's logit recompute (all null on the bf16 / f32 path):
+// the codes and scales of H and W, and room for one chunk of gathered active rows.
+struct Fp8Recompute {
+  const uint8_t* H8 = nullptr;
+  const float* h_scale = nullptr;
+  const uint8_t* W8 = nullptr;
+  const float* w_scale = nullptr;
+  uint8_t* H8_act = nullptr;
+  float* hs_act = nullptr;
+};
+
 template <typename T>
 int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, const float* adv,
              const float* ref_lp, const float* lp, const float* lse, int64_t N, int64_t L,
              int64_t d, int64_t V, float beta, float grad_loss, int64_t chunk,
              const grpo::LogitXform& xf, const grpo::LossVariant& lv, T* dH, float* dW, char* ws,
-             int dtype, hipStream_t s) {
+             int dtype, hipStream_t s, const Fp8Recompute& f8 = Fp8Recompute()) {
   const BwdPlan p = plan_bwd(N, d, V, dtype, chunk);
   int32_t* idx = (int32_t*)(ws + p.o_idx);
   int32_t* cnt = (int32_t*)(ws + p.o_cnt);
@@ -310,11 +321,20 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
                                       lse, L, beta, grad_loss, xf, lv, seq_n, B, H_act, coef,
                                       lse_c, y_c, tgt_c, s));
     GRPO_HIP(grpo::launch_transpose<T>(H_act, p.cpad, d, HT, p.cpad, s));
+    if (f8.H8 != nullptr)
+      GRPO_HIP(grpo::launch_fp8_gather_rows(f8.H8, f8.h_scale, d, idx, cnt, c0, C, (int)p.cpad,
+                                            f8.H8_act, f8.hs_act, s));
     for (int64_t sl = 0; sl < p.nslabs; ++sl) {
       const int64_t v0 = sl * p.vs;
       const int vs_valid = (int)std::min<int64_t>(p.vs, V - v0);
-      GRPO_HIP(grpo::launch_dz<T>(W, H_act, d, V, v0, vs_valid, (int)p.vs, cnt, c0, C,
-                                  (int)p.cpad, xf, coef, lse_c, y_c, tgt_c, dZ, dZT, s));
+      if (f8.W8 != nullptr)
+        GRPO_HIP(grpo::launch_dz<uint8_t>(f8.W8, f8.H8_act, d, V, v0, vs_valid, (int)p.vs, cnt,
+                                          c0, C, (int)p.cpad, xf, f8.w_scale, f8.hs_act, coef,
+                                          lse_c, y_c, tgt_c, (__bf16*)dZ, (__bf16*)dZT, s));
+      else
+        GRPO_HIP(grpo::launch_dz<T>(W, H_act, d, V, v0, vs_valid, (int)p.vs, cnt, c0, C,
+                                    (int)p.cpad, xf, nullptr, nullptr, coef, lse_c, y_c, tgt_c,
+                                    dZ, dZT, s));
       GRPO_HIP(grpo::launch_dh_gemm<T>(WT, p.vpad, v0, vs_valid, dZ, (int)p.vs, d, cnt, c0, C,
                                        (int)p.cpad, (int)p.nsplit, sl == 0 ? 1 : 0, dH_acc, s));
       GRPO_HIP(grpo::launch_dw_gemm<T>(HT, (int)p.cpad, dZT, d, V, v0, vs_valid, cnt, c0, C, dW,
@@ -346,14 +366,17 @@ const char* grpo_last_error(void) { return g_last_error; }
 // The fp8 backward runs the bf16 backward on exact bf16 copies of H and W,
 // kept after the bf16 plan's workspace.
 struct Fp8BwdPlan {
-  size_t o_h, o_w, total;
+  size_t o_h, o_w, o_h8act, o_hsact, total;
 };
 Fp8BwdPlan plan_bwd_fp8(int64_t N, int64_t d, int64_t V, int64_t chunk) {
   Fp8BwdPlan p{};
+  const BwdPlan b = plan_bwd(N, d, V, GRPO_BF16, chunk);
   Carve c;
-  c.off = plan_bwd(N, d, V, GRPO_BF16, chunk).total;
+  c.off = b.total;
   p.o_h = c.take((size_t)(N * d) * 2);
   p.o_w = c.take((size_t)(V * d) * 2);
+  p.o_h8act = c.take((size_t)(b.cpad * d));      // one chunk of active fp8 rows
+  p.o_hsact = c.take((size_t)b.cpad * 4);
   p.total = c.off;
   return p;
 }
@@ -694,8 +717,17 @@ int grpo_loss_bwd_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8
   __bf16* Wb = (__bf16*)(ws + p.o_w);
   GRPO_HIP(grpo::launch_fp8_dequantize(H8, N, d, h_scale, 1, Hb, s));
   GRPO_HIP(grpo::launch_fp8_dequantize(W8, V, d, w_scale, 0, Wb, s));
+  // the logits are recomputed from the fp8 codes (as the forward formed them);
+  // dH and dW come from the bf16 GEMMs on the exact copies
+  Fp8Recompute f8;
+  f8.H8 = H8;
+  f8.h_scale = h_scale;
+  f8.W8 = W8;
+  f8.w_scale = w_scale;
+  f8.H8_act = (uint8_t*)(ws + p.o_h8act);
+  f8.hs_act = (float*)(ws + p.o_hsact);
   return bwd_pass<__bf16>(Hb, Wb, y, mask, adv, ref_lp, lp, lse, N, L, d, V, beta, grad_loss, chunk,
-                          xf, lv, (__bf16*)dH, dW, ws, GRPO_BF16, s);
+                          xf, lv, (__bf16*)dH, dW, ws, GRPO_BF16, s, f8);
 }
 
 int grpo_gemm_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int dtype,

@@ -510,14 +510,19 @@ __device__ __forceinline__ float dz_value(float z, float ct, float lb, int64_t v
   return v < vs_valid ? ct * (onehot - p) * slope : 0.f;
 }
 
+// T = uint8_t: the logits are recomputed from float8 e4m3 codes (w_scale[0] the
+// head's scale, hs_act[j] active token j's), exactly as the fp8 forward formed
+// them, and dZ / dZT are bfloat16; other T ignore both scale pointers.
 template <typename T, bool SC>
 __global__ void __launch_bounds__(kThreads, 1)
     k_dz(const T* __restrict__ W, const T* __restrict__ H_act, int64_t d, int64_t v0,
          int vs_valid, int vs, const int32_t* __restrict__ count, int64_t c0, int C, int cpad,
-         int tm, int tn, LogitXform xf, const float* __restrict__ coef,
+         int tm, int tn, LogitXform xf, const float* __restrict__ w_scale,
+         const float* __restrict__ hs_act, const float* __restrict__ coef,
          const float* __restrict__ lse_c,
-         const int32_t* __restrict__ y_c, const float* __restrict__ tgt_c, T* __restrict__ dZ,
-         T* __restrict__ dZT) {
+         const int32_t* __restrict__ y_c, const float* __restrict__ tgt_c,
+         typename DzOut<T>::type* __restrict__ dZ, typename DzOut<T>::type* __restrict__ dZT) {
+  constexpr bool kFp8 = std::is_same<T, uint8_t>::value;
   __shared__ __attribute__((aligned(1024))) char smem[kDzLdsBytes];
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
   int n_act = count[0] - (int)c0;
@@ -531,10 +536,13 @@ __global__ void __launch_bounds__(kThreads, 1)
   const Operand A{(const char*)(W + (v0 + m0) * d), rowb, vs_valid - m0, rowb};
   const Operand B{(const char*)(H_act + (int64_t)n0 * d), rowb, n_act - n0, rowb};
   Acc acc;
-  tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+  if constexpr (kFp8)
+    tile_mainloop_fp8(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+  else
+    tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
 
   const int lane = threadIdx.x & 63, wave = wave_id();
-  float ct[kWN], lb[kWN];
+  float ct[kWN], lb[kWN], cs[kWN];
   int64_t yl[kWN];
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
@@ -542,8 +550,10 @@ __global__ void __launch_bounds__(kThreads, 1)
     ct[j] = coef[t];
     lb[j] = lse_c[t] * kLog2e;
     yl[j] = (int64_t)y_c[t] - v0;  // target relative to the slab
+    cs[j] = 1.f;                    // accumulator -> logit (fp8 scales; exactly 1 otherwise)
+    if constexpr (kFp8) cs[j] = w_scale[0] * hs_act[t];
   }
-  if (sizeof(T) == 4) {
+  if constexpr (std::is_same<T, float>::value) {
     // float32 (small shapes only): direct stores
 #pragma unroll
     for (int j = 0; j < kWN; ++j) {
@@ -575,15 +585,15 @@ __global__ void __launch_bounds__(kThreads, 1)
       for (int i = 0; i < kWM; ++i)
 #pragma unroll
         for (int e = 0; e < kAcc; ++e) {
-          const float t = tanh_fast(xf.a * acc[i][j][e]);
+          const float t = tanh_fast(xf.a * (acc[i][j][e] * cs[j]));
           acc[i][j][e] = nc * (1.f - t * t) * ex2(fmaf(xf.b * t, kLog2e, -lb[j]));
         }
     }
   } else {
-    const float kl = xf.k * kLog2e;
 #pragma unroll
     for (int j = 0; j < kWN; ++j) {
       const float nc = -ct[j] * xf.k;
+      const float kl = xf.k * kLog2e * cs[j];
 #pragma unroll
       for (int i = 0; i < kWM; ++i)
 #pragma unroll
@@ -978,19 +988,46 @@ hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int3
 template <typename T>
 hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,
                      int vs, const int32_t* count, int64_t c0, int C, int cpad,
-                     const LogitXform& xf, const float* coef, const float* lse_c,
-                     const int32_t* y_c, const float* tgt_c, T* dZ, T* dZT, hipStream_t s) {
+                     const LogitXform& xf, const float* w_scale, const float* hs_act,
+                     const float* coef, const float* lse_c, const int32_t* y_c,
+                     const float* tgt_c, typename DzOut<T>::type* dZ,
+                     typename DzOut<T>::type* dZT, hipStream_t s) {
   ScopedKernelTimer timer_(KK_DZ, s);
   (void)V;
   const int tm = cdiv(vs_valid, kBM), tn = cdiv(C, kBN);
   if (xf.softcap)
     hipLaunchKernelGGL((k_dz<T, true>), dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0,
-                       vs_valid, vs, count, c0, C, cpad, tm, tn, xf, coef, lse_c, y_c, tgt_c, dZ,
-                       dZT);
+                       vs_valid, vs, count, c0, C, cpad, tm, tn, xf, w_scale, hs_act, coef, lse_c,
+                       y_c, tgt_c, dZ, dZT);
   else
     hipLaunchKernelGGL((k_dz<T, false>), dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0,
-                       vs_valid, vs, count, c0, C, cpad, tm, tn, xf, coef, lse_c, y_c, tgt_c, dZ,
-                       dZT);
+                       vs_valid, vs, count, c0, C, cpad, tm, tn, xf, w_scale, hs_act, coef, lse_c,
+                       y_c, tgt_c, dZ, dZT);
+  return hipGetLastError();
+}
+
+// fp8 codes and scales of chunk c's active tokens (zeros past the count).
+__global__ void __launch_bounds__(256)
+    k_fp8_gather_rows(const uint8_t* __restrict__ H8, const float* __restrict__ h_scale,
+                      int64_t d, const int32_t* __restrict__ idx,
+                      const int32_t* __restrict__ count, int64_t c0, int C,
+                      uint8_t* __restrict__ H8_act, float* __restrict__ hs_act) {
+  const int cnt = count[0];
+  const int j = blockIdx.x;
+  const bool valid = j < C && c0 + j < cnt;
+  const int64_t t = valid ? idx[c0 + j] : 0;
+  const int4* src = (const int4*)(H8 + t * d);
+  int4* dst = (int4*)(H8_act + (int64_t)j * d);
+  for (int v = threadIdx.x; v < (int)(d / 16); v += 256) dst[v] = valid ? src[v] : int4{0, 0, 0, 0};
+  if (threadIdx.x == 0) hs_act[j] = valid ? h_scale[t] : 0.f;
+}
+
+hipError_t launch_fp8_gather_rows(const uint8_t* H8, const float* h_scale, int64_t d,
+                                  const int32_t* idx, const int32_t* count, int64_t c0, int C,
+                                  int cpad, uint8_t* H8_act, float* hs_act, hipStream_t s) {
+  ScopedKernelTimer timer_(KK_BWD_PREP, s);
+  hipLaunchKernelGGL(k_fp8_gather_rows, dim3(cpad), dim3(256), 0, s, H8, h_scale, d, idx, count,
+                     c0, C, H8_act, hs_act);
   return hipGetLastError();
 }
 
@@ -1065,8 +1102,8 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
                                          float*, int32_t*, float*, hipStream_t);                  \
   template hipError_t launch_dz<T>(const T*, const T*, int64_t, int64_t, int64_t, int, int,       \
                                    const int32_t*, int64_t, int, int, const LogitXform&,         \
-                                   const float*, const float*, const int32_t*, const float*, T*,  \
-                                   T*, hipStream_t);                                              \
+                                   const float*, const float*, const float*, const float*,        \
+                                   const int32_t*, const float*, T*, T*, hipStream_t);            \
   template hipError_t launch_dh_gemm<T>(const T*, int64_t, int64_t, int, const T*, int, int64_t,  \
                                         const int32_t*, int64_t, int, int, int, int, float*,      \
                                         hipStream_t);                                             \
@@ -1079,6 +1116,11 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
 
 GRPO_INSTANTIATE(float)
 GRPO_INSTANTIATE(__bf16)
+template hipError_t launch_dz<uint8_t>(const uint8_t*, const uint8_t*, int64_t, int64_t, int64_t,
+                                         int, int, const int32_t*, int64_t, int, int,
+                                         const LogitXform&, const float*, const float*,
+                                         const float*, const float*, const int32_t*, const float*,
+                                         __bf16*, __bf16*, hipStream_t);
 template hipError_t launch_lse_partials<uint8_t>(const uint8_t*, const uint8_t*, const int32_t*,
                                                  int64_t, int64_t, int, int, const LogitXform&,
                                                  const float*, const float*, float*, float*,

@@ -257,11 +257,12 @@ int grpo_loss_bwd_ex(const void* H, const void* W, const int32_t* y, const uint8
  *   (w_scale [1]); outputs and workspace (grpo_workspace_bytes with dtype
  *   GRPO_FP8_E4M3) as there.  d must be a multiple of 16.
  * grpo_loss_bwd_fp8: the backward of that loss with respect to the dequantised
- *   H and W: it writes exact bfloat16 copies of them into its workspace
- *   (grpo_workspace_bytes(GRPO_OP_BWD, ..., GRPO_FP8_E4M3, chunk) includes
- *   them) and runs the bfloat16 backward; dH [N, d] is bfloat16.  The
- *   recomputed logits then differ from the forward's only by the order of
- *   float32 summation.
+ *   H and W.  The logits are recomputed from the fp8 codes through the same
+ *   MFMA loop as the forward (so they equal the forward's), and dH = dZ W,
+ *   dW += dZ^T H run in bfloat16 on exact bfloat16 copies of H and W that it
+ *   writes into its workspace (grpo_workspace_bytes(GRPO_OP_BWD, ...,
+ *   GRPO_FP8_E4M3, chunk) includes them and one chunk of gathered fp8 rows);
+ *   dH [N, d] is bfloat16.
  */
 size_t grpo_quantize_fp8_workspace_bytes(void);
 int grpo_quantize_fp8(const void* X, int dtype, int64_t rows, int64_t cols, int per_row,
