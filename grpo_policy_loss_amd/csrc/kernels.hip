@@ -716,6 +716,8 @@ __global__ void __launch_bounds__(kThreads, 1)
   }
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 template <typename T>
 __global__ void __launch_bounds__(kThreads, 1)
     k_dw_gemm(const T* __restrict__ HT, int cpad, const T* __restrict__ dZT, int64_t d,
@@ -737,17 +739,45 @@ __global__ void __launch_bounds__(kThreads, 1)
   Acc acc;
   tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
 
+  // fp32 read-modify-write of the tile's dW rows through a buffer resource
+  // that spans exactly the valid rows: a row past the slab or a column past d
+  // (offset kOOB) loads 0 and drops its store, so there is no branch.  The 8
+  // loads of column block j+1 are in flight while block j is added and
+  // stored: one memory round trip per block instead of one per load.
   const int lane = threadIdx.x & 63, wave = wave_id();
+  const int rows = (vs_valid - n0) < kBN ? (vs_valid - n0) : kBN;
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(dW + (v0 + n0) * d, (uint32_t)((int64_t)rows * d * (int64_t)sizeof(float)));
+  uint32_t coff[kWM];
+#pragma unroll
+  for (int i = 0; i < kWM; ++i) {
+    const int64_t nd = m0 + acc_row(wave, lane, i, 0);   // 4 consecutive d
+    coff[i] = nd < d ? (uint32_t)nd * 4u : kOOB;
+  }
+  auto row_off = [&](int j) { return (uint32_t)acc_col(wave, lane, j) * (uint32_t)d * 4u; };
+  auto at = [](uint32_t r, uint32_t c) { return c == kOOB ? c : r + c; };
+  f32x4_t cur[kWM], nxt[kWM];
+#pragma unroll
+  for (int i = 0; i < kWM; ++i)
+    cur[i] = __builtin_bit_cast(
+        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, at(row_off(0), coff[i]), 0, 0));
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
-    const int v = n0 + acc_col(wave, lane, j);
-    if (v >= vs_valid) continue;
+    if (j + 1 < kWN) {
+      const uint32_t rn = row_off(j + 1);
 #pragma unroll
-    for (int i = 0; i < kWM; ++i) {
-      const int64_t nd = m0 + acc_row(wave, lane, i, 0);   // 4 consecutive d
-      if (nd >= d) continue;
-      f32x4_t* p = (f32x4_t*)(dW + (v0 + v) * d + nd);
-      *p += acc[i][j];
+      for (int i = 0; i < kWM; ++i)
+        nxt[i] = __builtin_bit_cast(
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, at(rn, coff[i]), 0, 0));
+    }
+    const uint32_t r = row_off(j);
+#pragma unroll
+    for (int i = 0; i < kWM; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, cur[i] + acc[i][j]), rs,
+                                             at(r, coff[i]), 0, 0);
+    if (j + 1 < kWN) {
+#pragma unroll
+      for (int i = 0; i < kWM; ++i) cur[i] = nxt[i];
     }
   }
 }
