@@ -665,6 +665,66 @@ __global__ void __launch_bounds__(kThreads, 1)
   }
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Write (accumulate = false) or add (accumulate = true) the tile's fp32
+// accumulators into a row-major [rows x d] block whose tile row r (the GEMM's
+// N index) starts at base + r * d and whose columns are m0 + (the GEMM's M
+// index).  Addressing goes through a buffer resource spanning exactly the
+// valid rows: a row past `rows` or a column past d (offset kOOB) loads 0 and
+// drops its store, so there is no branch.  When accumulating, the 8 loads of
+// column block j+1 are in flight while block j is added and stored: one
+// memory round trip per block instead of one per load.
+__device__ __forceinline__ void store_tile_f32(float* base, int rows, int64_t m0, int64_t d,
+                                               const Acc& acc, bool accumulate) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(base, (uint32_t)((int64_t)rows * d * (int64_t)sizeof(float)));
+  uint32_t coff[kWM];
+#pragma unroll
+  for (int i = 0; i < kWM; ++i) {
+    const int64_t nd = m0 + acc_row(wave, lane, i, 0);   // 4 consecutive d
+    coff[i] = nd < d ? (uint32_t)nd * 4u : kOOB;
+  }
+  auto row_off = [&](int j) { return (uint32_t)acc_col(wave, lane, j) * (uint32_t)d * 4u; };
+  auto at = [](uint32_t r, uint32_t c) { return c == kOOB ? c : r + c; };
+  if (!accumulate) {
+#pragma unroll
+    for (int j = 0; j < kWN; ++j) {
+      const uint32_t r = row_off(j);
+#pragma unroll
+      for (int i = 0; i < kWM; ++i)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[i][j]), rs,
+                                               at(r, coff[i]), 0, 0);
+    }
+    return;
+  }
+  f32x4_t cur[kWM], nxt[kWM];
+#pragma unroll
+  for (int i = 0; i < kWM; ++i)
+    cur[i] = __builtin_bit_cast(
+        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, at(row_off(0), coff[i]), 0, 0));
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    if (j + 1 < kWN) {
+      const uint32_t rn = row_off(j + 1);
+#pragma unroll
+      for (int i = 0; i < kWM; ++i)
+        nxt[i] = __builtin_bit_cast(
+            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, at(rn, coff[i]), 0, 0));
+    }
+    const uint32_t r = row_off(j);
+#pragma unroll
+    for (int i = 0; i < kWM; ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, cur[i] + acc[i][j]), rs,
+                                             at(r, coff[i]), 0, 0);
+    if (j + 1 < kWN) {
+#pragma unroll
+      for (int i = 0; i < kWM; ++i) cur[i] = nxt[i];
+    }
+  }
+}
+
 // dH partial of split `sp`: vocabulary columns [k0, k1) of the slab.  Split
 // sp accumulates into its own buffer dH_acc[sp], so no two workgroups ever
 // write the same element and the final sum over splits has a fixed order.
@@ -698,25 +758,9 @@ __global__ void __launch_bounds__(kThreads, 1)
   tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
   if (klen == 0 && !first) return;
 
-  float* out = dH_acc + (int64_t)sp * cpad * d;
-  const int lane = threadIdx.x & 63, wave = wave_id();
-#pragma unroll
-  for (int j = 0; j < kWN; ++j) {
-    const int t = n0 + acc_col(wave, lane, j);
-    if (t >= n_act) continue;
-#pragma unroll
-    for (int i = 0; i < kWM; ++i) {
-      const int64_t nd = m0 + acc_row(wave, lane, i, 0);   // 4 consecutive d
-      if (nd >= d) continue;
-      f32x4_t* p = (f32x4_t*)(out + (int64_t)t * d + nd);
-      f32x4_t v = acc[i][j];
-      if (!first) v += *p;
-      *p = v;
-    }
-  }
+  const int rows = (n_act - n0) < kBN ? (n_act - n0) : kBN;
+  store_tile_f32(dH_acc + ((int64_t)sp * cpad + n0) * d, rows, m0, d, acc, !first);
 }
-
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __global__ void __launch_bounds__(kThreads, 1)
@@ -739,47 +783,8 @@ __global__ void __launch_bounds__(kThreads, 1)
   Acc acc;
   tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
 
-  // fp32 read-modify-write of the tile's dW rows through a buffer resource
-  // that spans exactly the valid rows: a row past the slab or a column past d
-  // (offset kOOB) loads 0 and drops its store, so there is no branch.  The 8
-  // loads of column block j+1 are in flight while block j is added and
-  // stored: one memory round trip per block instead of one per load.
-  const int lane = threadIdx.x & 63, wave = wave_id();
   const int rows = (vs_valid - n0) < kBN ? (vs_valid - n0) : kBN;
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(dW + (v0 + n0) * d, (uint32_t)((int64_t)rows * d * (int64_t)sizeof(float)));
-  uint32_t coff[kWM];
-#pragma unroll
-  for (int i = 0; i < kWM; ++i) {
-    const int64_t nd = m0 + acc_row(wave, lane, i, 0);   // 4 consecutive d
-    coff[i] = nd < d ? (uint32_t)nd * 4u : kOOB;
-  }
-  auto row_off = [&](int j) { return (uint32_t)acc_col(wave, lane, j) * (uint32_t)d * 4u; };
-  auto at = [](uint32_t r, uint32_t c) { return c == kOOB ? c : r + c; };
-  f32x4_t cur[kWM], nxt[kWM];
-#pragma unroll
-  for (int i = 0; i < kWM; ++i)
-    cur[i] = __builtin_bit_cast(
-        f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, at(row_off(0), coff[i]), 0, 0));
-#pragma unroll
-  for (int j = 0; j < kWN; ++j) {
-    if (j + 1 < kWN) {
-      const uint32_t rn = row_off(j + 1);
-#pragma unroll
-      for (int i = 0; i < kWM; ++i)
-        nxt[i] = __builtin_bit_cast(
-            f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, at(rn, coff[i]), 0, 0));
-    }
-    const uint32_t r = row_off(j);
-#pragma unroll
-    for (int i = 0; i < kWM; ++i)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, cur[i] + acc[i][j]), rs,
-                                             at(r, coff[i]), 0, 0);
-    if (j + 1 < kWN) {
-#pragma unroll
-      for (int i = 0; i < kWM; ++i) cur[i] = nxt[i];
-    }
-  }
+  store_tile_f32(dW + (v0 + n0) * d, rows, m0, d, acc, true);
 }
 
 template <typename T>
