@@ -281,11 +281,22 @@ __device__ __forceinline__ float kl_slope(int kl, float x, float lp) {
 }
 
 // ---------------------------------------------------------------- forward merge
-// 256 threads = 32 tokens x 8 splits of the vocabulary-tile partials.  Split q
-// folds partials q, q + 8, ... of its token in order; the 8 split results are
-// then folded in order 0..7, so the result is independent of timing.
+// 256 threads = 16 tokens x 16 splits of the vocabulary-tile partials (256
+// workgroups per 4096 tokens, so every CU gets one).  Split q folds partials
+// q, q + 16, ... of its token in order, loading four at a time; the 16 split
+// results are then folded in order 0..15, so the result is independent of
+// timing.
 constexpr int kMergeTok = kMergeTokens;
-constexpr int kMergeSplit = 8;
+constexpr int kMergeSplit = 256 / kMergeTok;
+
+__device__ __forceinline__ void lse_fold(float& M, float& Ssum, float m, float v) {
+  if (m > M) {
+    Ssum = Ssum * exp2f((M - m) * kLog2e) + v;
+    M = m;
+  } else {
+    Ssum += v * exp2f((m - M) * kLog2e);
+  }
+}
 
 __global__ void __launch_bounds__(256)
     k_lse_merge(int mode, const float* __restrict__ part_m, const float* __restrict__ part_s,
@@ -300,21 +311,25 @@ __global__ void __launch_bounds__(256)
   const int t = blockIdx.x * kMergeTok + tt;
   float M = kNegInf, Ssum = 0.f;
   if (t < n_tok) {
-    for (int s = q; s < S; s += kMergeSplit) {
-      const float m = part_m[(int64_t)s * cpad + t];
-      const float v = part_s[(int64_t)s * cpad + t];
-      if (m > M) {
-        Ssum = Ssum * exp2f((M - m) * kLog2e) + v;
-        M = m;
-      } else {
-        Ssum += v * exp2f((m - M) * kLog2e);
+    const float* pm = part_m + t;
+    const float* ps = part_s + t;
+    int sp = q;
+    for (; sp + 3 * kMergeSplit < S; sp += 4 * kMergeSplit) {
+      float m4[4], v4[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m4[u] = pm[(int64_t)(sp + u * kMergeSplit) * cpad];
+        v4[u] = ps[(int64_t)(sp + u * kMergeSplit) * cpad];
       }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) lse_fold(M, Ssum, m4[u], v4[u]);
     }
+    for (; sp < S; sp += kMergeSplit) lse_fold(M, Ssum, pm[(int64_t)sp * cpad], ps[(int64_t)sp * cpad]);
   }
   sm_m[q][tt] = M;
   sm_s[q][tt] = Ssum;
   __syncthreads();
-  // split 0 (lanes 0..31 of wave 0) finishes its token; waves 1..3 are done
+  // split 0 (lanes 0..15 of wave 0) finishes its token; waves 1..3 are done
   if (threadIdx.x >= 64) return;
   double ml = 0.0;
   int cnt = 0;
@@ -341,7 +356,7 @@ __global__ void __launch_bounds__(256)
     }
   }
   if (mode == 1) {
-    // fixed-order butterfly over wave 0 (lanes 32..63 contribute 0)
+    // fixed-order butterfly over wave 0 (lanes 16..63 contribute 0)
     ml = wave_sum(ml);
     cnt = wave_sum(cnt);
     if (threadIdx.x == 0) {
@@ -416,22 +431,40 @@ __global__ void __launch_bounds__(1024)
   if (tid == 1023) count[0] = sc[1023];
 }
 
-// out[c][r] = in[r][c] for r < R; out[c][r] = 0 for R <= r < Rpad.
+// out[c][r] = in[r][c] for r < R; out[c][r] = 0 for R <= r < Rpad.  One
+// workgroup moves a 64 x 64 block with 16-byte accesses on both sides: rows
+// of `in` are read 16 B per lane into LDS, and each lane then gathers 16 B
+// worth of one column (E consecutive r) and writes it as one store.  Needs
+// Cc and Rpad to be multiples of E = 16 / sizeof(T) (the host checks d).
 template <typename T>
 __global__ void __launch_bounds__(256)
     k_transpose(const T* __restrict__ in, int64_t R, int64_t Cc, T* __restrict__ out,
                 int64_t Rpad) {
-  __shared__ T tile[64][65];
+  constexpr int E = 16 / (int)sizeof(T);   // elements per 16 B
+  constexpr int LPR = 64 / E;              // lanes per 64-element row
+  constexpr int RPP = 256 / LPR;           // rows per pass
+  constexpr int P = 64 + 2;                // LDS row pitch (elements)
+  __shared__ T tile[64 * P];
   const int64_t r0 = (int64_t)blockIdx.x * 64, c0 = (int64_t)blockIdx.y * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t rr = r0 + r, cc = c0 + tx;
-    tile[r][tx] = (rr < R && cc < Cc) ? in[rr * Cc + cc] : to_elem<T>(0.f);
+  const int lx = threadIdx.x % LPR, ly = threadIdx.x / LPR;
+#pragma unroll
+  for (int r = ly; r < 64; r += RPP) {
+    const int64_t rr = r0 + r, cc = c0 + lx * E;
+    int4 v = {0, 0, 0, 0};
+    if (rr < R && cc < Cc) v = *(const int4*)(in + rr * Cc + cc);
+    const T* e = (const T*)&v;
+#pragma unroll
+    for (int k = 0; k < E; ++k) tile[r * P + lx * E + k] = e[k];
   }
   __syncthreads();
-  for (int c = ty; c < 64; c += 4) {
-    const int64_t cc = c0 + c, rr = r0 + tx;
-    if (cc < Cc && rr < Rpad) out[cc * Rpad + rr] = tile[tx][c];
+#pragma unroll
+  for (int c = ly; c < 64; c += RPP) {
+    const int64_t cc = c0 + c, rr = r0 + lx * E;
+    int4 v;
+    T* e = (T*)&v;
+#pragma unroll
+    for (int k = 0; k < E; ++k) e[k] = tile[(lx * E + k) * P + c];
+    if (cc < Cc && rr < Rpad) *(int4*)(out + cc * Rpad + rr) = v;
   }
 }
 

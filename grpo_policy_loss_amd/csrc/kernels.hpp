@@ -7,7 +7,7 @@
 namespace grpo {
 
 // Tokens per block of the forward merge kernel (one loss partial per block).
-constexpr int kMergeTokens = 32;
+constexpr int kMergeTokens = 16;
 
 // Logit transform applied to every z = h . w before the log-softmax:
 //   without a cap:  z' = k z                      (k = scale / temperature)
