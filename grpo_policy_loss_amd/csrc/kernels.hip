@@ -58,16 +58,11 @@ __device__ __forceinline__ void lse_combine(float& m, float& s, float m2, float 
   m = M;
 }
 
-// Hardware dispatches workgroup b to XCD b % 8.  Remap so that XCD x
-// receives a contiguous range of logical tile ids, then order the logical
-// ids in groups of 4 M-tiles (M fastest), so the ~32 workgroups resident on
-// one XCD share 4 A-panels and ~8 B-panels in that XCD's L2.
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tm, int tn, int& mt,
-                                            int& nt) {
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int q = nblocks >> 3, r = nblocks & 7;
-  const int p = xcd * q + (xcd < r ? xcd : r) + slot;
-  constexpr int GM = 4;
+// Logical tile id p -> (M-tile, N-tile), in groups of GM M-tiles (M
+// fastest), so the ~32 workgroups resident on one XCD share GM A-panels and
+// ~32/GM B-panels in that XCD's L2.
+template <int GM>
+__device__ __forceinline__ void group_coords(int p, int tm, int tn, int& mt, int& nt) {
   const int per_group = GM * tn;
   const int g = p / per_group;
   const int first = g * GM;
@@ -75,6 +70,17 @@ __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tm, int tn
   const int rem = p - g * per_group;
   mt = first + rem % gm;
   nt = rem / gm;
+}
+
+// Hardware dispatches workgroup b to XCD b % 8.  Remap so that XCD x
+// receives a contiguous range of logical tile ids, then order them in
+// groups of 4 M-tiles: the ~32 workgroups resident on one XCD share 4
+// A-panels and ~8 B-panels.
+__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tm, int tn, int& mt,
+                                            int& nt) {
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int q = nblocks >> 3, r = nblocks & 7;
+  group_coords<4>(xcd * q + (xcd < r ? xcd : r) + slot, tm, tn, mt, nt);
 }
 
 template <typename T>
@@ -129,33 +135,21 @@ __global__ void __launch_bounds__(64) k_advantages(const float* __restrict__ r, 
 }
 
 // ---------------------------------------------------------------- forward tile
-// T = uint8_t: float8 e4m3 codes, with w_scale[0] the head's scale and h_scale[t]
-// each token's (the logit is acc * w_scale * h_scale[t]); other T ignore both.
+// Epilogue of one forward tile (vocabulary rows [m0, m0 + mvalid), tokens
+// [n0, n0 + 256) of the chunk): fold the accumulators into one (max, sum exp)
+// pair per token for this vocabulary tile and pick the target logits.  yv[j]
+// is the target of this lane's token column j (any value when the token is
+// past n_tok); `red` is 512 floats of workgroup memory the main loop does not
+// use.  Contains two workgroup barriers.
 template <typename T, bool SC>
-__global__ void __launch_bounds__(kThreads, 1)
-    k_lse_partials(const T* __restrict__ W, const T* __restrict__ H, const int32_t* __restrict__ y,
-                   int64_t V, int64_t d, int n_tok, int cpad, int tm, int tn, LogitXform xf,
-                   const float* __restrict__ w_scale, const float* __restrict__ h_scale,
-                   float* __restrict__ part_m, float* __restrict__ part_s,
-                   float* __restrict__ zy) {
+__device__ __forceinline__ void lse_epilogue(const Acc& acc, int mt, int64_t m0, int mvalid,
+                                             int n0, int n_tok, int cpad, const LogitXform& xf,
+                                             const float* __restrict__ w_scale,
+                                             const float* __restrict__ h_scale,
+                                             const int (&yv)[kWN], float* red,
+                                             float* __restrict__ part_m,
+                                             float* __restrict__ part_s, float* __restrict__ zy) {
   constexpr bool kFp8 = std::is_same<T, uint8_t>::value;
-  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
-  char GRPO_LDS* lds = (char GRPO_LDS*)smem;
-  int mt, nt;
-  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
-  const int64_t m0 = (int64_t)mt * kBM;  // first vocab row
-  const int n0 = nt * kBN;               // first token (chunk-local)
-  const uint32_t rowb = (uint32_t)(d * (int64_t)sizeof(T));
-  const int mvalid = (int)((V - m0) < kBM ? (V - m0) : kBM);
-  const Operand A{(const char*)(W + m0 * d), rowb, mvalid, rowb};
-  const Operand B{(const char*)(H + (int64_t)n0 * d), rowb, n_tok - n0, rowb};
-
-  Acc acc;
-  if constexpr (kFp8)
-    tile_mainloop_fp8(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
-  else
-    tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
-
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm0 = (wave >> 1) * 128;
   const bool full = mvalid >= wm0 + 128;
@@ -220,7 +214,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   for (int j = 0; j < kWN; ++j) {
     const int t = n0 + acc_col(wave, lane, j);
     if (t < n_tok) {
-      const int r = y[t] - (int)(m0 + wm0);
+      const int r = yv[j] - (int)(m0 + wm0);
       if (r >= 0 && r < 128 && r < mvalid - wm0 && ((r >> 2) & 3) == (lane >> 4)) {
         const int ti = r >> 4, te = r & 3;
         float v = 0.f;
@@ -236,7 +230,6 @@ __global__ void __launch_bounds__(kThreads, 1)
 
   // combine the two waves that share token columns (w and w + 2), through LDS
   __syncthreads();
-  float* red = (float*)smem;  // [256 token columns] max, then [256] sums
   if ((wave >> 1) == 1 && lane < 16) {
 #pragma unroll
     for (int j = 0; j < kWN; ++j) {
@@ -258,6 +251,49 @@ __global__ void __launch_bounds__(kThreads, 1)
       }
     }
   }
+}
+
+// Targets of this lane's token columns.
+__device__ __forceinline__ void load_targets(const int32_t* __restrict__ y, int n0, int n_tok,
+                                             int (&yv)[kWN]) {
+  const int lane = threadIdx.x & 63, wave = wave_id();
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    const int t = n0 + acc_col(wave, lane, j);
+    yv[j] = t < n_tok ? y[t] : -1;
+  }
+}
+
+// T = uint8_t: float8 e4m3 codes, with w_scale[0] the head's scale and h_scale[t]
+// each token's (the logit is acc * w_scale * h_scale[t]); other T ignore both.
+template <typename T, bool SC>
+__global__ void __launch_bounds__(kThreads, 1)
+    k_lse_partials(const T* __restrict__ W, const T* __restrict__ H, const int32_t* __restrict__ y,
+                   int64_t V, int64_t d, int n_tok, int cpad, int tm, int tn, LogitXform xf,
+                   const float* __restrict__ w_scale, const float* __restrict__ h_scale,
+                   float* __restrict__ part_m, float* __restrict__ part_s,
+                   float* __restrict__ zy) {
+  constexpr bool kFp8 = std::is_same<T, uint8_t>::value;
+  __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
+  char GRPO_LDS* lds = (char GRPO_LDS*)smem;
+  int mt, nt;
+  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  const int64_t m0 = (int64_t)mt * kBM;  // first vocab row
+  const int n0 = nt * kBN;               // first token (chunk-local)
+  const uint32_t rowb = (uint32_t)(d * (int64_t)sizeof(T));
+  const int mvalid = (int)((V - m0) < kBM ? (V - m0) : kBM);
+  const Operand A{(const char*)(W + m0 * d), rowb, mvalid, rowb};
+  const Operand B{(const char*)(H + (int64_t)n0 * d), rowb, n_tok - n0, rowb};
+
+  Acc acc;
+  if constexpr (kFp8)
+    tile_mainloop_fp8(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+  else
+    tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+  int yv[kWN];
+  load_targets(y, n0, n_tok, yv);
+  lse_epilogue<T, SC>(acc, mt, m0, mvalid, n0, n_tok, cpad, xf, w_scale, h_scale, yv,
+                      (float*)smem, part_m, part_s, zy);
 }
 
 // ---------------------------------------------------------------- per-token KL
