@@ -134,6 +134,79 @@ __global__ void __launch_bounds__(64) k_advantages(const float* __restrict__ r, 
     adv[base + i] = (float)(((double)r[base + i] - mean) / (sd + (double)eps));
 }
 
+// Reductions over the four 16-lane groups of a wave (lane l with l ^ 16,
+// l ^ 32, l ^ 48) through the VALU lane swaps, with no LDS round trip.  The
+// swaps hand every lane the same pair in the same order, so all lanes end with
+// the same bits.
+__device__ __forceinline__ float bits_f(unsigned u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ unsigned f_bits(float f) { return __builtin_bit_cast(unsigned, f); }
+__device__ __forceinline__ float group4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
+  x = __builtin_elementwise_maximum(bits_f(a[0]), bits_f(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
+  return __builtin_elementwise_maximum(bits_f(b[0]), bits_f(b[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
+  x = bits_f(a[0]) + bits_f(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(f_bits(x), f_bits(x), false, false);
+  return bits_f(b[0]) + bits_f(b[1]);
+}
+
+// (max, sum exp) of the transformed logits of every token column of this
+// wave, over the wave's 128 vocabulary rows.  ROWS: rows at or past `mvalid`
+// (tile-relative) are left out; otherwise every row counts and the loops have
+// no per-element test.  cs[j] turns the accumulator into the logit (fp8
+// scales; exactly 1 otherwise).  mx[j] is the transformed max (-inf when no
+// row counts), sm[j] the sum of exp(logit - mx[j]).
+template <bool SC, bool ROWS>
+__device__ __forceinline__ void lse_columns(const Acc& acc, int wave, int lane, int mvalid,
+                                            const float (&cs)[kWN], const LogitXform& xf,
+                                            float (&mx)[kWN], float (&sm)[kWN]) {
+  auto valid = [&](int i, int e) { return !ROWS || acc_row(wave, lane, i, e) < mvalid; };
+  // one token column at a time, so only its 32 values are live in VGPRs
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    // the max: two independent chains of three-input maxima (v_maximum3_f32,
+    // which needs no canonicalisation of its inputs)
+    float ma = kNegInf, mb = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kWM; ++i) {
+      const float a0 = valid(i, 0) ? acc[i][j][0] : kNegInf;
+      const float a1 = valid(i, 1) ? acc[i][j][1] : kNegInf;
+      const float a2 = valid(i, 2) ? acc[i][j][2] : kNegInf;
+      const float a3 = valid(i, 3) ? acc[i][j][3] : kNegInf;
+      if (i == 0) {
+        ma = __builtin_elementwise_maximum(a0, a1);
+        mb = __builtin_elementwise_maximum(a2, a3);
+      } else {
+        ma = __builtin_elementwise_maximum(__builtin_elementwise_maximum(ma, a0), a1);
+        mb = __builtin_elementwise_maximum(__builtin_elementwise_maximum(mb, a2), a3);
+      }
+    }
+    const float m = group4_max(__builtin_elementwise_maximum(ma, mb));
+    const float mt = m == kNegInf ? kNegInf : xform<SC>(m * cs[j], xf);
+    const float mbase = mt * kLog2e;
+    // the sum: four partial sums keep four exps in flight
+    float s[kAcc] = {0.f, 0.f, 0.f, 0.f};
+    if (!ROWS || mt != kNegInf) {
+      const float kl = xf.k * kLog2e * cs[j];
+#pragma unroll
+      for (int i = 0; i < kWM; ++i)
+#pragma unroll
+        for (int e = 0; e < kAcc; ++e) {
+          const float z = acc[i][j][e];
+          const float p = SC ? ex2(fmaf(xform<true>(z * cs[j], xf), kLog2e, -mbase))
+                             : ex2(fmaf(z, kl, -mbase));
+          if (valid(i, e)) s[e] = i == 0 ? p : s[e] + p;
+        }
+    }
+    mx[j] = mt;
+    sm[j] = group4_sum((s[0] + s[1]) + (s[2] + s[3]));
+  }
+}
+
+
 // ---------------------------------------------------------------- forward tile
 // Epilogue of one forward tile (vocabulary rows [m0, m0 + mvalid), tokens
 // [n0, n0 + 256) of the chunk): fold the accumulators into one (max, sum exp)
@@ -165,49 +238,16 @@ __device__ __forceinline__ void lse_epilogue(const Acc& acc, int mt, int64_t m0,
     }
   }
 
-  // per token column j of this lane: (max, sum exp) of the transformed logits
-  // over its 32 vocabulary rows.  The transform is increasing, so the max of
-  // the transformed logits is the transform of the raw max.
+  // per token column j: (max, sum exp) of the transformed logits over the
+  // wave's 128 vocabulary rows (32 per lane, the four 16-lane groups hold the
+  // rest).  The transform is increasing, so the max of the transformed logits
+  // is the transform of the raw max.  The max is reduced over the wave first,
+  // so every exp already uses the wave's shift and nothing is rescaled.
   float mx[kWN], sm[kWN];
-#pragma unroll
-  for (int j = 0; j < kWN; ++j) {
-    float m = kNegInf;
-#pragma unroll
-    for (int i = 0; i < kWM; ++i)
-#pragma unroll
-      for (int e = 0; e < kAcc; ++e)
-        if (full || acc_row(wave, lane, i, e) < mvalid) m = fmaxf(m, acc[i][j][e]);
-    const float mt = m == kNegInf ? kNegInf : xform<SC>(m * cs[j], xf);
-    const float mb = mt * kLog2e;
-    float s = 0.f;
-    if (SC) {
-#pragma unroll
-      for (int i = 0; i < kWM; ++i)
-#pragma unroll
-        for (int e = 0; e < kAcc; ++e)
-          if (full || acc_row(wave, lane, i, e) < mvalid)
-            s += ex2(fmaf(xform<true>(acc[i][j][e] * cs[j], xf), kLog2e, -mb));
-    } else {
-      const float kl = xf.k * kLog2e * cs[j];
-#pragma unroll
-      for (int i = 0; i < kWM; ++i)
-#pragma unroll
-        for (int e = 0; e < kAcc; ++e)
-          if (full || acc_row(wave, lane, i, e) < mvalid) s += ex2(fmaf(acc[i][j][e], kl, -mb));
-    }
-    mx[j] = mt;
-    sm[j] = s;
-  }
-  // the four 16-lane groups of a wave hold the same token columns
-#pragma unroll
-  for (int j = 0; j < kWN; ++j) {
-#pragma unroll
-    for (int o = 16; o <= 32; o <<= 1) {
-      const float om = __shfl_xor(mx[j], o, 64);
-      const float os = __shfl_xor(sm[j], o, 64);
-      lse_combine(mx[j], sm[j], om, os);
-    }
-  }
+  if (full)
+    lse_columns<SC, false>(acc, wave, lane, mvalid, cs, xf, mx, sm);
+  else
+    lse_columns<SC, true>(acc, wave, lane, mvalid, cs, xf, mx, sm);
 
   // target logit: exactly one lane of the grid holds z[t][y_t]
 #pragma unroll
@@ -579,6 +619,41 @@ __device__ __forceinline__ float dz_value(float z, float ct, float lb, int64_t v
   return v < vs_valid ? ct * (onehot - p) * slope : 0.f;
 }
 
+// Stage -c_t p f'(z) of every accumulator entry of this lane as bf16 into the
+// [token][vocabulary] LDS tile (pitch kStagePitch).  ROWS: vocabulary rows at
+// or past `rows` (tile-relative) are written as 0; otherwise no per-element
+// test.  Values go from the accumulators straight to packed bf16 in VGPRs.
+template <bool SC, bool ROWS>
+__device__ __forceinline__ void dz_stage(const Acc& acc, int wave, int lane, int rows,
+                                         const float (&ct)[kWN], const float (&lb)[kWN],
+                                         const float (&cs)[kWN], const LogitXform& xf,
+                                         char GRPO_LDS* lds) {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+#pragma unroll
+  for (int j = 0; j < kWN; ++j) {
+    const int tl = acc_col(wave, lane, j);
+    const float nc = SC ? -ct[j] * xf.a * xf.b : -ct[j] * xf.k;
+    const float kl = xf.k * kLog2e * cs[j];
+#pragma unroll
+    for (int i = 0; i < kWM; ++i) {
+      const int vl = acc_row(wave, lane, i, 0);
+      float q[kAcc];
+#pragma unroll
+      for (int e = 0; e < kAcc; ++e) {
+        if (SC) {
+          const float t = tanh_fast(xf.a * (acc[i][j][e] * cs[j]));
+          q[e] = nc * (1.f - t * t) * ex2(fmaf(xf.b * t, kLog2e, -lb[j]));
+        } else {
+          q[e] = nc * ex2(fmaf(acc[i][j][e], kl, -lb[j]));
+        }
+        if (ROWS && vl + e >= rows) q[e] = 0.f;
+      }
+      *(bf16x4_t GRPO_LDS*)(lds + tl * kStagePitch + vl * 2) =
+          bf16x4_t{(__bf16)q[0], (__bf16)q[1], (__bf16)q[2], (__bf16)q[3]};
+    }
+  }
+}
+
 // T = uint8_t: the logits are recomputed from float8 e4m3 codes (w_scale[0] the
 // head's scale, hs_act[j] active token j's), exactly as the fp8 forward formed
 // them, and dZ / dZT are bfloat16; other T ignore both scale pointers.
@@ -641,68 +716,28 @@ __global__ void __launch_bounds__(kThreads, 1)
     }
     return;
   }
-  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
   typedef __attribute__((ext_vector_type(4))) int i32x4_t;
   typedef __attribute__((ext_vector_type(4))) short s16x4_t;
   typedef __attribute__((ext_vector_type(8))) short s16x8_t;
-  // 1. every entry as if it were not the target, in place: -c_t p f'(z)
-  if (SC) {
-#pragma unroll
-    for (int j = 0; j < kWN; ++j) {
-      const float nc = -ct[j] * xf.a * xf.b;
-#pragma unroll
-      for (int i = 0; i < kWM; ++i)
-#pragma unroll
-        for (int e = 0; e < kAcc; ++e) {
-          const float t = tanh_fast(xf.a * (acc[i][j][e] * cs[j]));
-          acc[i][j][e] = nc * (1.f - t * t) * ex2(fmaf(xf.b * t, kLog2e, -lb[j]));
-        }
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < kWN; ++j) {
-      const float nc = -ct[j] * xf.k;
-      const float kl = xf.k * kLog2e * cs[j];
-#pragma unroll
-      for (int i = 0; i < kWM; ++i)
-#pragma unroll
-        for (int e = 0; e < kAcc; ++e) acc[i][j][e] = nc * ex2(fmaf(acc[i][j][e], kl, -lb[j]));
-    }
-  }
-  if (m0 + kBM > vs_valid) {
-    // ragged last vocabulary tile of the slab: rows past it hold zeros
-#pragma unroll
-    for (int i = 0; i < kWM; ++i)
-#pragma unroll
-      for (int e = 0; e < kAcc; ++e)
-        if (m0 + acc_row(wave, lane, i, e) >= vs_valid) {
-#pragma unroll
-          for (int j = 0; j < kWN; ++j) acc[i][j][e] = 0.f;
-        }
-  }
-  // 2. stage the tile as bf16 [token][vocab]: each lane holds 4 consecutive
-  // vocabulary rows of one token per block
+  // 1. every entry as if it were not the target, -c_t p f'(z), rounded to bf16
+  // and staged as [token][vocab]: each lane holds 4 consecutive vocabulary rows
+  // of one token per block.  Rows past the slab (ragged last vocabulary tile)
+  // hold zeros.  The barrier first: other waves may still read the main loop's
+  // operands from LDS.
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kWN; ++j) {
-    const int tl = acc_col(wave, lane, j);
-#pragma unroll
-    for (int i = 0; i < kWM; ++i) {
-      const int vl = acc_row(wave, lane, i, 0);
-      *(bf16x4_t GRPO_LDS*)(lds + tl * kStagePitch + vl * 2) =
-          bf16x4_t{(__bf16)acc[i][j][0], (__bf16)acc[i][j][1], (__bf16)acc[i][j][2],
-                   (__bf16)acc[i][j][3]};
-    }
-  }
+  if (m0 + kBM > vs_valid)
+    dz_stage<SC, true>(acc, wave, lane, vs_valid - m0, ct, lb, cs, xf, lds);
+  else
+    dz_stage<SC, false>(acc, wave, lane, vs_valid - m0, ct, lb, cs, xf, lds);
   __syncthreads();
-  // 3. the target entry of each token, c_t (1 - p_y) f'(z_y), if it falls in this tile
+  // 2. the target entry of each token, c_t (1 - p_y) f'(z_y), if it falls in this tile
   for (int tl = (int)threadIdx.x; tl < kBN; tl += kThreads) {
     const int64_t yr = (int64_t)y_c[n0 + tl] - v0 - m0;  // y_c = -1 for padding tokens
     if (yr >= 0 && yr < kBM && m0 + yr < vs_valid)
       *(__bf16 GRPO_LDS*)(lds + tl * kStagePitch + yr * 2) = (__bf16)tgt_c[n0 + tl];
   }
   __syncthreads();
-  // 4. dZ rows (token-major, vocabulary contiguous), 16 bytes per thread
+  // 3. dZ rows (token-major, vocabulary contiguous), 16 bytes per thread
 #pragma unroll 8
   for (int it = 0; it < kBN * 32 / kThreads; ++it) {
     const int idx = it * kThreads + (int)threadIdx.x;
@@ -710,7 +745,7 @@ __global__ void __launch_bounds__(kThreads, 1)
     *(i32x4_t*)(dZ + (int64_t)(n0 + r) * vs + m0 + c * 8) =
         *(const i32x4_t GRPO_LDS*)(lds + r * kStagePitch + c * 16);
   }
-  // 5. dZT rows (vocabulary-major, token contiguous) through transposed LDS reads.
+  // 4. dZT rows (vocabulary-major, token contiguous) through transposed LDS reads.
   // A 16-lane group moves one unit of 4 vocabulary rows x 32 tokens: lane m reads
   // the 4 entries (4 vocabulary rows) of token 8 (m & 3) + (m >> 2) (and of the
   // token 4 further), and ds_read_b64_tr_b16 hands lane m the 4 consecutive tokens
