@@ -122,6 +122,49 @@ def summarize_traffic(fetch_csv, write_csv, workload, kernel="lse_partials"):
     print(path)
 
 
+def summarize_stats(stats_csv, workload, steps, warmup):
+    """Turn a `rocprofv3 --kernel-trace --stats` run of this benchmark into
+    profiles/kernel_stats_<workload>.md (per-kernel calls, average and total
+    time, share of GPU time), with the command that made it."""
+    import workloads
+
+    w = workloads.BY_NAME[workload]
+    rows = []
+    for r in csv.DictReader(open(stats_csv)):
+        name = r["Name"]
+        m = re.search(r"(k_[a-z0-9_]+)", name)
+        short = m.group(1) if m else None
+        rows.append((short, name, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                     float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    ours = [r for r in rows if r[0] is not None]
+    other_ms = sum(r[4] for r in rows if r[0] is None)
+    other_pct = sum(r[5] for r in rows if r[0] is None)
+    ours.sort(key=lambda r: -r[4])
+    lines = [f"# Kernel trace statistics: full step on the {workload} workload ({w.dtype})", "",
+             f"Workload: {w.N:,} flattened tokens ({w.prompts} prompts x {w.G} generations x {w.L}), "
+             f"d = {w.d}, V = {w.V:,}, chunk {w.chunk}; one step = advantages + reference "
+             f"log-probs + loss forward + loss backward. {steps} timed steps plus {warmup} "
+             f"warm-up (each library kernel's launches appear {steps + warmup} times).", "",
+             "Command (repo root on the GPU box, `R` = repo root):", "", "```",
+             "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv \\",
+             f"    -d $R/gpurun_out/prof -o bench -- python3 $R/bench.py --workload {workload} "
+             f"--steps {steps} --warmup {warmup} --no-cpu-baseline",
+             f"python3 $R/bench.py --summarize-stats $R/gpurun_out/prof/bench_kernel_stats.csv "
+             f"--workload {workload} --steps {steps} --warmup {warmup}",
+             "```", "",
+             "| kernel | calls | average (us) | total (ms) | share of GPU time |",
+             "|---|---|---|---|---|"]
+    for short, _, calls, avg, tot, pct in ours:
+        lines.append(f"| `{short}` | {calls} | {avg:.1f} | {tot:.2f} | {pct:.2f}% |")
+    lines.append(f"| (torch input generation, copies, fills) | | | {other_ms:.2f} | {other_pct:.2f}% |")
+    lines.append("")
+    lines.append("source_hash: " + kernel_source_hash())
+    path = os.path.join(PROFILES, f"kernel_stats_{workload}.md")
+    with open(path, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def alg_flops(kind, d, V, N, N_act):
     """Algorithmic MFMA flops of one step's launches of a kernel kind."""
     if kind == "lse_partials":          # reference pass + loss forward: 2 d V per token each
@@ -208,6 +251,9 @@ def main():
                     help="run a 1 GiB calibration copy and one reference pass, then exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two counter runs of --traffic-probe")
+    ap.add_argument("--summarize-stats", metavar="STATS_CSV",
+                    help="write the kernel statistics summary from a rocprofv3 --stats run of "
+                         "this benchmark (with the --workload/--steps/--warmup it ran with)")
     args = ap.parse_args()
     xopts = {k: v for k, v in (("logit_scale_multiply", args.scale_multiply),
                                ("logit_scale_divide", args.scale_divide),
@@ -216,6 +262,10 @@ def main():
                                ("kl_estimator", args.kl_estimator),
                                ("no_detach", int(args.no_detach)),
                                ("aggregation", int(args.sequence_mean))) if v} or None
+
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.workload, args.steps, args.warmup)
+        return
 
     if args.summarize_traffic:
         summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload)
