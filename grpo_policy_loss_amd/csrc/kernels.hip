@@ -737,13 +737,15 @@ __global__ void __launch_bounds__(kThreads, 1)
       *(__bf16 GRPO_LDS*)(lds + tl * kStagePitch + yr * 2) = (__bf16)tgt_c[n0 + tl];
   }
   __syncthreads();
-  // 3. dZ rows (token-major, vocabulary contiguous), 16 bytes per thread
+  // 3. dZ rows (token-major, vocabulary contiguous), 16 bytes per thread.  The
+  // slab (1-2 GB) is read back only after the whole launch, so its stores are
+  // non-temporal: they do not evict the W panels the other tiles re-read.
 #pragma unroll 8
   for (int it = 0; it < kBN * 32 / kThreads; ++it) {
     const int idx = it * kThreads + (int)threadIdx.x;
     const int r = idx >> 5, c = idx & 31;
-    *(i32x4_t*)(dZ + (int64_t)(n0 + r) * vs + m0 + c * 8) =
-        *(const i32x4_t GRPO_LDS*)(lds + r * kStagePitch + c * 16);
+    __builtin_nontemporal_store(*(const i32x4_t GRPO_LDS*)(lds + r * kStagePitch + c * 16),
+                                (i32x4_t*)(dZ + (int64_t)(n0 + r) * vs + m0 + c * 8));
   }
   // 4. dZT rows (vocabulary-major, token contiguous) through transposed LDS reads.
   // A 16-lane group moves one unit of 4 vocabulary rows x 32 tokens: lane m reads
@@ -763,8 +765,9 @@ __global__ void __launch_bounds__(kThreads, 1)
       const s16x4_t hi =
           __builtin_amdgcn_ds_read_tr16_b64_v4i16((GRPO_LDS s16x4_t*)(src + 4 * kStagePitch));
       const s16x8_t v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      *(i32x4_t*)(dZT + (int64_t)(m0 + 4 * quad + (m & 3)) * cpad + n0 + 32 * blk + 8 * (m >> 2)) =
-          __builtin_bit_cast(i32x4_t, v8);
+      __builtin_nontemporal_store(
+          __builtin_bit_cast(i32x4_t, v8),
+          (i32x4_t*)(dZT + (int64_t)(m0 + 4 * quad + (m & 3)) * cpad + n0 + 32 * blk + 8 * (m >> 2)));
     }
   }
 }
