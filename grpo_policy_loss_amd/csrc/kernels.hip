@@ -207,6 +207,16 @@ __device__ __forceinline__ void lse_columns(const Acc& acc, int wave, int lane, 
 }
 
 
+// threadIdx.x & 63 through an opaque move, so lane-derived epilogue addresses
+// are formed after the main loop instead of being hoisted across it (where
+// every register is in use) and spilled.  Used by the fp8 instances, whose
+// main loop holds the most fragment registers; the bf16 ones do not spill.
+__device__ __forceinline__ int lane_fresh() {
+  int t;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(t) : "v"((int)threadIdx.x));
+  return t & 63;
+}
+
 // ---------------------------------------------------------------- forward tile
 // Epilogue of one forward tile (vocabulary rows [m0, m0 + mvalid), tokens
 // [n0, n0 + 256) of the chunk): fold the accumulators into one (max, sum exp)
@@ -223,7 +233,7 @@ __device__ __forceinline__ void lse_epilogue(const Acc& acc, int mt, int64_t m0,
                                              float* __restrict__ part_m,
                                              float* __restrict__ part_s, float* __restrict__ zy) {
   constexpr bool kFp8 = std::is_same<T, uint8_t>::value;
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = kFp8 ? lane_fresh() : (int)(threadIdx.x & 63), wave = wave_id();
   const int wm0 = (wave >> 1) * 128;
   const bool full = mvalid >= wm0 + 128;
   // per token column: the factor that turns the accumulator into the logit
@@ -294,9 +304,10 @@ __device__ __forceinline__ void lse_epilogue(const Acc& acc, int mt, int64_t m0,
 }
 
 // Targets of this lane's token columns.
+template <bool kFresh>
 __device__ __forceinline__ void load_targets(const int32_t* __restrict__ y, int n0, int n_tok,
                                              int (&yv)[kWN]) {
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = kFresh ? lane_fresh() : (int)(threadIdx.x & 63), wave = wave_id();
 #pragma unroll
   for (int j = 0; j < kWN; ++j) {
     const int t = n0 + acc_col(wave, lane, j);
@@ -331,7 +342,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   else
     tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
   int yv[kWN];
-  load_targets(y, n0, n_tok, yv);
+  load_targets<kFp8>(y, n0, n_tok, yv);
   lse_epilogue<T, SC>(acc, mt, m0, mvalid, n0, n_tok, cpad, xf, w_scale, h_scale, yv,
                       (float*)smem, part_m, part_s, zy);
 }
@@ -685,7 +696,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   else
     tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
 
-  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int lane = kFp8 ? lane_fresh() : (int)(threadIdx.x & 63), wave = wave_id();
   float ct[kWN], lb[kWN], cs[kWN];
   int64_t yl[kWN];
 #pragma unroll
