@@ -1,0 +1,89 @@
+"""Host-side logic of bench.py (no GPU): the multi-GPU refusal, the flop
+accounting, and the two rocprofv3 summarizers with their staleness check."""
+from __future__ import annotations
+
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_algorithmic_flops():
+    d, V, N, Na = 1536, 151936, 32768, 27732
+    assert bench.alg_flops("lse_partials", d, V, N, Na) == 2 * 2.0 * d * V * N
+    for k in ("dz", "dh_gemm", "dw_gemm"):
+        assert bench.alg_flops(k, d, V, N, Na) == 2.0 * d * V * Na
+    assert bench.alg_flops("lse_merge", d, V, N, Na) is None
+
+
+def _counter_csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value\n")
+        for disp, name, value in rows:
+            f.write(f'{disp},"{name}",{counter},{value}\n')
+
+
+def test_summarize_traffic_scales_by_the_calibration_copy(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    gib_kib = bench.COPY_BYTES / 1024
+    kname = "void grpo::(anonymous namespace)::k_lse_partials<__bf16, false>(...)"
+    # the copy reads 1 GiB and FETCH_SIZE reports half of it; the kernel reports 1000
+    # and 3000 KiB (two dispatches, one of them split over two counter rows)
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE",
+                 [(1, "__amd_rocclr_copyBuffer", gib_kib / 2), (2, kname, 600), (2, kname, 400),
+                  (3, kname, 3000), (4, "k_lse_merge", 77)])
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE",
+                 [(1, "__amd_rocclr_copyBuffer", gib_kib), (2, kname, 10), (3, kname, 30)])
+    bench.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "wl")
+    text = open(tmp_path / "traffic_lse_partials_wl.md").read()
+    rec = json.loads(text.split("traffic_record: ")[1])
+    assert rec["launches"] == 2
+    assert rec["copy_fetch_scale"] == 0.5 and rec["copy_write_scale"] == 1.0
+    assert rec["fetch_bytes_per_launch"] == round(2000 * 1024 / 0.5)    # mean 2000 KiB, x2
+    assert rec["write_bytes_per_launch"] == round(20 * 1024)
+    assert rec["source_hash"] == bench.kernel_source_hash()
+    assert bench.read_traffic("lse_partials", "wl") == rec["hbm_bytes_per_launch"]
+
+
+def test_traffic_record_goes_stale_when_the_kernels_change(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    rec = {"source_hash": "0" * 16, "hbm_bytes_per_launch": 123}
+    (tmp_path / "traffic_lse_partials_wl.md").write_text("traffic_record: " + json.dumps(rec) + "\n")
+    assert bench.read_traffic("lse_partials", "wl") is None
+    assert bench.read_traffic("lse_partials", "other") is None
+
+
+def test_summarize_stats_table(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    csv_path = tmp_path / "stats.csv"
+    csv_path.write_text(
+        '"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n'
+        '"_ZN4grpo12_GLOBAL__N_14k_dzIDF16bLb0EEEvPKT_",8,8000000,1000000.0,20.0,1,2,0\n'
+        '"_ZN4grpo12_GLOBAL__N_114k_lse_partialsIDF16bLb0EEEvPKT_",16,32000000,2000000.0,78.0,1,2,0\n'
+        '"void at::native::vectorized_elementwise_kernel<4>",3,800000,266666.7,2.0,1,2,0\n')
+    bench.summarize_stats(str(csv_path), "qwen2.5-1.5b-bf16", 3, 1)
+    text = open(tmp_path / "kernel_stats_qwen2.5-1.5b-bf16.md").read()
+    lines = [l for l in text.splitlines() if l.startswith("| `")]
+    assert lines[0].startswith("| `k_lse_partials` | 16 | 2000.0 | 32.00 | 78.00% |")
+    assert lines[1].startswith("| `k_dz` | 8 | 1000.0 | 8.00 | 20.00% |")
+    assert "| (torch input generation, copies, fills) | | | 0.80 | 2.00% |" in text
+    assert "--steps 3 --warmup 1" in text
+
+
+@pytest.mark.parametrize("name", ["qwen2.5-1.5b-bf16", "llama3.1-8b-20k-bf16"])
+def test_committed_profiles_name_their_command(name):
+    text = open(os.path.join(ROOT, "profiles", f"kernel_stats_{name}.md")).read()
+    assert "rocprofv3 --kernel-trace --stats" in text and f"--workload {name}" in text
