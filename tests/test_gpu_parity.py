@@ -42,7 +42,8 @@ def inputs(w, seed=0):
 
 # ----------------------------------------------------------------------------- tile main loop
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (300, 517, 192), (1000, 77, 320), (33, 600, 8)])
+@pytest.mark.parametrize("M,N,K", [(256, 256, 64), (300, 517, 192), (1000, 77, 320), (33, 600, 8),
+                                   (300, 517, 200)])
 def test_tile_gemm_matches_exact_product(dtype, M, N, K):
     _need_gpu()
     if dtype == torch.float32 and K % 4:
@@ -94,9 +95,12 @@ def test_chain_bf16_multiple_vocab_slabs(monkeypatch):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("chunk", [256, 300, 4096])
-def test_chain_matches_oracle(dtype, chunk):
+@pytest.mark.parametrize("d", [320, 200])
+def test_chain_matches_oracle(dtype, chunk, d):
+    # d = 200: the last K slice of every tile is partial (400 B of bf16 = 3 slices of
+    # 128 B + 16 B; 800 B of f32 = 6 slices + 32 B), in the forward and the dZ recompute
     _need_gpu()
-    w = small(dtype, chunk=chunk)
+    w = small(dtype, chunk=chunk, d=d)
     inp = inputs(w, seed=1)
     g = gpu_chain(inp, w)
     o = oracle_chain(inp, w)
