@@ -43,6 +43,9 @@ def test_full_size_sampled_parity(name):
     w = workloads.BY_NAME[name]
     print(f"[full] {name}: N={w.N} d={w.d} V={w.V} chunk={w.chunk}", flush=True)
     inp = workloads.generate(w, seed=11, device="cuda")
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
     adv = gp.grpo_advantages(inp["rewards"], w.G, EPS)
     ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk)
     loss, lp, kl, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref,
@@ -50,6 +53,12 @@ def test_full_size_sampled_parity(name):
     dH, dW = gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp, lse,
                               w.B, w.L, BETA, 1.0, w.chunk)
     torch.cuda.synchronize()
+    # everything the calls allocate (workspaces, dH, dW and the per-token outputs) stays
+    # below one bf16 tokens x vocab tensor: no (tokens x vocab) tensor is ever resident
+    extra = torch.cuda.max_memory_allocated() - base
+    print(f"[full] {name}: peak allocated by the calls {extra / 1e9:.2f} GB against "
+          f"N x V x 2 B = {w.N * w.V * 2 / 1e9:.2f} GB", flush=True)
+    assert extra < w.N * w.V * 2
 
     mask = inp["mask"].cpu().numpy()
     y = inp["y"].cpu().numpy().astype(np.int64)
