@@ -122,10 +122,10 @@ def summarize_traffic(fetch_csv, write_csv, workload, kernel="lse_partials"):
     print(path)
 
 
-def summarize_stats(stats_csv, workload, steps, warmup):
+def summarize_stats(stats_csv, workload, steps, warmup, fp8=False):
     """Turn a `rocprofv3 --kernel-trace --stats` run of this benchmark into
-    profiles/kernel_stats_<workload>.md (per-kernel calls, average and total
-    time, share of GPU time), with the command that made it."""
+    profiles/kernel_stats_<workload>[_fp8].md (per-kernel calls, average and
+    total time, share of GPU time), with the command that made it."""
     import workloads
 
     w = workloads.BY_NAME[workload]
@@ -140,7 +140,9 @@ def summarize_stats(stats_csv, workload, steps, warmup):
     other_ms = sum(r[4] for r in rows if r[0] is None)
     other_pct = sum(r[5] for r in rows if r[0] is None)
     ours.sort(key=lambda r: -r[4])
-    lines = [f"# Kernel trace statistics: full step on the {workload} workload ({w.dtype})", "",
+    flag = " --fp8" if fp8 else ""
+    kind = "fp8 e4m3 forward, bf16 backward" if fp8 else w.dtype
+    lines = [f"# Kernel trace statistics: full step on the {workload} workload ({kind})", "",
              f"Workload: {w.N:,} flattened tokens ({w.prompts} prompts x {w.G} generations x {w.L}), "
              f"d = {w.d}, V = {w.V:,}, chunk {w.chunk}; one step = advantages + reference "
              f"log-probs + loss forward + loss backward. {steps} timed steps plus {warmup} "
@@ -148,9 +150,9 @@ def summarize_stats(stats_csv, workload, steps, warmup):
              "Command (repo root on the GPU box, `R` = repo root):", "", "```",
              "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats --output-format csv \\",
              f"    -d $R/gpurun_out/prof -o bench -- python3 $R/bench.py --workload {workload} "
-             f"--steps {steps} --warmup {warmup} --no-cpu-baseline",
+             f"--steps {steps} --warmup {warmup} --no-cpu-baseline{flag}",
              f"python3 $R/bench.py --summarize-stats $R/gpurun_out/prof/bench_kernel_stats.csv "
-             f"--workload {workload} --steps {steps} --warmup {warmup}",
+             f"--workload {workload} --steps {steps} --warmup {warmup}{flag}",
              "```", "",
              "| kernel | calls | average (us) | total (ms) | share of GPU time |",
              "|---|---|---|---|---|"]
@@ -159,7 +161,7 @@ def summarize_stats(stats_csv, workload, steps, warmup):
     lines.append(f"| (torch input generation, copies, fills) | | | {other_ms:.2f} | {other_pct:.2f}% |")
     lines.append("")
     lines.append("source_hash: " + kernel_source_hash())
-    path = os.path.join(PROFILES, f"kernel_stats_{workload}.md")
+    path = os.path.join(PROFILES, f"kernel_stats_{workload}{'_fp8' if fp8 else ''}.md")
     with open(path, "w") as fo:
         fo.write("\n".join(lines) + "\n")
     print(path)
@@ -264,7 +266,7 @@ def main():
                                ("aggregation", int(args.sequence_mean))) if v} or None
 
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.workload, args.steps, args.warmup)
+        summarize_stats(args.summarize_stats, args.workload, args.steps, args.warmup, args.fp8)
         return
 
     if args.summarize_traffic:
