@@ -45,7 +45,10 @@ is offered beside the global token mean.
 Parity unpinned: nothing.  Every function is pinned by the CPU tests against
 closed forms, invariants, library routines (scipy log_softmax, numpy std,
 torch float64 autograd of the literal policy-term expression) and central
-finite differences of the stop-gradient surrogate.
+finite differences of the stop-gradient surrogate.  The row-block loop of
+loss_backward is pinned with more than one block: on the 512-token tiny
+workload (two blocks of 256 rows, against autograd and central differences)
+and with 3- and 7-row blocks on a toy problem.
 """
 from __future__ import annotations
 

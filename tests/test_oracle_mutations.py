@@ -130,6 +130,13 @@ MUTATIONS = [
        "e = np.array([fp8_scale_exponent(np.abs(X[0]).max() if X.size else 0.0)])")]),
     ("backward: recomputed logits against the transposed head",
      [("Z = Hs @ Wf.T", "Z = Hs @ Wf[::-1].T")]),
+    ("backward: dW overwritten by each row block",
+     [("dW += dZ.T @ Hs", "dW = dZ.T @ Hs")]),
+    ("backward: row blocks past the first skipped",
+     [("sel = need[b0:b0 + block]", "sel = need[b0:block]")]),
+    ("backward: only the requested dH rows visited (unmasked tokens not added)",
+     [("need = np.union1d(active, rows) if want_dW else np.unique(rows)",
+       "need = np.unique(rows)")]),
 ]
 
 

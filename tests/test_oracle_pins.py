@@ -276,6 +276,99 @@ def test_policy_equals_reference_gradient_is_weighted_cross_entropy():
     np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-10, atol=1e-16)
 
 
+# --------------------------------------------------------------------------- multi-block backward
+# loss_backward visits its rows in blocks of ROW_BLOCK = 256; the tiny workload
+# (2 prompts x 4 generations x 64 tokens, d 256, V 1024) has 512 flattened tokens,
+# so these pins run the block loop twice with active tokens in both blocks.
+def _tiny_problem():
+    from workloads import BY_NAME, generate
+
+    w = BY_NAME["tiny-f32"]
+    inp = generate(w, seed=3, device="cpu")
+    f64 = lambda t: t.double().numpy()   # noqa: E731
+    H, W, H_ref = f64(inp["H"]), f64(inp["W"]), f64(inp["H_ref"])
+    y = inp["y"].numpy().astype(np.int64)
+    mask = inp["mask"].numpy()
+    adv = oracle.group_advantages(inp["rewards"].numpy(), w.G)
+    ref_lp, _ = oracle.token_logprobs(H_ref, W, y)
+    p = dict(H=H, W=W, H_ref=H_ref, y=y, mask=mask, adv=adv, ref_lp=ref_lp, L=w.L, G=w.G,
+             N=w.N, V=w.V, d=w.d)
+    assert w.N == 2 * 256          # the oracle's default row block
+    assert mask[:w.N // 2].any() and mask[w.N // 2:].any()
+    return p
+
+
+def test_tiny_config_gradients_match_torch_autograd_across_row_blocks():
+    p = _tiny_problem()
+    H = torch.tensor(p["H"], requires_grad=True)
+    W = torch.tensor(p["W"], requires_grad=True)
+    _torch_autograd_loss(p, H, W).backward()
+    dH, dW = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                  p["L"], BETA)
+    np.testing.assert_allclose(dH, H.grad.numpy(), rtol=1e-10, atol=1e-14 * np.abs(dH).max())
+    np.testing.assert_allclose(dW, W.grad.numpy(), rtol=1e-10, atol=1e-14 * np.abs(dW).max())
+
+
+def test_tiny_config_gradients_match_central_differences():
+    """Central differences of the stop-gradient surrogate on the 512-token tiny
+    workload: along one random direction over all of H and all of W (the
+    directional derivative <dX, U> sums every token's share, so each row block
+    must contribute), and at single entries in both row blocks."""
+    p = _tiny_problem()
+    lp0, _ = oracle.token_logprobs(p["H"], p["W"], p["y"])
+    dH, dW = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                  p["L"], BETA)
+    rng = np.random.default_rng(15)
+    h = 1e-6
+    UH = rng.standard_normal(p["H"].shape)
+    UW = rng.standard_normal(p["W"].shape)
+    fd = (_surrogate(p, p["H"] + h * UH, p["W"], lp0) -
+          _surrogate(p, p["H"] - h * UH, p["W"], lp0)) / (2 * h)
+    assert abs(fd - (dH * UH).sum()) < 1e-6 * abs(fd) + 1e-9, (fd, (dH * UH).sum())
+    fd = (_surrogate(p, p["H"], p["W"] + h * UW, lp0) -
+          _surrogate(p, p["H"], p["W"] - h * UW, lp0)) / (2 * h)
+    assert abs(fd - (dW * UW).sum()) < 1e-6 * abs(fd) + 1e-9, (fd, (dW * UW).sum())
+    active = np.nonzero(p["mask"])[0]
+    for t in (active[0], active[-1]):                 # first and second row block
+        k = rng.integers(0, p["d"])
+        Hp, Hm = p["H"].copy(), p["H"].copy()
+        Hp[t, k] += h
+        Hm[t, k] -= h
+        fd = (_surrogate(p, Hp, p["W"], lp0) - _surrogate(p, Hm, p["W"], lp0)) / (2 * h)
+        assert abs(fd - dH[t, k]) < 1e-8 + 1e-6 * abs(fd), (t, k, fd, dH[t, k])
+    for v in (p["y"][active[0]], p["y"][active[-1]], rng.integers(0, p["V"])):
+        k = rng.integers(0, p["d"])
+        Wp, Wm = p["W"].copy(), p["W"].copy()
+        Wp[v, k] += h
+        Wm[v, k] -= h
+        fd = (_surrogate(p, p["H"], Wp, lp0) - _surrogate(p, p["H"], Wm, lp0)) / (2 * h)
+        assert abs(fd - dW[v, k]) < 1e-8 + 1e-6 * abs(fd), (v, k, fd, dW[v, k])
+
+
+def test_backward_row_block_size_and_requested_rows():
+    """Small row blocks (7 rows: five blocks on the 30-token problem) give the
+    one-block result and torch autograd's; dW does not depend on which dH rows
+    are requested (it sums every unmasked token, requested or not)."""
+    p = _problem(16)
+    one = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"],
+                               BETA)
+    many = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"],
+                                BETA, block=7)
+    for a, b in zip(one, many):
+        np.testing.assert_allclose(b, a, rtol=1e-12, atol=1e-15 * np.abs(a).max())
+    H = torch.tensor(p["H"], requires_grad=True)
+    W = torch.tensor(p["W"], requires_grad=True)
+    _torch_autograd_loss(p, H, W).backward()
+    np.testing.assert_allclose(many[0], H.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(many[1], W.grad.numpy(), rtol=1e-10, atol=1e-15)
+    masked = np.nonzero(p["mask"] == 0)[0]
+    rows = np.array([masked[0], np.nonzero(p["mask"])[0][1]])   # one masked, one active
+    dHr, dWr = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"],
+                                    p["L"], BETA, dh_rows=rows, block=3)
+    np.testing.assert_allclose(dWr, one[1], rtol=1e-12, atol=1e-15 * np.abs(one[1]).max())
+    np.testing.assert_allclose(dHr, one[0][rows], rtol=1e-12, atol=1e-18)
+
+
 def test_grad_loss_scales_linearly():
     p = _problem(14)
     a = oracle.loss_backward(p["H"], p["W"], p["y"], p["mask"], p["adv"], p["ref_lp"], p["L"], BETA)
