@@ -3,12 +3,20 @@ one batch of synthetic inputs on one GPU:
 
     advantages -> reference log-probs (no grad) -> loss forward -> loss backward
 
-Prints ONE JSON line.  `value` is flattened tokens per second of the whole
-step (inputs resident in HBM before the timed region).  Also reported: the
-forward+backward-only rate and its fraction of dense bf16 MFMA peak, peak HBM
-allocated, a roofline entry for the dominant kernel timed with HIP events on
-its own stream, and the float64 oracle timed on the host cores on a bounded
-sample of the same workload.
+Prints ONE JSON line.  `value` is flattened tokens per second of the loss
+forward + backward (the metric's rate; inputs resident in HBM before the timed
+region), measured with HIP events around those two calls inside the timed
+steps; the rate of the whole step (advantages and reference log-probs
+included) is `step_tokens_per_s`.  Also reported: the forward + backward
+fraction of dense bf16 MFMA peak, peak HBM (torch allocator peak and the
+device's free memory before and after, from hipMemGetInfo), a roofline entry
+for the dominant kernel, and the float64 oracle timed on the host cores on a
+bounded sample of the same workload.
+
+The roofline's per-kernel times come from a second pass of the same number of
+steps, run right after the timed one with the library's per-kernel HIP events
+on (each launch bracketed by two events on its own stream), so that the timed
+steps carry no instrumentation.
 """
 from __future__ import annotations
 
@@ -26,7 +34,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "flattened tokens/s GRPO loss fwd+bwd (1 GPU) + % bf16 MFMA peak + peak HBM"
 PEAK_FLOPS = {"bf16": 2.5e15, "f32": 157.3e12, "fp8": 5.0e15}   # MI355X dense MFMA peaks
-DEFAULT_WORKLOAD = "qwen2.5-1.5b-bf16"
+# the largest single-GPU workload: the pages' long-context setting (Llama-3.1-8B
+# LM head, 20K-token completions, 8 generations per prompt)
+DEFAULT_WORKLOAD = "llama3.1-8b-20k-bf16"
 
 
 def log(*a):
@@ -167,6 +177,18 @@ def summarize_stats(stats_csv, workload, steps, warmup, fp8=False):
     print(path)
 
 
+def cpu_model():
+    """The host CPU's model name (first 'model name' line of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def alg_flops(kind, d, V, N, N_act):
     """Algorithmic MFMA flops of one step's launches of a kernel kind."""
     if kind == "lse_partials":          # reference pass + loss forward: 2 d V per token each
@@ -218,6 +240,7 @@ def cpu_baseline(w, inp, seconds=15.0, opts=None):
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     return {"value": n2 / t2, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"first {n2} flattened tokens of the batch (ref + fwd + bwd, float64 "
                       f"NumPy, full V={w.V}, d={w.d}); {t2:.1f} s on "
                       f"{len(os.sched_getaffinity(0))} visible host CPUs"}
@@ -376,17 +399,27 @@ def main():
         log(f"[bench] warmup {i + 1}/{args.warmup} done")
 
     torch.cuda.reset_peak_memory_stats(dev)
+    free_before, total_hbm = torch.cuda.mem_get_info(dev)        # hipMemGetInfo
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    gp.grpo_timing_begin()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
-    kernels = gp.grpo_timing_end()
+    free_after, _ = torch.cuda.mem_get_info(dev)
     peak_bytes = torch.cuda.max_memory_allocated(dev)
     log(f"[bench] {args.steps} timed steps in {t_total:.3f}s")
+    # per-kernel times: the same steps again, each launch bracketed by HIP events
+    gp.grpo_timing_begin()
+    torch.cuda.synchronize()
+    t_inst = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t_inst = time.perf_counter() - t_inst
+    kernels = gp.grpo_timing_end()
+    log(f"[bench] {args.steps} instrumented steps in {t_inst:.3f}s")
 
     ms_ref = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     ms_fwd = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
@@ -420,7 +453,7 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": round(N / (ms_step * 1e-3), 1),
+        "value": round(N / ((ms_fwd + ms_bwd) * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -435,13 +468,18 @@ def main():
                    "chunk": w.chunk, "beta": workloads.BETA,
                    "step": "advantages + reference log-probs + loss fwd + loss bwd",
                    **({"opts": xopts} if xopts else {}), **({"fp8": True} if args.fp8 else {})},
-        "fwd_bwd_tokens_per_s": round(N / ((ms_fwd + ms_bwd) * 1e-3), 1),
+        "value_is": "flattened tokens / (loss forward + loss backward time)",
+        "step_tokens_per_s": round(N / (ms_step * 1e-3), 1),
         "fwd_bwd_mfma_frac": round(fb_flops / ((ms_fwd + ms_bwd) * 1e-3) / PEAK_FLOPS[w.dtype], 4),
         "ms": {"advantages+ref": round(ms_ref, 3), "fwd": round(ms_fwd, 3),
                "bwd": round(ms_bwd, 3)},
         "peak_hbm_gb": round(peak_bytes / 1e9, 3),
+        "hip_mem_get_info_gb": {"free_before": round(free_before / 1e9, 3),
+                                "free_after": round(free_after / 1e9, 3),
+                                "total": round(total_hbm / 1e9, 3)},
         "full_fp32_logits_gb": round(N * V * 4 / 1e9, 2),
         "kernels_ms_per_step": {k: round(v[1] / args.steps, 3) for k, v in kernels.items()},
+        "instrumented_ms_per_step": round(t_inst * 1e3 / args.steps, 3),
         "roofline": roof,
         "cpu_baseline": cpu,
     }

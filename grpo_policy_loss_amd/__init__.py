@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     grpo_loss_fwd_fp8,
     grpo_loss_bwd_fp8,
     GRPO_OP_BWD,
+    GRPO_OP_BWD_MIN,
     GRPO_OP_FWD,
     GRPO_OP_REF,
     AGG_SEQUENCE_MEAN,

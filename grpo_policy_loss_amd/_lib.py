@@ -15,7 +15,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgrpo.so")
 
 GRPO_F32, GRPO_BF16, GRPO_FP8_E4M3 = 0, 1, 2
-GRPO_OP_REF, GRPO_OP_FWD, GRPO_OP_BWD = 0, 1, 2
+GRPO_OP_REF, GRPO_OP_FWD, GRPO_OP_BWD, GRPO_OP_BWD_MIN = 0, 1, 2, 3
 STATUS = {0: "GRPO_OK", -1: "GRPO_ERR_INVALID_ARG", -2: "GRPO_ERR_WORKSPACE",
           -3: "GRPO_ERR_UNSUPPORTED", -4: "GRPO_ERR_HIP"}
 
@@ -117,6 +117,28 @@ def _dev(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
+def _arg(t, name, dtype=None, shape=None, numel=None):
+    """Check one tensor argument's type, dtype and size before any device call.
+    The C ABI cannot see buffer sizes, so this is the only guard against a
+    kernel writing past an output or reading past an input."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+    return t
+
+
+def _matrix(t, name):
+    _arg(t, name)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    return t.shape
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -137,11 +159,6 @@ def _opts(opts):
                                   for k, v in opts.items()}))
 
 
-def _want(t: torch.Tensor, dtype, name):
-    if t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-
-
 def grpo_workspace_bytes(op: int, N: int, d: int, V: int, dtype: int, chunk: int) -> int:
     return int(lib().grpo_workspace_bytes(op, N, d, V, dtype, chunk))
 
@@ -157,21 +174,40 @@ def auto_chunk(B: int, L: int, d: int, V: int, dtype: int, budget_bytes=None) ->
     return c
 
 
+def _check_workspace(workspace, op, N, d, V, dt, chunk):
+    """A caller's workspace must be a uint8 tensor of at least the op's minimum size
+    (the backward plans its dZ slab from the size it is given)."""
+    if workspace is None:
+        return
+    _arg(workspace, "workspace", dtype=torch.uint8)
+    if chunk == 0:
+        return                      # checked again once the chunk is known
+    least = grpo_workspace_bytes(GRPO_OP_BWD_MIN if op == GRPO_OP_BWD else op, N, d, V, dt, chunk)
+    if least == 0:
+        _check("grpo_workspace_bytes", -1)
+    if workspace.numel() < least:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes; this call needs at least {least}")
+
+
 def _workspace(op, N, d, V, dt, chunk, device, workspace):
+    """The caller's workspace, or a new one of grpo_workspace_bytes(op, ...) bytes."""
+    if workspace is not None:
+        _check_workspace(workspace, op, N, d, V, dt, chunk)
+        _dev(workspace)
+        return workspace
     need = grpo_workspace_bytes(op, N, d, V, dt, chunk)
     if need == 0:
         _check("grpo_workspace_bytes", -1)
-    if workspace is not None and workspace.numel() * workspace.element_size() >= need:
-        return workspace
     return torch.empty(need, dtype=torch.uint8, device=device)
 
 
 def grpo_advantages(rewards: torch.Tensor, group_size: int, eps: float = 1e-4, out=None):
-    _dev(rewards)
-    _want(rewards, torch.float32, "rewards")
-    if rewards.numel() % group_size:
-        raise ValueError("rewards length must be a multiple of group_size")
-    out = torch.empty_like(rewards) if out is None else out
+    _arg(rewards, "rewards", dtype=torch.float32)
+    if group_size <= 0 or rewards.numel() % group_size:
+        raise ValueError("rewards length must be a positive multiple of group_size")
+    out = torch.empty_like(rewards) if out is None else \
+        _arg(out, "out", dtype=torch.float32, numel=rewards.numel())
+    _dev(rewards, out)
     _check("grpo_advantages", lib().grpo_advantages(
         _ptr(rewards), rewards.numel() // group_size, group_size, eps, _ptr(out), _stream()))
     return out
@@ -179,14 +215,15 @@ def grpo_advantages(rewards: torch.Tensor, group_size: int, eps: float = 1e-4, o
 
 def grpo_ref_logprobs(H_ref, W, y, chunk: int = 4096, out=None, workspace=None,
                       opts=None):
-    _dev(H_ref, W, y)
-    _want(y, torch.int32, "y")
-    N, d = H_ref.shape
-    V = W.shape[0]
+    N, d = _matrix(H_ref, "H_ref")
     dt = _dt(H_ref)
-    if W.dtype != H_ref.dtype or W.shape[1] != d or y.numel() != N:
-        raise ValueError("shape/dtype mismatch between H_ref, W, y")
-    out = torch.empty(N, dtype=torch.float32, device=H_ref.device) if out is None else out
+    V = _matrix(W, "W")[0]
+    _arg(W, "W", dtype=H_ref.dtype, shape=(V, d))
+    _arg(y, "y", dtype=torch.int32, numel=N)
+    out = torch.empty(N, dtype=torch.float32, device=H_ref.device) if out is None else \
+        _arg(out, "out", dtype=torch.float32, numel=N)
+    _check_workspace(workspace, GRPO_OP_REF, N, d, V, dt, chunk)
+    _dev(H_ref, W, y, out)
     if chunk == 0:
         chunk = auto_chunk(1, N, d, V, dt)
     ws = _workspace(GRPO_OP_REF, N, d, V, dt, chunk, H_ref.device, workspace)
@@ -202,17 +239,18 @@ def grpo_loss_fwd(H, W, y, mask, adv, ref_lp, B: int, L: int, beta: float = 0.04
     of grpo_opts fields (logit_scale_multiply, logit_scale_divide, logit_softcapping,
     temperature, kl_estimator, no_detach, aggregation), or None for the plain loss.
     chunk 0 (here and in the other calls): auto_chunk with half the free HBM."""
-    _dev(H, W, y, mask, adv, ref_lp)
-    _want(y, torch.int32, "y")
-    _want(mask, torch.uint8, "mask")
-    _want(adv, torch.float32, "adv")
-    _want(ref_lp, torch.float32, "ref_lp")
-    N, d = H.shape
-    V = W.shape[0]
+    N, d = _matrix(H, "H")
     dt = _dt(H)
-    if W.dtype != H.dtype or W.shape[1] != d or N != B * L or y.numel() != N \
-            or mask.numel() != N or ref_lp.numel() != N or adv.numel() != B:
-        raise ValueError("shape/dtype mismatch")
+    V = _matrix(W, "W")[0]
+    _arg(W, "W", dtype=H.dtype, shape=(V, d))
+    if N != B * L:
+        raise ValueError(f"H has {N} rows, B * L = {B * L}")
+    _arg(y, "y", dtype=torch.int32, numel=N)
+    _arg(mask, "mask", dtype=torch.uint8, numel=N)
+    _arg(adv, "adv", dtype=torch.float32, numel=B)
+    _arg(ref_lp, "ref_lp", dtype=torch.float32, numel=N)
+    _check_workspace(workspace, GRPO_OP_FWD, N, d, V, dt, chunk)
+    _dev(H, W, y, mask, adv, ref_lp)
     dev = H.device
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     lp = torch.empty(N, dtype=torch.float32, device=dev)
@@ -234,17 +272,23 @@ def grpo_loss_bwd(H, W, y, mask, adv, ref_lp, lp, lse, B: int, L: int, beta: flo
     """Returns (dH[N, d] in H's dtype, dW[V, d] float32).  dW is accumulated into
     when given (zeros are allocated otherwise).  `opts` must be those of the
     forward that produced lp and lse."""
-    _dev(H, W, y, mask, adv, ref_lp, lp, lse)
-    N, d = H.shape
-    V = W.shape[0]
+    N, d = _matrix(H, "H")
     dt = _dt(H)
-    if W.dtype != H.dtype or N != B * L:
-        raise ValueError("shape/dtype mismatch")
+    V = _matrix(W, "W")[0]
+    _arg(W, "W", dtype=H.dtype, shape=(V, d))
+    if N != B * L:
+        raise ValueError(f"H has {N} rows, B * L = {B * L}")
+    _arg(y, "y", dtype=torch.int32, numel=N)
+    _arg(mask, "mask", dtype=torch.uint8, numel=N)
+    _arg(adv, "adv", dtype=torch.float32, numel=B)
+    for t, name in ((ref_lp, "ref_lp"), (lp, "lp"), (lse, "lse")):
+        _arg(t, name, dtype=torch.float32, numel=N)
     dev = H.device
-    dH = torch.empty_like(H) if dH is None else dH
-    dW = torch.zeros(V, d, dtype=torch.float32, device=dev) if dW is None else dW
-    _dev(dH, dW)
-    _want(dW, torch.float32, "dW")
+    dH = torch.empty_like(H) if dH is None else _arg(dH, "dH", dtype=H.dtype, shape=(N, d))
+    dW = torch.zeros(V, d, dtype=torch.float32, device=dev) if dW is None else \
+        _arg(dW, "dW", dtype=torch.float32, shape=(V, d))
+    _check_workspace(workspace, GRPO_OP_BWD, N, d, V, dt, chunk)
+    _dev(H, W, y, mask, adv, ref_lp, lp, lse, dH, dW)
     if chunk == 0:
         chunk = auto_chunk(B, L, d, V, dt)
     ws = _workspace(GRPO_OP_BWD, N, d, V, dt, chunk, dev, workspace)
@@ -271,11 +315,11 @@ def grpo_timing_end(max_entries: int = 32):
 
 def grpo_gemm_nt(A, B):
     """C = A @ B.T in float32 through the library's MFMA tile main loop."""
+    M, K = _matrix(A, "A")
+    _dt(A)
+    N = _matrix(B, "B")[0]
+    _arg(B, "B", dtype=A.dtype, shape=(N, K))
     _dev(A, B)
-    M, K = A.shape
-    N = B.shape[0]
-    if B.shape[1] != K or A.dtype != B.dtype:
-        raise ValueError("shape/dtype mismatch")
     C = torch.empty(M, N, dtype=torch.float32, device=A.device)
     _check("grpo_gemm_nt", lib().grpo_gemm_nt(_ptr(A), _ptr(B), M, N, K, _dt(A), _ptr(C), _stream()))
     return C
@@ -296,8 +340,9 @@ class Fp8:
 
 def quantize_fp8(X, per_row=True) -> Fp8:
     """grpo_quantize_fp8 of a float32 or bfloat16 matrix on the GPU."""
+    rows, cols = _matrix(X, "X")
+    _dt(X)
     _dev(X)
-    rows, cols = X.shape
     codes = torch.empty(rows, cols, dtype=torch.uint8, device=X.device)
     scales = torch.empty(rows if per_row else 1, dtype=torch.float32, device=X.device)
     ws = None if per_row else torch.empty(int(lib().grpo_quantize_fp8_workspace_bytes()),
@@ -310,7 +355,10 @@ def quantize_fp8(X, per_row=True) -> Fp8:
 
 def dequantize_fp8(q: Fp8):
     """grpo_dequantize_fp8: the exact bfloat16 values of q."""
-    rows, cols = q.codes.shape
+    rows, cols = _matrix(q.codes, "codes")
+    _arg(q.codes, "codes", dtype=torch.uint8)
+    _arg(q.scales, "scales", dtype=torch.float32, numel=rows if q.per_row else 1)
+    _dev(q.codes, q.scales)
     out = torch.empty(rows, cols, dtype=torch.bfloat16, device=q.codes.device)
     _check("grpo_dequantize_fp8", lib().grpo_dequantize_fp8(
         _ptr(q.codes), _ptr(q.scales), rows, cols, int(q.per_row), _ptr(out), _stream()))
@@ -318,20 +366,25 @@ def dequantize_fp8(q: Fp8):
 
 
 def _fp8_args(H: Fp8, W: Fp8):
-    if not H.per_row or W.per_row or W.scales.numel() != 1:
+    if not H.per_row or W.per_row:
         raise ValueError("fp8 loss takes per-row H scales and one W scale")
-    if H.codes.shape[1] != W.codes.shape[1]:
-        raise ValueError("H and W hidden sizes differ")
-    _dev(H.codes, H.scales, W.codes, W.scales)
-    return H.codes.shape[0], H.codes.shape[1], W.codes.shape[0]
+    N, d = _matrix(H.codes, "H codes")
+    V = _matrix(W.codes, "W codes")[0]
+    _arg(H.codes, "H codes", dtype=torch.uint8)
+    _arg(W.codes, "W codes", dtype=torch.uint8, shape=(V, d))
+    _arg(H.scales, "H scales", dtype=torch.float32, numel=N)
+    _arg(W.scales, "W scales", dtype=torch.float32, numel=1)
+    return N, d, V
 
 
 def grpo_ref_logprobs_fp8(H_ref: Fp8, W: Fp8, y, chunk: int = 4096, out=None, workspace=None,
                           opts=None):
     N, d, V = _fp8_args(H_ref, W)
-    _dev(y)
-    _want(y, torch.int32, "y")
-    out = torch.empty(N, dtype=torch.float32, device=y.device) if out is None else out
+    _arg(y, "y", dtype=torch.int32, numel=N)
+    out = torch.empty(N, dtype=torch.float32, device=y.device) if out is None else \
+        _arg(out, "out", dtype=torch.float32, numel=N)
+    _check_workspace(workspace, GRPO_OP_REF, N, d, V, GRPO_FP8_E4M3, chunk)
+    _dev(H_ref.codes, H_ref.scales, W.codes, W.scales, y, out)
     if chunk == 0:
         chunk = auto_chunk(1, N, d, V, GRPO_FP8_E4M3)
     ws = _workspace(GRPO_OP_REF, N, d, V, GRPO_FP8_E4M3, chunk, y.device, workspace)
@@ -345,11 +398,14 @@ def grpo_loss_fwd_fp8(H: Fp8, W: Fp8, y, mask, adv, ref_lp, B: int, L: int, beta
                       chunk: int = 4096, workspace=None, opts=None):
     """grpo_loss_fwd on fp8 operands: (loss[1], lp[N], kl[N], lse[N])."""
     N, d, V = _fp8_args(H, W)
-    _dev(y, mask, adv, ref_lp)
-    _want(y, torch.int32, "y")
-    _want(mask, torch.uint8, "mask")
     if N != B * L:
-        raise ValueError("N != B * L")
+        raise ValueError(f"H has {N} rows, B * L = {B * L}")
+    _arg(y, "y", dtype=torch.int32, numel=N)
+    _arg(mask, "mask", dtype=torch.uint8, numel=N)
+    _arg(adv, "adv", dtype=torch.float32, numel=B)
+    _arg(ref_lp, "ref_lp", dtype=torch.float32, numel=N)
+    _check_workspace(workspace, GRPO_OP_FWD, N, d, V, GRPO_FP8_E4M3, chunk)
+    _dev(H.codes, H.scales, W.codes, W.scales, y, mask, adv, ref_lp)
     dev = y.device
     loss = torch.empty(1, dtype=torch.float32, device=dev)
     lp, kl, lse = (torch.empty(N, dtype=torch.float32, device=dev) for _ in range(3))
@@ -369,13 +425,20 @@ def grpo_loss_bwd_fp8(H: Fp8, W: Fp8, y, mask, adv, ref_lp, lp, lse, B: int, L: 
     """Backward of grpo_loss_fwd_fp8 with respect to the dequantised H and W:
     (dH[N, d] bfloat16, dW[V, d] float32, accumulated into when given)."""
     N, d, V = _fp8_args(H, W)
-    _dev(y, mask, adv, ref_lp, lp, lse)
     if N != B * L:
-        raise ValueError("N != B * L")
+        raise ValueError(f"H has {N} rows, B * L = {B * L}")
+    _arg(y, "y", dtype=torch.int32, numel=N)
+    _arg(mask, "mask", dtype=torch.uint8, numel=N)
+    _arg(adv, "adv", dtype=torch.float32, numel=B)
+    for t, name in ((ref_lp, "ref_lp"), (lp, "lp"), (lse, "lse")):
+        _arg(t, name, dtype=torch.float32, numel=N)
     dev = y.device
-    dH = torch.empty(N, d, dtype=torch.bfloat16, device=dev) if dH is None else dH
-    dW = torch.zeros(V, d, dtype=torch.float32, device=dev) if dW is None else dW
-    _want(dW, torch.float32, "dW")
+    dH = torch.empty(N, d, dtype=torch.bfloat16, device=dev) if dH is None else \
+        _arg(dH, "dH", dtype=torch.bfloat16, shape=(N, d))
+    dW = torch.zeros(V, d, dtype=torch.float32, device=dev) if dW is None else \
+        _arg(dW, "dW", dtype=torch.float32, shape=(V, d))
+    _check_workspace(workspace, GRPO_OP_BWD, N, d, V, GRPO_FP8_E4M3, chunk)
+    _dev(H.codes, H.scales, W.codes, W.scales, y, mask, adv, ref_lp, lp, lse, dH, dW)
     if chunk == 0:
         chunk = auto_chunk(B, L, d, V, GRPO_FP8_E4M3)
     ws = _workspace(GRPO_OP_BWD, N, d, V, GRPO_FP8_E4M3, chunk, dev, workspace)

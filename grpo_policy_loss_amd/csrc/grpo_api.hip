@@ -72,61 +72,90 @@ FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
   return p;
 }
 
-// Backward workspace.  The dZ slab (and its transpose) covers `vs`
-// vocabulary rows of one chunk, vs chosen so each is at most the slab budget:
-// 2 GiB by default, or GRPO_SLAB_MIB MiB when that variable is set.  It is
-// read at every call, so a workspace query and the backward it sizes must run
-// under the same setting.  Both slabs together hold chunk x vs x 4 bytes,
-// never more than one chunk's float32 logits.  Fewer, wider slabs mean fewer
-// read-modify-write passes over the dH split partials: at the Qwen2.5-1.5B
-// shape one full-vocabulary slab runs the backward about 10 % faster than
-// 256 MiB slabs, for 2 GB more workspace.
+// Backward workspace: the fixed part (active-token index list, one chunk of
+// gathered hidden states and its transpose, the chunk's per-token coefficient /
+// lse / target id / target dZ entry, nsplit float32 dH partials of the chunk,
+// per-sequence counts), then one dZ slab: the token-major [cpad x vs] bf16 (or
+// f32) gradient of `vs` vocabulary columns of the chunk's logits, stored once.
+//
+// The slab width comes from the workspace the caller passes: the widest
+// multiple of 256 vocabulary columns (at most the padded vocabulary) that fits
+// after the fixed part, then, among widths down to half of that, the one with
+// the fewest modelled GEMM waves.  grpo_workspace_bytes(GRPO_OP_BWD) sizes the
+// workspace for a slab of at most kSlabBytesDefault; GRPO_OP_BWD_MIN for one
+// 256-column slab.  Wider slabs mean fewer read-modify-write passes over the dH
+// partials: at the Qwen2.5-1.5B LM-head shape one full-vocabulary slab ran the
+// backward about 10 % faster than 256 MiB slabs.  Two hardware bounds cap the
+// width: the dW GEMM reads the slab K-major through one buffer resource
+// (cpad x vs elements) and the dH GEMM reads W the same way (vs x d elements),
+// and a resource spans less than 2^31 bytes.
 constexpr int64_t kSlabBytesDefault = 2048ll << 20;
-int64_t slab_bytes() {
-  const char* e = getenv("GRPO_SLAB_MIB");
-  const long long mib = e ? atoll(e) : 0;
-  return mib > 0 ? (int64_t)mib << 20 : kSlabBytesDefault;
-}
 constexpr int64_t kCUs = 256;  // MI355X compute units (one GEMM workgroup each: 128 KB LDS, 4 full-register waves)
 
 struct BwdPlan {
+  bool ok;
   int64_t C, cpad, vpad, vs, nslabs, nchunks, nsplit;
-  size_t o_idx, o_cnt, o_wt, o_hact, o_ht, o_coef, o_lse, o_y, o_tgt, o_dz, o_dzt, o_dhacc, o_seq,
-      total;
+  size_t o_idx, o_cnt, o_hact, o_ht, o_coef, o_lse, o_y, o_tgt, o_dhacc, o_seq, o_dz, fixed, total;
 };
 
-BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
+// ws_bytes: the caller's workspace size; 0 plans the default slab budget and
+// -1 the narrowest slab (the minimum workspace).
+BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk, int64_t ws_bytes) {
   BwdPlan p{};
-  const size_t es = esize(dtype);
+  const int64_t es = (int64_t)esize(dtype);
   p.C = std::min<int64_t>(chunk, N);
   p.cpad = round_up(p.C, grpo::kBN);
   p.vpad = round_up(V, grpo::kBM);
   p.nchunks = (N + p.C - 1) / p.C;
-  int64_t vs_max = slab_bytes() / (p.cpad * (int64_t)es);
-  vs_max = std::max<int64_t>(grpo::kBM, vs_max / grpo::kBM * grpo::kBM);
-  vs_max = std::min<int64_t>(vs_max, p.vpad);
   // Split the dH GEMM's vocabulary range when its tile grid alone cannot fill the
   // chip: pick the split count (1..8) whose launch wastes the least of its last
   // wave of workgroups (one GEMM workgroup per CU), preferring fewer splits.
   const int64_t ct = p.cpad / 256, dt = (d + 255) / 256;
   const int64_t dh_tiles = dt * ct;
-  p.nsplit = 1;
+  int64_t nsplit_grid = 1;
   if (dh_tiles < 2 * kCUs) {
     double best = -1.0;
-    for (int64_t n = 1; n <= 8 && n * 256 <= vs_max; ++n) {
+    for (int64_t n = 1; n <= 8; ++n) {
       const int64_t wg = dh_tiles * n;
       const double fill = (double)wg / (double)(((wg + kCUs - 1) / kCUs) * kCUs);
       const double score = fill * std::min(1.0, (double)wg / (2.0 * kCUs));
       if (score > best + 1e-9) {
         best = score;
-        p.nsplit = n;
+        nsplit_grid = n;
       }
     }
   }
+  Carve c;
+  p.o_idx = c.take((size_t)N * 4);
+  p.o_cnt = c.take(4);
+  p.o_hact = c.take((size_t)(p.cpad * d) * es);
+  p.o_ht = c.take((size_t)(d * p.cpad) * es);
+  p.o_coef = c.take((size_t)p.cpad * 4);
+  p.o_lse = c.take((size_t)p.cpad * 4);
+  p.o_y = c.take((size_t)p.cpad * 4);
+  p.o_tgt = c.take((size_t)p.cpad * 4);
+  p.o_dhacc = c.take((size_t)(nsplit_grid * p.cpad * d) * 4);
+  p.o_seq = c.take((size_t)N * 4);   // per-sequence counts: B <= N sequences
+  p.o_dz = c.off;
+  p.fixed = c.off;
+
+  const int64_t col_bytes = p.cpad * es;            // one vocabulary column of the slab
+  const int64_t lim = ((1ll << 31) - 1) / (std::max(p.cpad, d) * es) / 256 * 256;
+  int64_t vs_max;
+  if (ws_bytes == 0)
+    vs_max = kSlabBytesDefault / col_bytes / 256 * 256;
+  else if (ws_bytes < 0)
+    vs_max = 256;
+  else
+    vs_max = ws_bytes > (int64_t)p.fixed ? (ws_bytes - (int64_t)p.fixed) / col_bytes / 256 * 256 : 0;
+  vs_max = std::min(std::min(vs_max, p.vpad), lim);
+  p.ok = vs_max >= 256;
+  if (!p.ok) vs_max = 256;
+  p.nsplit = std::min<int64_t>(nsplit_grid, vs_max / 256);
   // Slab width: every launch runs in whole waves of kCUs workgroups, so model a
   // chunk's backward as sum over slabs of waves(launch) x K-length(launch) for the
   // dz (K = d), dW (K = chunk) and dH (K = slab / nsplit) GEMMs, and take the
-  // cheapest multiple of 256 up to the memory budget.
+  // cheapest multiple of 256 down to half the widest.
   auto waves = [](int64_t wg) { return (wg + kCUs - 1) / kCUs; };
   double best_cost = 0.0;
   p.vs = vs_max;
@@ -146,21 +175,7 @@ BwdPlan plan_bwd(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk) {
     }
   }
   p.nslabs = (V + p.vs - 1) / p.vs;
-  Carve c;
-  p.o_idx = c.take((size_t)N * 4);
-  p.o_cnt = c.take(4);
-  p.o_wt = c.take((size_t)(d * p.vpad) * es);
-  p.o_hact = c.take((size_t)(p.cpad * d) * es);
-  p.o_ht = c.take((size_t)(d * p.cpad) * es);
-  p.o_coef = c.take((size_t)p.cpad * 4);
-  p.o_lse = c.take((size_t)p.cpad * 4);
-  p.o_y = c.take((size_t)p.cpad * 4);
-  p.o_tgt = c.take((size_t)p.cpad * 4);
-  p.o_dz = c.take((size_t)(p.cpad * p.vs) * es);
-  p.o_dzt = c.take((size_t)(p.vs * p.cpad) * es);
-  p.o_dhacc = c.take((size_t)(p.nsplit * p.cpad * d) * 4);
-  p.o_seq = c.take((size_t)N * 4);   // per-sequence counts: B <= N sequences
-  p.total = c.off;
+  p.total = align_up(p.fixed + (size_t)(p.cpad * p.vs * es));
   return p;
 }
 
@@ -290,12 +305,10 @@ template <typename T>
 int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, const float* adv,
              const float* ref_lp, const float* lp, const float* lse, int64_t N, int64_t L,
              int64_t d, int64_t V, float beta, float grad_loss, int64_t chunk,
-             const grpo::LogitXform& xf, const grpo::LossVariant& lv, T* dH, float* dW, char* ws,
-             int dtype, hipStream_t s, const Fp8Recompute& f8 = Fp8Recompute()) {
-  const BwdPlan p = plan_bwd(N, d, V, dtype, chunk);
+             const grpo::LogitXform& xf, const grpo::LossVariant& lv, T* dH, float* dW,
+             const BwdPlan& p, char* ws, hipStream_t s, const Fp8Recompute& f8 = Fp8Recompute()) {
   int32_t* idx = (int32_t*)(ws + p.o_idx);
   int32_t* cnt = (int32_t*)(ws + p.o_cnt);
-  T* WT = (T*)(ws + p.o_wt);
   T* H_act = (T*)(ws + p.o_hact);
   T* HT = (T*)(ws + p.o_ht);
   float* coef = (float*)(ws + p.o_coef);
@@ -303,7 +316,6 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
   int32_t* y_c = (int32_t*)(ws + p.o_y);
   float* tgt_c = (float*)(ws + p.o_tgt);
   T* dZ = (T*)(ws + p.o_dz);
-  T* dZT = (T*)(ws + p.o_dzt);
   float* dH_acc = (float*)(ws + p.o_dhacc);
   int32_t* seq_n = lv.seq_mean ? (int32_t*)(ws + p.o_seq) : nullptr;
   const int64_t B = N / L;
@@ -311,7 +323,6 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
   GRPO_HIP(grpo::launch_zero(dH, (size_t)(N * d) * sizeof(T), s));
   GRPO_HIP(grpo::launch_active_scan(mask, N, idx, cnt, s));
   if (seq_n != nullptr) GRPO_HIP(grpo::launch_seq_counts(mask, B, L, seq_n, s));
-  GRPO_HIP(grpo::launch_transpose<T>(W, V, d, WT, p.vpad, s));
   // Chunks are planned for the worst case (every token active); chunks past
   // the device-side active count exit at once, so no host sync is needed.
   for (int64_t c = 0; c < p.nchunks; ++c) {
@@ -330,15 +341,15 @@ int bwd_pass(const T* H, const T* W, const int32_t* y, const uint8_t* mask, cons
       if (f8.W8 != nullptr)
         GRPO_HIP(grpo::launch_dz<uint8_t>(f8.W8, f8.H8_act, d, V, v0, vs_valid, (int)p.vs, cnt,
                                           c0, C, (int)p.cpad, xf, f8.w_scale, f8.hs_act, coef,
-                                          lse_c, y_c, tgt_c, (__bf16*)dZ, (__bf16*)dZT, s));
+                                          lse_c, y_c, tgt_c, (__bf16*)dZ, s));
       else
         GRPO_HIP(grpo::launch_dz<T>(W, H_act, d, V, v0, vs_valid, (int)p.vs, cnt, c0, C,
                                     (int)p.cpad, xf, nullptr, nullptr, coef, lse_c, y_c, tgt_c,
-                                    dZ, dZT, s));
-      GRPO_HIP(grpo::launch_dh_gemm<T>(WT, p.vpad, v0, vs_valid, dZ, (int)p.vs, d, cnt, c0, C,
-                                       (int)p.cpad, (int)p.nsplit, sl == 0 ? 1 : 0, dH_acc, s));
-      GRPO_HIP(grpo::launch_dw_gemm<T>(HT, (int)p.cpad, dZT, d, V, v0, vs_valid, cnt, c0, C, dW,
-                                       s));
+                                    dZ, s));
+      GRPO_HIP(grpo::launch_dh_gemm<T>(W, v0, vs_valid, dZ, (int)p.vs, d, cnt, c0, C, (int)p.cpad,
+                                       (int)p.nsplit, sl == 0 ? 1 : 0, dH_acc, s));
+      GRPO_HIP(grpo::launch_dw_gemm<T>(HT, (int)p.cpad, dZ, (int)p.vs, d, v0, vs_valid, cnt, c0,
+                                       C, dW, s));
     }
     GRPO_HIP(grpo::launch_dh_scatter<T>(dH_acc, (int)p.nsplit, (int)p.cpad, d, idx, cnt, c0, C, dH,
                                         s));
@@ -364,20 +375,26 @@ const char* grpo_strerror(int code) {
 const char* grpo_last_error(void) { return g_last_error; }
 
 // The fp8 backward runs the bf16 backward on exact bf16 copies of H and W,
-// kept after the bf16 plan's workspace.
+// which come first in its workspace; the bf16 plan (with its slab) follows.
 struct Fp8BwdPlan {
-  size_t o_h, o_w, o_h8act, o_hsact, total;
+  size_t o_h, o_w, o_h8act, o_hsact, o_bf16;
+  BwdPlan b;
+  size_t total;
 };
-Fp8BwdPlan plan_bwd_fp8(int64_t N, int64_t d, int64_t V, int64_t chunk) {
+// ws_bytes as for plan_bwd.
+Fp8BwdPlan plan_bwd_fp8(int64_t N, int64_t d, int64_t V, int64_t chunk, int64_t ws_bytes) {
   Fp8BwdPlan p{};
-  const BwdPlan b = plan_bwd(N, d, V, GRPO_BF16, chunk);
+  const int64_t cpad = round_up(std::min<int64_t>(chunk, N), grpo::kBN);
   Carve c;
-  c.off = b.total;
   p.o_h = c.take((size_t)(N * d) * 2);
   p.o_w = c.take((size_t)(V * d) * 2);
-  p.o_h8act = c.take((size_t)(b.cpad * d));      // one chunk of active fp8 rows
-  p.o_hsact = c.take((size_t)b.cpad * 4);
-  p.total = c.off;
+  p.o_h8act = c.take((size_t)(cpad * d));      // one chunk of active fp8 rows
+  p.o_hsact = c.take((size_t)cpad * 4);
+  p.o_bf16 = c.off;
+  int64_t rest = ws_bytes;
+  if (ws_bytes > 0) rest = ws_bytes > (int64_t)p.o_bf16 ? ws_bytes - (int64_t)p.o_bf16 : 1;
+  p.b = plan_bwd(N, d, V, GRPO_BF16, chunk, rest);
+  p.total = p.o_bf16 + p.b.total;
   return p;
 }
 
@@ -387,8 +404,11 @@ size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, 
     case GRPO_OP_REF:
     case GRPO_OP_FWD: return plan_fwd(N, V, chunk).total;
     case GRPO_OP_BWD:
-      return dtype == GRPO_FP8_E4M3 ? plan_bwd_fp8(N, d, V, chunk).total
-                                    : plan_bwd(N, d, V, dtype, chunk).total;
+    case GRPO_OP_BWD_MIN: {
+      const int64_t how = op == GRPO_OP_BWD ? 0 : -1;
+      return dtype == GRPO_FP8_E4M3 ? plan_bwd_fp8(N, d, V, chunk, how).total
+                                    : plan_bwd(N, d, V, dtype, chunk, how).total;
+    }
     default: fail(GRPO_ERR_INVALID_ARG, "unknown op %d", op); return 0;
   }
 }
@@ -537,18 +557,22 @@ int grpo_loss_bwd_ex(const void* H, const void* W, const int32_t* y, const uint8
   if (st != GRPO_OK) return st;
   if (!isfinite(beta)) return fail(GRPO_ERR_INVALID_ARG, "beta must be finite");
   if (!isfinite(grad_loss)) return fail(GRPO_ERR_INVALID_ARG, "grad_loss must be finite");
-  const size_t need = plan_bwd(N, d, V, dtype, chunk).total;
-  if (workspace == nullptr || workspace_bytes < need)
-    return fail(GRPO_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", need,
+  // a caller's size is always a size (>= 1 here): 0 and -1 select the default and
+  // minimum plans only in the workspace queries
+  const int64_t wsb = std::max<int64_t>(1, (int64_t)std::min<size_t>(workspace_bytes, (size_t)INT64_MAX));
+  const BwdPlan p = plan_bwd(N, d, V, dtype, chunk, workspace == nullptr ? 1 : wsb);
+  if (workspace == nullptr || !p.ok)
+    return fail(GRPO_ERR_WORKSPACE, "workspace needs at least %zu bytes, got %zu",
+                plan_bwd(N, d, V, dtype, chunk, -1).total,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   hipStream_t s = (hipStream_t)stream;
   if (dtype == GRPO_BF16)
     return bwd_pass<__bf16>((const __bf16*)H, (const __bf16*)W, y, mask, adv, ref_lp, lp, lse, N,
-                            L, d, V, beta, grad_loss, chunk, xf, lv, (__bf16*)dH, dW,
-                            (char*)workspace, dtype, s);
+                            L, d, V, beta, grad_loss, chunk, xf, lv, (__bf16*)dH, dW, p,
+                            (char*)workspace, s);
   return bwd_pass<float>((const float*)H, (const float*)W, y, mask, adv, ref_lp, lp, lse, N, L, d,
-                         V, beta, grad_loss, chunk, xf, lv, (float*)dH, dW, (char*)workspace,
-                         dtype, s);
+                         V, beta, grad_loss, chunk, xf, lv, (float*)dH, dW, p, (char*)workspace,
+                         s);
 }
 
 int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
@@ -707,9 +731,13 @@ int grpo_loss_bwd_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8
   if (st != GRPO_OK) return st;
   if (!isfinite(beta)) return fail(GRPO_ERR_INVALID_ARG, "beta must be finite");
   if (!isfinite(grad_loss)) return fail(GRPO_ERR_INVALID_ARG, "grad_loss must be finite");
-  const Fp8BwdPlan p = plan_bwd_fp8(N, d, V, chunk);
-  if (workspace == nullptr || workspace_bytes < p.total)
-    return fail(GRPO_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", p.total,
+  // a caller's size is always a size (>= 1 here): 0 and -1 select the default and
+  // minimum plans only in the workspace queries
+  const int64_t wsb = std::max<int64_t>(1, (int64_t)std::min<size_t>(workspace_bytes, (size_t)INT64_MAX));
+  const Fp8BwdPlan p = plan_bwd_fp8(N, d, V, chunk, workspace == nullptr ? 1 : wsb);
+  if (workspace == nullptr || !p.b.ok)
+    return fail(GRPO_ERR_WORKSPACE, "workspace needs at least %zu bytes, got %zu",
+                plan_bwd_fp8(N, d, V, chunk, -1).total,
                 workspace == nullptr ? (size_t)0 : workspace_bytes);
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -727,7 +755,7 @@ int grpo_loss_bwd_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8
   f8.H8_act = (uint8_t*)(ws + p.o_h8act);
   f8.hs_act = (float*)(ws + p.o_hsact);
   return bwd_pass<__bf16>(Hb, Wb, y, mask, adv, ref_lp, lp, lse, N, L, d, V, beta, grad_loss, chunk,
-                          xf, lv, (__bf16*)dH, dW, ws, GRPO_BF16, s, f8);
+                          xf, lv, (__bf16*)dH, dW, p.b, ws + p.o_bf16, s, f8);
 }
 
 int grpo_gemm_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int dtype,

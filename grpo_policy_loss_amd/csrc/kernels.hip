@@ -12,10 +12,12 @@
 //   (k_seq_counts: unmasked tokens per sequence, for the per-sequence mean.)
 // Backward (per chunk of ACTIVE tokens, per vocabulary slab):
 //   k_dz: the same tile recomputed; the epilogue forms
-//     dZ = c_t (onehot(y_t) - exp(z - lse_t)) in registers and stores it in
-//     H's dtype into a bounded [chunk x slab] buffer and its transpose.
-//   k_dh_gemm: dH_acc[t][:] (+)= sum_v dZ[t][v] W[v][:]   (MFMA, fp32 acc)
-//   k_dw_gemm: dW[v][:]     +=  sum_t dZ[t][v] h_t[:]     (MFMA, fp32 RMW)
+//     dZ = c_t (onehot(y_t) - exp(z - lse_t)) in registers and stores it once,
+//     in H's dtype, into a bounded token-major [chunk x slab] buffer.
+//   k_dh_gemm: dH_acc[t][:] (+)= sum_v dZ[t][v] W[v][:]   (MFMA, fp32 acc;
+//     W read K-major straight from the caller's [V, d] array)
+//   k_dw_gemm: dW[v][:]     +=  sum_t dZ[t][v] h_t[:]     (MFMA, fp32 RMW;
+//     the dZ slab read K-major)
 // Every reduction runs in a fixed order, so results are bitwise reproducible.
 #include <math.h>
 
@@ -667,7 +669,7 @@ __device__ __forceinline__ void dz_stage(const Acc& acc, int wave, int lane, int
 
 // T = uint8_t: the logits are recomputed from float8 e4m3 codes (w_scale[0] the
 // head's scale, hs_act[j] active token j's), exactly as the fp8 forward formed
-// them, and dZ / dZT are bfloat16; other T ignore both scale pointers.
+// them, and dZ is bfloat16; other T ignore both scale pointers.
 template <typename T, bool SC>
 __global__ void __launch_bounds__(kThreads, 1)
     k_dz(const T* __restrict__ W, const T* __restrict__ H_act, int64_t d, int64_t v0,
@@ -676,7 +678,7 @@ __global__ void __launch_bounds__(kThreads, 1)
          const float* __restrict__ hs_act, const float* __restrict__ coef,
          const float* __restrict__ lse_c,
          const int32_t* __restrict__ y_c, const float* __restrict__ tgt_c,
-         typename DzOut<T>::type* __restrict__ dZ, typename DzOut<T>::type* __restrict__ dZT) {
+         typename DzOut<T>::type* __restrict__ dZ) {
   constexpr bool kFp8 = std::is_same<T, uint8_t>::value;
   __shared__ __attribute__((aligned(1024))) char smem[kDzLdsBytes];
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
@@ -721,15 +723,11 @@ __global__ void __launch_bounds__(kThreads, 1)
         for (int u = 0; u < kAcc; ++u)
           q[u] = dz_value<SC>(acc[i][j][u], ct[j], lb[j], v + u, yl[j], vs_valid, xf);
         store4(dZ + (int64_t)t * vs + v, q[0], q[1], q[2], q[3]);
-#pragma unroll
-        for (int u = 0; u < kAcc; ++u) dZT[(int64_t)(v + u) * cpad + t] = to_elem<T>(q[u]);
       }
     }
     return;
   }
   typedef __attribute__((ext_vector_type(4))) int i32x4_t;
-  typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-  typedef __attribute__((ext_vector_type(8))) short s16x8_t;
   // 1. every entry as if it were not the target, -c_t p f'(z), rounded to bf16
   // and staged as [token][vocab]: each lane holds 4 consecutive vocabulary rows
   // of one token per block.  Rows past the slab (ragged last vocabulary tile)
@@ -748,38 +746,16 @@ __global__ void __launch_bounds__(kThreads, 1)
       *(__bf16 GRPO_LDS*)(lds + tl * kStagePitch + yr * 2) = (__bf16)tgt_c[n0 + tl];
   }
   __syncthreads();
-  // 3. dZ rows (token-major, vocabulary contiguous), 16 bytes per thread.  The
-  // slab (1-2 GB) is read back only after the whole launch, so its stores are
-  // non-temporal: they do not evict the W panels the other tiles re-read.
+  // 3. dZ rows (token-major, vocabulary contiguous), 16 bytes per thread: each
+  // token's 512 bytes are written whole by 32 consecutive threads.  The slab is
+  // read back only after the whole launch, so its stores are non-temporal: they
+  // do not evict the W panels the other tiles re-read.
 #pragma unroll 8
   for (int it = 0; it < kBN * 32 / kThreads; ++it) {
     const int idx = it * kThreads + (int)threadIdx.x;
     const int r = idx >> 5, c = idx & 31;
     __builtin_nontemporal_store(*(const i32x4_t GRPO_LDS*)(lds + r * kStagePitch + c * 16),
                                 (i32x4_t*)(dZ + (int64_t)(n0 + r) * vs + m0 + c * 8));
-  }
-  // 4. dZT rows (vocabulary-major, token contiguous) through transposed LDS reads.
-  // A 16-lane group moves one unit of 4 vocabulary rows x 32 tokens: lane m reads
-  // the 4 entries (4 vocabulary rows) of token 8 (m & 3) + (m >> 2) (and of the
-  // token 4 further), and ds_read_b64_tr_b16 hands lane m the 4 consecutive tokens
-  // 8 (m >> 2) + 0..3 (then + 4..7) of vocabulary row m & 3.
-  {
-    const int m = lane & 15;
-    const int rd = 8 * (m & 3) + (m >> 2);
-    constexpr int kGroups = kThreads / 16;   // 16-lane groups in the workgroup
-#pragma unroll 8
-    for (int it = 0; it < 512 / kGroups; ++it) {
-      const int u = it * kGroups + wave * 4 + (lane >> 4);
-      const int quad = u >> 3, blk = u & 7;   // one wave: 4 rows x 128 tokens
-      const char GRPO_LDS* src = lds + (32 * blk + rd) * kStagePitch + quad * 8;
-      const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GRPO_LDS s16x4_t*)src);
-      const s16x4_t hi =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((GRPO_LDS s16x4_t*)(src + 4 * kStagePitch));
-      const s16x8_t v8 = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      __builtin_nontemporal_store(
-          __builtin_bit_cast(i32x4_t, v8),
-          (i32x4_t*)(dZT + (int64_t)(m0 + 4 * quad + (m & 3)) * cpad + n0 + 32 * blk + 8 * (m >> 2)));
-    }
   }
 }
 
@@ -793,18 +769,26 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // drops its store, so there is no branch.  When accumulating, the 8 loads of
 // column block j+1 are in flight while block j is added and stored: one
 // memory round trip per block instead of one per load.
+// SW: the accumulators are in the transposed layout of tile_mainloop<..., SWAP>
+// (tile row r = its A index, columns m0 + its B index); acc[i][j] then plays
+// the part of acc[j][i] below.
+template <bool SW = false>
 __device__ __forceinline__ void store_tile_f32(float* base, int rows, int64_t m0, int64_t d,
                                                const Acc& acc, bool accumulate) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(base, (uint32_t)((int64_t)rows * d * (int64_t)sizeof(float)));
+  // tile row of block j's lane, and its first column in block i
+  const int wr = SW ? (wave >> 1) * 128 : (wave & 1) * 128;
+  const int wc = SW ? (wave & 1) * 128 : (wave >> 1) * 128;
   uint32_t coff[kWM];
 #pragma unroll
   for (int i = 0; i < kWM; ++i) {
-    const int64_t nd = m0 + acc_row(wave, lane, i, 0);   // 4 consecutive d
+    const int64_t nd = m0 + wc + 16 * i + 4 * (lane >> 4);   // 4 consecutive d
     coff[i] = nd < d ? (uint32_t)nd * 4u : kOOB;
   }
-  auto row_off = [&](int j) { return (uint32_t)acc_col(wave, lane, j) * (uint32_t)d * 4u; };
+  auto row_off = [&](int j) { return (uint32_t)(wr + 16 * j + (lane & 15)) * (uint32_t)d * 4u; };
+  auto blk = [&](int i, int j) -> const f32x4_t& { return SW ? acc[j][i] : acc[i][j]; };
   auto at = [](uint32_t r, uint32_t c) { return c == kOOB ? c : r + c; };
   if (!accumulate) {
 #pragma unroll
@@ -812,7 +796,7 @@ __device__ __forceinline__ void store_tile_f32(float* base, int rows, int64_t m0
       const uint32_t r = row_off(j);
 #pragma unroll
       for (int i = 0; i < kWM; ++i)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, acc[i][j]), rs,
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, blk(i, j)), rs,
                                                at(r, coff[i]), 0, 0);
     }
     return;
@@ -834,7 +818,7 @@ __device__ __forceinline__ void store_tile_f32(float* base, int rows, int64_t m0
     const uint32_t r = row_off(j);
 #pragma unroll
     for (int i = 0; i < kWM; ++i)
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, cur[i] + acc[i][j]), rs,
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, cur[i] + blk(i, j)), rs,
                                              at(r, coff[i]), 0, 0);
     if (j + 1 < kWN) {
 #pragma unroll
@@ -846,12 +830,13 @@ __device__ __forceinline__ void store_tile_f32(float* base, int rows, int64_t m0
 // dH partial of split `sp`: vocabulary columns [k0, k1) of the slab.  Split
 // sp accumulates into its own buffer dH_acc[sp], so no two workgroups ever
 // write the same element and the final sum over splits has a fixed order.
+// The GEMM's A operand (rows = hidden dimension, K = vocabulary) is W itself,
+// read K-major: no transposed copy of the head is made.
 template <typename T>
 __global__ void __launch_bounds__(kThreads, 1)
-    k_dh_gemm(const T* __restrict__ WT, int64_t vpad, int64_t v0, int vs_valid,
-              const T* __restrict__ dZ, int vs, int64_t d, const int32_t* __restrict__ count,
-              int64_t c0, int C, int cpad, int tm, int tn, int nsplit, int kchunk, int first,
-              float* __restrict__ dH_acc) {
+    k_dh_gemm(const T* __restrict__ W, int64_t v0, int vs_valid, const T* __restrict__ dZ, int vs,
+              int64_t d, const int32_t* __restrict__ count, int64_t c0, int C, int cpad, int tm,
+              int tn, int nsplit, int kchunk, int first, float* __restrict__ dH_acc) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
   int n_act = count[0] - (int)c0;
@@ -868,21 +853,29 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int k1 = (k0 + kchunk) < vs_valid ? (k0 + kchunk) : vs_valid;
   const int klen = k1 > k0 ? k1 - k0 : 0;
   const uint32_t kb = (uint32_t)(((int64_t)klen * (int64_t)sizeof(T) + 15) & ~(int64_t)15);
-  const Operand A{(const char*)(WT + m0 * vpad + v0 + k0), (uint32_t)(vpad * (int64_t)sizeof(T)),
-                  (int)((d - m0) < kBM ? (d - m0) : kBM), kb};
+  const int64_t ldw = d * (int64_t)sizeof(T);
+  Operand A{(const char*)(W + (v0 + k0) * d + m0), (uint32_t)ldw,
+            (int)((d - m0) < kBM ? (d - m0) : kBM), 0};
+  A.k_rows = (uint32_t)klen;
+  A.range = klen > 0 ? (uint32_t)((int64_t)klen * ldw - m0 * (int64_t)sizeof(T)) : 0u;
   const Operand B{(const char*)(dZ + (int64_t)n0 * vs + k0), (uint32_t)(vs * (int64_t)sizeof(T)),
                   n_act - n0, kb};
   Acc acc;
-  tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
+  tile_mainloop<T, true, false>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
   if (klen == 0 && !first) return;
 
   const int rows = (n_act - n0) < kBN ? (n_act - n0) : kBN;
   store_tile_f32(dH_acc + ((int64_t)sp * cpad + n0) * d, rows, m0, d, acc, !first);
 }
 
+// dW rows v0 + [m0, m0 + 256) (the GEMM's M = vocabulary) by hidden columns
+// [n0, n0 + 256) (N = hidden dimension), K = the chunk's active tokens: A is
+// the token-major dZ slab read K-major, B the transposed hidden-state chunk.
+// The blocks are computed transposed (SWAP), so each lane holds four
+// consecutive hidden columns of one vocabulary row, as dW's rows are laid out.
 template <typename T>
 __global__ void __launch_bounds__(kThreads, 1)
-    k_dw_gemm(const T* __restrict__ HT, int cpad, const T* __restrict__ dZT, int64_t d,
+    k_dw_gemm(const T* __restrict__ HT, int cpad, const T* __restrict__ dZ, int vs, int64_t d,
               int64_t v0, int vs_valid, const int32_t* __restrict__ count, int64_t c0, int C,
               int tm, int tn, float* __restrict__ dW) {
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
@@ -892,17 +885,20 @@ __global__ void __launch_bounds__(kThreads, 1)
   if (n_act <= 0) return;
   int mt, nt;
   tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
-  const int64_t m0 = (int64_t)mt * kBM;
-  const int n0 = nt * kBN;
+  const int m0 = mt * kBM;                  // first vocabulary row of the slab
+  const int64_t n0 = (int64_t)nt * kBN;     // first hidden column
   const uint32_t kb = (uint32_t)(((int64_t)n_act * (int64_t)sizeof(T) + 15) & ~(int64_t)15);
+  const int64_t ldz = (int64_t)vs * (int64_t)sizeof(T);
+  Operand A{(const char*)(dZ + m0), (uint32_t)ldz, vs_valid - m0, 0};
+  A.k_rows = (uint32_t)n_act;
+  A.range = (uint32_t)((int64_t)n_act * ldz - (int64_t)m0 * (int64_t)sizeof(T));
   const uint32_t ldb = (uint32_t)(cpad * (int64_t)sizeof(T));
-  const Operand A{(const char*)(HT + m0 * cpad), ldb, (int)((d - m0) < kBM ? (d - m0) : kBM), kb};
-  const Operand B{(const char*)(dZT + (int64_t)n0 * cpad), ldb, vs_valid - n0, kb};
+  const Operand B{(const char*)(HT + n0 * cpad), ldb, (int)((d - n0) < kBN ? (d - n0) : kBN), kb};
   Acc acc;
-  tile_mainloop<T>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
+  tile_mainloop<T, true, false, true>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
 
-  const int rows = (vs_valid - n0) < kBN ? (vs_valid - n0) : kBN;
-  store_tile_f32(dW + (v0 + n0) * d, rows, m0, d, acc, true);
+  const int rows = (vs_valid - m0) < kBM ? (vs_valid - m0) : kBM;
+  store_tile_f32<true>(dW + (v0 + m0) * d, rows, n0, d, acc, true);
 }
 
 template <typename T>
@@ -1168,19 +1164,18 @@ hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v
                      int vs, const int32_t* count, int64_t c0, int C, int cpad,
                      const LogitXform& xf, const float* w_scale, const float* hs_act,
                      const float* coef, const float* lse_c, const int32_t* y_c,
-                     const float* tgt_c, typename DzOut<T>::type* dZ,
-                     typename DzOut<T>::type* dZT, hipStream_t s) {
+                     const float* tgt_c, typename DzOut<T>::type* dZ, hipStream_t s) {
   ScopedKernelTimer timer_(KK_DZ, s);
   (void)V;
   const int tm = cdiv(vs_valid, kBM), tn = cdiv(C, kBN);
   if (xf.softcap)
     hipLaunchKernelGGL((k_dz<T, true>), dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0,
                        vs_valid, vs, count, c0, C, cpad, tm, tn, xf, w_scale, hs_act, coef, lse_c,
-                       y_c, tgt_c, dZ, dZT);
+                       y_c, tgt_c, dZ);
   else
     hipLaunchKernelGGL((k_dz<T, false>), dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0,
                        vs_valid, vs, count, c0, C, cpad, tm, tn, xf, w_scale, hs_act, coef, lse_c,
-                       y_c, tgt_c, dZ, dZT);
+                       y_c, tgt_c, dZ);
   return hipGetLastError();
 }
 
@@ -1210,27 +1205,25 @@ hipError_t launch_fp8_gather_rows(const uint8_t* H8, const float* h_scale, int64
 }
 
 template <typename T>
-hipError_t launch_dh_gemm(const T* WT, int64_t vpad, int64_t v0, int vs_valid, const T* dZ, int vs,
-                          int64_t d, const int32_t* count, int64_t c0, int C, int cpad,
-                          int nsplit, int first, float* dH_acc, hipStream_t s) {
+hipError_t launch_dh_gemm(const T* W, int64_t v0, int vs_valid, const T* dZ, int vs, int64_t d,
+                          const int32_t* count, int64_t c0, int C, int cpad, int nsplit, int first,
+                          float* dH_acc, hipStream_t s) {
   ScopedKernelTimer timer_(KK_DH_GEMM, s);
   const int tm = cdiv(d, kBM), tn = cdiv(C, kBN);
   // K range per split: a whole number of 64-element (128-byte bf16) slices
   const int kchunk = (int)(((int64_t)cdiv(vs_valid, nsplit) + 63) / 64 * 64);
-  hipLaunchKernelGGL(k_dh_gemm<T>, dim3(tm * tn * nsplit), dim3(kThreads), 0, s, WT, vpad, v0,
-                     vs_valid, dZ, vs, d, count, c0, C, cpad, tm, tn, nsplit, kchunk, first,
-                     dH_acc);
+  hipLaunchKernelGGL(k_dh_gemm<T>, dim3(tm * tn * nsplit), dim3(kThreads), 0, s, W, v0, vs_valid,
+                     dZ, vs, d, count, c0, C, cpad, tm, tn, nsplit, kchunk, first, dH_acc);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZT, int64_t d, int64_t V, int64_t v0,
+hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZ, int vs, int64_t d, int64_t v0,
                           int vs_valid, const int32_t* count, int64_t c0, int C, float* dW,
                           hipStream_t s) {
   ScopedKernelTimer timer_(KK_DW_GEMM, s);
-  (void)V;
-  const int tm = cdiv(d, kBM), tn = cdiv(vs_valid, kBN);
-  hipLaunchKernelGGL(k_dw_gemm<T>, dim3(tm * tn), dim3(kThreads), 0, s, HT, cpad, dZT, d, v0,
+  const int tm = cdiv(vs_valid, kBM), tn = cdiv(d, kBN);
+  hipLaunchKernelGGL(k_dw_gemm<T>, dim3(tm * tn), dim3(kThreads), 0, s, HT, cpad, dZ, vs, d, v0,
                      vs_valid, count, c0, C, tm, tn, dW);
   return hipGetLastError();
 }
@@ -1281,11 +1274,11 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
   template hipError_t launch_dz<T>(const T*, const T*, int64_t, int64_t, int64_t, int, int,       \
                                    const int32_t*, int64_t, int, int, const LogitXform&,         \
                                    const float*, const float*, const float*, const float*,        \
-                                   const int32_t*, const float*, T*, T*, hipStream_t);            \
-  template hipError_t launch_dh_gemm<T>(const T*, int64_t, int64_t, int, const T*, int, int64_t,  \
+                                   const int32_t*, const float*, T*, hipStream_t);                \
+  template hipError_t launch_dh_gemm<T>(const T*, int64_t, int, const T*, int, int64_t,           \
                                         const int32_t*, int64_t, int, int, int, int, float*,      \
                                         hipStream_t);                                             \
-  template hipError_t launch_dw_gemm<T>(const T*, int, const T*, int64_t, int64_t, int64_t, int,  \
+  template hipError_t launch_dw_gemm<T>(const T*, int, const T*, int, int64_t, int64_t, int,      \
                                         const int32_t*, int64_t, int, float*, hipStream_t);       \
   template hipError_t launch_dh_scatter<T>(const float*, int, int, int64_t, const int32_t*,      \
                                            const int32_t*, int64_t, int, T*, hipStream_t);        \
@@ -1298,7 +1291,7 @@ template hipError_t launch_dz<uint8_t>(const uint8_t*, const uint8_t*, int64_t, 
                                          int, int, const int32_t*, int64_t, int, int,
                                          const LogitXform&, const float*, const float*,
                                          const float*, const float*, const int32_t*, const float*,
-                                         __bf16*, __bf16*, hipStream_t);
+                                         __bf16*, hipStream_t);
 template hipError_t launch_lse_partials<uint8_t>(const uint8_t*, const uint8_t*, const int32_t*,
                                                  int64_t, int64_t, int, int, const LogitXform&,
                                                  const float*, const float*, float*, float*,

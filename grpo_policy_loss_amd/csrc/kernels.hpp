@@ -93,15 +93,14 @@ hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int3
 template <typename T> struct DzOut { typedef T type; };
 template <> struct DzOut<uint8_t> { typedef __bf16 type; };
 
-// T = uint8_t: fp8 operands (w_scale, hs_act as in k_lse_partials), bf16 dZ / dZT;
-// other T: both scale pointers unused (null).
+// dZ: the token-major [cpad, vs] slab.  T = uint8_t: fp8 operands (w_scale,
+// hs_act as in k_lse_partials), bf16 dZ; other T: both scale pointers unused (null).
 template <typename T>
 hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,
                      int vs, const int32_t* count, int64_t c0, int C, int cpad,
                      const LogitXform& xf, const float* w_scale, const float* hs_act,
                      const float* coef, const float* lse_c, const int32_t* y_c,
-                     const float* tgt_c, typename DzOut<T>::type* dZ,
-                     typename DzOut<T>::type* dZT, hipStream_t s);
+                     const float* tgt_c, typename DzOut<T>::type* dZ, hipStream_t s);
 
 // The fp8 codes and scales of chunk c's active tokens, for the fp8 recompute.
 hipError_t launch_fp8_gather_rows(const uint8_t* H8, const float* h_scale, int64_t d,
@@ -109,14 +108,17 @@ hipError_t launch_fp8_gather_rows(const uint8_t* H8, const float* h_scale, int64
                                   int cpad, uint8_t* H8_act, float* hs_act, hipStream_t s);
 
 // dH_acc holds nsplit partial buffers of [cpad, d] floats; split sp covers
-// one contiguous share of the slab's vocabulary columns.
+// one contiguous share of the slab's vocabulary columns.  W is the caller's
+// [V, d] head (read K-major); vs_valid * d * sizeof(T) must be < 2^31.
 template <typename T>
-hipError_t launch_dh_gemm(const T* WT, int64_t vpad, int64_t v0, int vs_valid, const T* dZ, int vs,
-                          int64_t d, const int32_t* count, int64_t c0, int C, int cpad,
-                          int nsplit, int first, float* dH_acc, hipStream_t s);
+hipError_t launch_dh_gemm(const T* W, int64_t v0, int vs_valid, const T* dZ, int vs, int64_t d,
+                          const int32_t* count, int64_t c0, int C, int cpad, int nsplit, int first,
+                          float* dH_acc, hipStream_t s);
 
+// dZ is the token-major [cpad, vs] slab (read K-major); C * vs * sizeof(T) must
+// be < 2^31.
 template <typename T>
-hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZT, int64_t d, int64_t V, int64_t v0,
+hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZ, int vs, int64_t d, int64_t v0,
                           int vs_valid, const int32_t* count, int64_t c0, int C, float* dW,
                           hipStream_t s);
 

@@ -48,6 +48,19 @@
 //          of its 4-float chunk l / 16 to MFMA e, so the four MFMAs together
 //          cover the 16 k of the step (in a permuted k order that A and B share).
 //
+//  * Either operand may instead be "K-major": stored k-row by k-row, the tile's
+//    256 rows (m or n) contiguous within each k-row (so an operand that is read
+//    transposed needs no transposed copy in memory).  A slice is then 64 k-rows
+//    (bf16; 32 for f32) of 512 B, copied by the same buffer-to-LDS instructions
+//    (two k-rows per instruction), its 32-byte blocks XOR-swizzled by the k-row.
+//    bf16 fragments come out of LDS through gfx950's transposing read
+//    ds_read_b64_tr_b16: within each 16-lane group, lane s addresses the four
+//    rows 4 (s % 4) .. + 3 of k-row s / 4 and receives element i of its own row
+//    at k-row i, so two such reads (k-rows +0..3 and +4..7) give a lane the
+//    eight consecutive k of its row that the MFMA takes.  The swizzle puts the
+//    eight k-rows a half-wave reads at one column into eight distinct 32-byte
+//    bank groups.  f32 fragments take four 4-byte reads.
+//
 // Output register layout (both MFMAs): lane l of wave w, block (i, j),
 // element e holds C[128 (w / 2) + 16 i + 4 (l / 16) + e][128 (w % 2) + 16 j + l % 16].
 #pragma once
@@ -96,13 +109,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
-// One operand's view for the loader: rows [row0, row0 + rows_valid) of a
-// row-major matrix with row pitch `ld_bytes`, k-bytes [0, k_bytes) valid.
+// One operand's view for the loader.
+// K-contiguous (the default): rows [row0, row0 + rows_valid) of a row-major
+// matrix with row pitch `ld_bytes`, k-bytes [0, k_bytes) valid.
+// K-major: `base` is the tile's first row (m or n) at k = 0, `ld_bytes` the
+// pitch between consecutive k, k-rows [0, k_rows) are valid and `range` is the
+// number of readable bytes from base (at most 2^31 - 1); everything past it
+// reads as zero.  (k_rows + 192) * ld_bytes must stay below 2^32 and 256
+// ld_bytes below 2^31.  Tile rows past the operand's end are read unmasked.
 struct Operand {
-  const char* base;      // address of row row0, column 0
-  uint32_t ld_bytes;     // row pitch in bytes
+  const char* base;
+  uint32_t ld_bytes;
   int rows_valid;        // rows of this tile that exist (may be <= 0)
-  uint32_t k_bytes;      // valid k extent in bytes (multiple of 16)
+  uint32_t k_bytes;      // K-contiguous: valid k extent in bytes (multiple of 16)
+  uint32_t k_rows = 0;   // K-major: valid k
+  uint32_t range = 0;    // K-major: readable bytes from base
 };
 
 // Each wave copies 64 rows of an operand slice: 8 DMA instructions, each
@@ -152,6 +173,116 @@ struct Loader {
   }
 };
 
+// Swizzle of a K-major slice: 32-byte block b of k-row r sits at block b ^ ksw(r).
+// A half-wave's transposing read touches k-rows {0..3} and {8..11} (+4, +32
+// multiples): ksw gives them the eight distinct values 0..7.
+__device__ __forceinline__ uint32_t ksw(uint32_t r) { return (r & 3u) | (((r >> 3) & 1u) << 2); }
+
+// Loader of a K-major operand slice (kBKB / sizeof(T) k-rows of 256 elements):
+// 8 DMA instructions per wave, each moving 1 KB into LDS at (8 wave + j) KB.
+// Lane i's 16 bytes land at physical chunk i of that KB; it loads the logical
+// chunk the swizzle puts there.  k-rows at or past k_rows read as zero (their
+// offset is at least the range).  Tile rows at or past rows_valid are not
+// masked: they read whatever lies there within the range, and feed only
+// output rows or columns the caller never stores.  (A masked offset of kOOB
+// would not do here: with a slice offset of up to ~2^31 added it could wrap
+// past 2^32 back into the range.)  Generic form (f32: one k-row per instruction).
+template <typename T>
+struct LoaderK {
+  static constexpr int kES = (int)sizeof(T);
+  static constexpr int kKS = kBKB / kES;        // k-rows per slice
+  static constexpr int kRB = kBM * kES;         // LDS bytes per k-row
+  static constexpr int kLPR = kRB / 16;         // lanes per k-row in one instruction
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t slice_bytes;     // global bytes between consecutive slices
+  uint32_t voff[8];         // byte offset of this lane's chunk in slice 0
+
+  __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
+    rsrc = make_rsrc(op.base, op.range);
+    slice_bytes = (uint32_t)__builtin_amdgcn_readfirstlane(kKS * op.ld_bytes);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t r = (uint32_t)((1024 / kRB) * (8 * wave + j) + lane / kLPR);
+      const uint32_t c = (uint32_t)(lane % kLPR);
+      const uint32_t mb = (((c >> 1) ^ ksw(r)) << 5) | ((c & 1u) << 4);
+      voff[j] = r * op.ld_bytes + mb;
+    }
+  }
+  // Copy instruction j of slice kt; k-rows past k_rows fall outside the range.
+  __device__ __forceinline__ void issue1(int kt, int j, char GRPO_LDS* tile, int wave) const {
+    char GRPO_LDS* dst = tile + (8 * wave + j) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16,
+                                             voff[j] + (uint32_t)kt * slice_bytes, 0, 0,
+                                             kCopyPolicy);
+  }
+  // A slice wholly inside k: the slice offset rides in the scalar offset.
+  __device__ __forceinline__ void issue1_full(int kt, int j, char GRPO_LDS* tile, int wave) const {
+    char GRPO_LDS* dst = tile + (8 * wave + j) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, voff[j],
+                                             (int)((uint32_t)kt * slice_bytes), 0, kCopyPolicy);
+  }
+  __device__ __forceinline__ void issue(int kt, char GRPO_LDS* tile, int wave) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue1(kt, j, tile, wave);
+  }
+  __device__ __forceinline__ static int full_slices(const Operand& op) {
+    return (int)(op.k_rows / (uint32_t)kKS);
+  }
+  // LDS byte offset of k-row r of a slice
+  __device__ __forceinline__ static uint32_t row_slot(uint32_t r) { return r * kRB; }
+};
+
+// bf16: a slice is 64 k-rows of 512 B, two per copy instruction.  The k-rows
+// sit in LDS in a permuted order so that the eight copies of one lane share a
+// swizzle and differ only by whole k-rows: k-row r lives in 512-byte slot
+//   slot(r) = r0 | r2 << 1 | r4 << 2 | r5 << 3 | r1 << 4 | r3 << 5   (r_i bit i of r)
+// so copy j of wave w, lane half h (lanes 32 h .. 32 h + 31) moves k-row
+//   h | w0 << 1 | w1 << 3 | j0 << 2 | j1 << 4 | j2 << 5,
+// whose swizzle bits (k-row bits 0, 1, 3) are the lane's own.  One offset
+// register per lane; the k-row and slice offsets travel in the scalar offset.
+template <>
+struct LoaderK<__bf16> {
+  static constexpr int kKS = 64;
+  __amdgpu_buffer_rsrc_t rsrc;
+  uint32_t ld;              // global bytes between consecutive k-rows
+  uint32_t voff;            // this lane's chunk in its first k-row
+
+  __device__ __forceinline__ static uint32_t row_of(int j) {   // k-row offset of copy j
+    return (uint32_t)(4 * (j & 1) + 16 * ((j >> 1) & 1) + 32 * (j >> 2));
+  }
+  __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
+    rsrc = make_rsrc(op.base, op.range);
+    ld = (uint32_t)__builtin_amdgcn_readfirstlane(op.ld_bytes);
+    const uint32_t h = (uint32_t)(lane >> 5), c = (uint32_t)(lane & 31);
+    const uint32_t r0 = h | (((uint32_t)wave & 1u) << 1) | (((uint32_t)wave >> 1) << 3);
+    const uint32_t mb = (((c >> 1) ^ ksw(r0)) << 5) | ((c & 1u) << 4);
+    voff = r0 * op.ld_bytes + mb;
+  }
+  __device__ __forceinline__ void issue1(int kt, int j, char GRPO_LDS* tile, int wave) const {
+    char GRPO_LDS* dst = tile + (8 * wave + j) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16,
+                                             voff + ((uint32_t)kt * 64u + row_of(j)) * ld, 0, 0,
+                                             kCopyPolicy);
+  }
+  __device__ __forceinline__ void issue1_full(int kt, int j, char GRPO_LDS* tile, int wave) const {
+    char GRPO_LDS* dst = tile + (8 * wave + j) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, voff,
+                                             (int)(((uint32_t)kt * 64u + row_of(j)) * ld), 0,
+                                             kCopyPolicy);
+  }
+  __device__ __forceinline__ void issue(int kt, char GRPO_LDS* tile, int wave) const {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) issue1(kt, j, tile, wave);
+  }
+  __device__ __forceinline__ static int full_slices(const Operand& op) {
+    return (int)(op.k_rows / 64u);
+  }
+  __device__ __forceinline__ static uint32_t row_slot(uint32_t r) {
+    return ((r & 1u) | ((r >> 2) & 1u) << 1 | ((r >> 4) & 1u) << 2 | ((r >> 5) & 1u) << 3 |
+            ((r >> 1) & 1u) << 4 | ((r >> 3) & 1u) << 5) * 512u;
+  }
+};
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt [3:0] and [15:14], expcnt
 // [6:4], lgkmcnt [11:8]); the counters not named are left unconstrained.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -174,28 +305,116 @@ __device__ __forceinline__ f32x4_t mfma_block(f32x4_t c, const f32x4_t& a, const
   return c;
 }
 
+// Fragment readers.  A wave's operand rows are row0 .. row0 + 127 of the tile
+// (row0 = 128 (wave / 2) for A, 128 (wave % 2) for B); fragment f covers rows
+// row0 + 16 f .. + 15; k-step s (0 or 1) is k-bytes 64 s .. 64 s + 63 of a slice.
+// Lane l gets row l % 16 of the fragment and k-chunk l / 16 of the k-step
+// (bf16: 8 consecutive k; f32: 4 consecutive k, element e feeding MFMA e).
+template <typename T, bool KMAJOR> struct Reader;
+
+// K-contiguous operand: one 16-byte read from the row-swizzled slice.
+template <typename T> struct Reader<T, false> {
+  typedef typename Frag<T>::type F;
+  uint32_t base, sw0, sw1;
+  __device__ __forceinline__ void init(int lane, int row0) {
+    base = (uint32_t)(row0 + (lane & 15)) * kBKB;
+    // fragment rows are 16-aligned blocks + lane % 16, so f(row) depends on the lane only
+    const uint32_t fr = (uint32_t)((lane & 7) ^ ((lane >> 3) & 1));
+    sw0 = ((0u + (uint32_t)(lane >> 4)) ^ fr) << 4;
+    sw1 = ((4u + (uint32_t)(lane >> 4)) ^ fr) << 4;
+  }
+  __device__ __forceinline__ void read(F& out, int f, const char GRPO_LDS* region, int s) const {
+    out = *(const F GRPO_LDS*)(region + base + f * 16 * kBKB + (s ? sw1 : sw0));
+  }
+};
+
+// K-major bf16 operand: two transposing 8-byte reads per fragment.  Lane s of a
+// 16-lane group g addresses rows 4 (s % 4) .. + 3 of k-row 8 g + s / 4 (and of
+// the k-row four further), and receives k 8 g .. 8 g + 7 of its own row.
+template <> struct Reader<__bf16, true> {
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+  uint32_t kb0;       // this lane's address of fragment 0, k-step 0, k-rows + 0..3
+  __device__ __forceinline__ void init(int lane, int row0) {
+    const uint32_t g = (uint32_t)(lane >> 4), sl = (uint32_t)(lane & 15);
+    // k-row 8 g + sl / 4 (+ 4 for the second read, + 32 in k-step 1): its swizzle
+    // (ksw) depends on the lane only, and the + 4 and + 32 move it by whole slots
+    const uint32_t r = 8u * g + (sl >> 2);
+    const uint32_t sw = ksw(r);
+    // bits 5..7 of the address are the swizzled block: fragment f is one XOR away
+    kb0 = LoaderK<__bf16>::row_slot(r) + (uint32_t)row0 * 2u + 8u * (sl & 3u) + (sw << 5);
+  }
+  // The two transposing reads of one fragment.  The builtin carries no alias
+  // information of its own, and an LDS read without any is taken to alias
+  // every buffer-to-LDS copy still in flight, so the compiler would wait for
+  // all of them (vmcnt(0)) before each read, exposing the copies' latency and
+  // more than doubling the loop time.  The restrict parameter gives both reads
+  // an alias scope once inlined, as the type-based metadata of the plain
+  // 16-byte reads does for them.  The loop's own waits and barriers order
+  // every read after the copies of the slice it reads.
+  __device__ __forceinline__ static bf16x8_t tr_pair(const char GRPO_LDS* __restrict__ p) {
+    const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GRPO_LDS bf16x4_t*)p);
+    const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((GRPO_LDS bf16x4_t*)(p + 1024));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  __device__ __forceinline__ void read(bf16x8_t& out, int f, const char GRPO_LDS* region,
+                                       int s) const {
+    // k-row + 32 s is slot bit 3 (4 KB), k-row + 4 slot bit 1 (1 KB)
+    out = tr_pair(region + (kb0 ^ ((uint32_t)f << 5)) + s * 4096);
+  }
+};
+
+// K-major f32 operand (small shapes only): four 4-byte reads, k-rows
+// 16 s + 4 g + e of the lane's row.
+template <> struct Reader<float, true> {
+  uint32_t g, col;
+  __device__ __forceinline__ void init(int lane, int row0) {
+    g = (uint32_t)(lane >> 4);
+    col = (uint32_t)(row0 + (lane & 15));
+  }
+  __device__ __forceinline__ void read(f32x4_t& out, int f, const char GRPO_LDS* region,
+                                       int s) const {
+    const uint32_t m = col + 16u * (uint32_t)f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t r = 16u * (uint32_t)s + 4u * g + (uint32_t)e;
+      out[e] = *(const float GRPO_LDS*)(region + r * (kBM * 4) + (((m >> 3) ^ ksw(r)) << 5) +
+                                        (m & 7u) * 4u);
+    }
+  }
+};
+
+template <typename T, bool KM> struct LoaderOf { typedef Loader type; };
+template <typename T> struct LoaderOf<T, true> { typedef LoaderK<T> type; };
+
+template <typename T, bool KM>
+__device__ __forceinline__ int full_slices(const Operand& op) {
+  if constexpr (KM) return LoaderK<T>::full_slices(op);
+  else return (int)(op.k_bytes / kBKB);
+}
+
 // One 64-byte k-step of the wave's 8 x 8 blocks, in a fixed order.  After
-// block q: for READ and even q < 32, LDS read q / 2 of the next k-step's
-// fragments (a0..a7, then b0..b7) from stage `rst` at chunk offset `sw`; for
-// COPY and q % 3 == 0, q < 48, copy instruction q / 3 of slice `ckt` into
-// stage `cst` (A rows for q / 3 < 8, then B rows), unchecked when FULL.
-template <typename T, bool READ, bool COPY, bool FULL = false>
+// block q: for READ and even q < 32, fragment q / 2 of k-step `rs` (a0..a7,
+// then b0..b7) from stage `rst`; for COPY and q % 3 == 0, q < 48, copy
+// instruction q / 3 of slice `ckt` into stage `cst` (A rows for q / 3 < 8,
+// then B rows), unchecked when FULL.  SWAP: each block is the MFMA of
+// (b[j], a[i]) instead of (a[i], b[j]), i.e. the block's transpose.
+template <typename T, bool READ, bool COPY, bool FULL, bool SWAP, typename LA, typename LB,
+          typename RA, typename RB>
 __device__ __forceinline__ void kstep(Acc& acc, const typename Frag<T>::type (&a)[kWM],
                                       const typename Frag<T>::type (&b)[kWN],
                                       typename Frag<T>::type (&na)[kWM], typename Frag<T>::type (&nb)[kWN],
-                                      const char GRPO_LDS* rst, uint32_t abase, uint32_t bbase,
-                                      uint32_t sw, const Loader& la, const Loader& lb, int ckt,
-                                      char GRPO_LDS* cst, int wave) {
-  typedef typename Frag<T>::type F;
+                                      const char GRPO_LDS* rst, int rs, const RA& ra, const RB& rb,
+                                      const LA& la, const LB& lb, int ckt, char GRPO_LDS* cst,
+                                      int wave) {
 #pragma unroll
   for (int q = 0; q < kWM * kWN; ++q) {
     const int i = q / kWN, j = q % kWN;
-    acc[i][j] = mfma_block(acc[i][j], a[i], b[j]);
+    acc[i][j] = SWAP ? mfma_block(acc[i][j], b[j], a[i]) : mfma_block(acc[i][j], a[i], b[j]);
     GRPO_FENCE();
     if (READ && (q & 1) == 0 && q < 32) {
       const int f = q >> 1;
-      if (f < kWM) na[f] = *(const F GRPO_LDS*)(rst + abase + f * 16 * kBKB + sw);
-      else nb[f - kWM] = *(const F GRPO_LDS*)(rst + kTileBytes + bbase + (f - kWM) * 16 * kBKB + sw);
+      if (f < kWM) ra.read(na[f], f, rst, rs);
+      else rb.read(nb[f - kWM], f - kWM, rst + kTileBytes, rs);
       GRPO_FENCE();
     }
     if (COPY && q % 3 == 0 && q < 48) {
@@ -212,9 +431,15 @@ __device__ __forceinline__ void kstep(Acc& acc, const typename Frag<T>::type (&a
   }
 }
 
-// The main loop.  `lds` must be kLdsBytes of workgroup memory.  On return no
-// copy is in flight; the caller must barrier before reusing LDS.
-template <typename T>
+// The main loop.  `lds` must be kLdsBytes of workgroup memory.  AK / BK: the
+// A / B operand is K-major (see Operand).  k_slices is the number of 128-byte
+// K slices (both operands must agree).  SWAP: every 16 x 16 block is computed
+// transposed, so lane l of wave w holds, in block (i, j), element e,
+//   C[128 (w / 2) + 16 i + l % 16][128 (w % 2) + 16 j + 4 (l / 16) + e]
+// (four consecutive B rows at one A row; the default layout is stated at the
+// top of this file).  On return no copy is in flight; the caller must barrier
+// before reusing LDS.
+template <typename T, bool AK = false, bool BK = false, bool SWAP = false>
 __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const Operand& B,
                                               int k_slices, char GRPO_LDS* lds) {
   typedef typename Frag<T>::type F;
@@ -227,15 +452,14 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
 #pragma unroll
       for (int e = 0; e < kAcc; ++e) acc[i][j][e] = 0.f;
   if (k_slices <= 0) return;
-  Loader la, lb;
+  typename LoaderOf<T, AK>::type la;
+  typename LoaderOf<T, BK>::type lb;
   la.init(A, wave, lane);
   lb.init(B, wave, lane);
-  const uint32_t abase = (uint32_t)((wave >> 1) * 128 + (lane & 15)) * kBKB;
-  const uint32_t bbase = (uint32_t)((wave & 1) * 128 + (lane & 15)) * kBKB;
-  // fragment rows are 16-aligned blocks + lane % 16, so f(row) depends on the lane only
-  const uint32_t fr = (uint32_t)((lane & 7) ^ ((lane >> 3) & 1));
-  const uint32_t sw0 = ((0u + (uint32_t)(lane >> 4)) ^ fr) << 4;
-  const uint32_t sw1 = ((4u + (uint32_t)(lane >> 4)) ^ fr) << 4;
+  Reader<T, AK> ra;
+  Reader<T, BK> rb;
+  ra.init(lane, (wave >> 1) * 128);
+  rb.init(lane, (wave & 1) * 128);
 
   // slices 0 and 1 (slice 1 reads as zeros when there is none)
   la.issue(0, lds, wave);
@@ -246,44 +470,43 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
   __builtin_amdgcn_s_barrier();
   F fa0[kWM], fb0[kWN], fa1[kWM], fb1[kWN];
 #pragma unroll
-  for (int f = 0; f < kWM; ++f) fa0[f] = *(const F GRPO_LDS*)(lds + abase + f * 16 * kBKB + sw0);
+  for (int f = 0; f < kWM; ++f) ra.read(fa0[f], f, lds, 0);
 #pragma unroll
-  for (int f = 0; f < kWN; ++f)
-    fb0[f] = *(const F GRPO_LDS*)(lds + kTileBytes + bbase + f * 16 * kBKB + sw0);
+  for (int f = 0; f < kWN; ++f) rb.read(fb0[f], f, lds + kTileBytes, 0);
 
   int kt = 0;
   // Slices wholly inside k in both operands take unchecked copies; the k tail
   // and the zero slices past it take the checked ones.
-  const int full_a = (int)(A.k_bytes / kBKB), full_b = (int)(B.k_bytes / kBKB);
+  const int full_a = full_slices<T, AK>(A), full_b = full_slices<T, BK>(B);
   const int full = full_a < full_b ? full_a : full_b;
   for (; kt + 2 < full; ++kt) {
     char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
     char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
     // k-step 0: read k-step 1's fragments of this slice
-    kstep<T, true, false>(acc, fa0, fb0, fa1, fb1, cur, abase, bbase, sw1, la, lb, 0, cur, wave);
+    kstep<T, true, false, false, SWAP>(acc, fa0, fb0, fa1, fb1, cur, 1, ra, rb, la, lb, 0, cur, wave);
     wait_vmem_all();   // this wave's copies of slice kt + 1 have landed
     wait_lds_all();
     __builtin_amdgcn_s_barrier();
     GRPO_FENCE();
     // k-step 1: read slice kt + 1's first fragments; copy slice kt + 2 into this
     // slice's stage
-    kstep<T, true, true, true>(acc, fa1, fb1, fa0, fb0, nxt, abase, bbase, sw0, la, lb, kt + 2, cur, wave);
+    kstep<T, true, true, true, SWAP>(acc, fa1, fb1, fa0, fb0, nxt, 0, ra, rb, la, lb, kt + 2, cur, wave);
   }
   for (; kt + 1 < k_slices; ++kt) {
     char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
     char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    kstep<T, true, false>(acc, fa0, fb0, fa1, fb1, cur, abase, bbase, sw1, la, lb, 0, cur, wave);
+    kstep<T, true, false, false, SWAP>(acc, fa0, fb0, fa1, fb1, cur, 1, ra, rb, la, lb, 0, cur, wave);
     wait_vmem_all();
     wait_lds_all();
     __builtin_amdgcn_s_barrier();
     GRPO_FENCE();
     // as above, checked (zeros past the end, drained below)
-    kstep<T, true, true>(acc, fa1, fb1, fa0, fb0, nxt, abase, bbase, sw0, la, lb, kt + 2, cur, wave);
+    kstep<T, true, true, false, SWAP>(acc, fa1, fb1, fa0, fb0, nxt, 0, ra, rb, la, lb, kt + 2, cur, wave);
   }
   {
     char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
-    kstep<T, true, false>(acc, fa0, fb0, fa1, fb1, cur, abase, bbase, sw1, la, lb, 0, cur, wave);
-    kstep<T, false, false>(acc, fa1, fb1, fa0, fb0, cur, abase, bbase, sw0, la, lb, 0, cur, wave);
+    kstep<T, true, false, false, SWAP>(acc, fa0, fb0, fa1, fb1, cur, 1, ra, rb, la, lb, 0, cur, wave);
+    kstep<T, false, false, false, SWAP>(acc, fa1, fb1, fa0, fb0, cur, 0, ra, rb, la, lb, 0, cur, wave);
   }
   wait_vmem_all();
 }

@@ -64,21 +64,32 @@ typedef enum {
   GRPO_ERR_HIP = -4          /* a HIP launch or runtime call failed */
 } grpo_status;
 
-typedef enum { GRPO_OP_REF = 0, GRPO_OP_FWD = 1, GRPO_OP_BWD = 2 } grpo_op;
+typedef enum {
+  GRPO_OP_REF = 0,     /* grpo_ref_logprobs */
+  GRPO_OP_FWD = 1,     /* grpo_loss_fwd */
+  GRPO_OP_BWD = 2,     /* grpo_loss_bwd, default (fastest) dZ slab */
+  GRPO_OP_BWD_MIN = 3  /* grpo_loss_bwd, the least workspace it accepts */
+} grpo_op;
 
 /*
  * Workspace bytes that grpo_ref_logprobs (op = GRPO_OP_REF), grpo_loss_fwd
- * (GRPO_OP_FWD) or grpo_loss_bwd (GRPO_OP_BWD) needs for these sizes.  The
- * workspace is caller-owned device memory with 256-byte alignment; its
- * contents on entry do not matter and are clobbered.  Returns 0 for invalid
- * arguments.  It never scales with N*V: the forward keeps only per-token
- * split partials of one chunk, the backward one bounded [chunk x V_s] slab
- * of dZ (and its transpose), a transposed copy of W and one chunk of hidden
- * states, plus 4 bytes per token for the per-sequence counts that the
- * per-sequence mean aggregation uses.  Each dZ slab is at most 2 GiB (V_s <= V), or at most
- * GRPO_SLAB_MIB MiB when that environment variable is set; a smaller budget
- * trades speed for memory.  The variable is read at every call: query the
- * workspace and run the backward under the same setting.
+ * (GRPO_OP_FWD) or grpo_loss_bwd (GRPO_OP_BWD, GRPO_OP_BWD_MIN) needs for
+ * these sizes.  The workspace is caller-owned device memory with 256-byte
+ * alignment; its contents on entry do not matter and are clobbered.  Returns
+ * 0 for invalid arguments.  It never scales with N*V: the forward keeps only
+ * per-token split partials of one chunk; the backward one chunk of hidden
+ * states (and its transpose), per-token scalars, float32 dH partials of one
+ * chunk, 8 bytes per token (active-token list, per-sequence counts) and one
+ * dZ slab: the token-major [chunk x V_s] gradient of V_s vocabulary columns of
+ * the chunk's logits, in H's dtype (bf16 for fp8), stored once.
+ * The backward plans V_s from the workspace_bytes it is passed: the widest
+ * multiple of 256 columns (up to the whole vocabulary) that fits, so a
+ * caller trades speed for memory by passing any size from
+ * grpo_workspace_bytes(GRPO_OP_BWD_MIN, ...) (one 256-column slab) up.
+ * GRPO_OP_BWD sizes a slab of at most 2 GiB (the whole vocabulary at the
+ * usual LM-head shapes and chunks up to 8192 tokens).  The slab's bytes
+ * (chunk x V_s) and V_s x d elements of W are each read through one buffer
+ * resource, so V_s is also capped below 2^31 bytes for both.
  */
 size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk);
 
@@ -95,7 +106,7 @@ size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, 
  * and at most N = B * L rounded up to 256, for which
  *   grpo_workspace_bytes(GRPO_OP_FWD, ...) + grpo_workspace_bytes(GRPO_OP_BWD, ...)
  * is at most budget_bytes; 256 if no candidate fits.  Pure host arithmetic:
- * no device call, deterministic for given arguments (and GRPO_SLAB_MIB).
+ * no device call, deterministic for given arguments.
  * The caller passes its own budget (for example part of the free HBM) and
  * then uses the result for the workspace query and every call.  Returns 0
  * for invalid arguments.
@@ -157,6 +168,10 @@ int grpo_loss_fwd(const void* H, const void* W, const int32_t* y, const uint8_t*
  *   dH [N, d] dtype, OVERWRITTEN (rows of masked tokens become 0).
  *   dW [V, d] float32, ACCUMULATED (+=): the caller zeroes it first for a
  *   plain gradient.
+ *   workspace_bytes: at least grpo_workspace_bytes(GRPO_OP_BWD_MIN, ...)
+ *   (GRPO_ERR_WORKSPACE otherwise); the dZ slab is planned from it (see
+ *   grpo_workspace_bytes), so results depend on it only through the
+ *   summation order of dH over slabs.
  */
 int grpo_loss_bwd(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
                   const float* adv, const float* ref_lp, const float* lp, const float* lse,

@@ -17,8 +17,22 @@ def to64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
 
-def gpu_chain(inp, w, beta=BETA, chunk=None, grad_loss=1.0, ref_from=None, opts=None):
-    """All outputs of the HIP path for inputs `inp` (tensors on the GPU)."""
+def bwd_workspace_for_slab(w, cols, chunk=None):
+    """A backward workspace (uint8, on the GPU) sized for a dZ slab of `cols`
+    vocabulary columns (a multiple of 256): the library plans its slab from the
+    workspace size it is given."""
+    chunk = w.chunk if chunk is None else chunk
+    dt = gp.GRPO_F32 if w.dtype == "f32" else gp.GRPO_BF16
+    cpad = -(-min(chunk, w.N) // 256) * 256
+    es = 4 if w.dtype == "f32" else 2
+    least = gp.grpo_workspace_bytes(gp.GRPO_OP_BWD_MIN, w.N, w.d, w.V, dt, chunk)
+    return torch.empty(least + (cols - 256) * cpad * es, dtype=torch.uint8, device="cuda")
+
+
+def gpu_chain(inp, w, beta=BETA, chunk=None, grad_loss=1.0, ref_from=None, opts=None,
+              ws_bwd=None):
+    """All outputs of the HIP path for inputs `inp` (tensors on the GPU).  ws_bwd:
+    the backward's workspace (None: the default size)."""
     chunk = w.chunk if chunk is None else chunk
     adv = gp.grpo_advantages(inp["rewards"], w.G, EPS)
     H_ref = inp["H_ref"] if ref_from is None else ref_from
@@ -26,7 +40,7 @@ def gpu_chain(inp, w, beta=BETA, chunk=None, grad_loss=1.0, ref_from=None, opts=
     loss, lp, kl, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref,
                                          w.B, w.L, beta, chunk, opts=opts)
     dH, dW = gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp, lse,
-                              w.B, w.L, beta, grad_loss, chunk, opts=opts)
+                              w.B, w.L, beta, grad_loss, chunk, opts=opts, workspace=ws_bwd)
     torch.cuda.synchronize()
     return dict(adv=adv, ref=ref, loss=loss, lp=lp, kl=kl, lse=lse, dH=dH, dW=dW)
 

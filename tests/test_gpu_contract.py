@@ -1,0 +1,129 @@
+"""GPU checks of the C ABI's own promises, called through ctypes where the
+binding would otherwise stand in between:
+
+  * the plain entry points (grpo_ref_logprobs, grpo_loss_fwd, grpo_loss_bwd)
+    give bitwise the results of their _ex forms with a NULL options pointer
+    (the binding itself always calls the _ex forms);
+  * the tiny float32 workload at its exact shape and chunk (512 tokens,
+    d 256, V 1024, chunk 128) against the float64 oracle, to relative 1e-5
+    on the loss and every lp;
+  * a NaN reward stays inside its own group of advantages;
+  * an out-of-range target (y < 0 or y >= V) gives lp = NaN at that token
+    and leaves every other token's lp, lse and ref bitwise unchanged."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_common import BETA, EPS, gpu_chain, max_abs_rel, oracle_chain, to64
+
+pytestmark = pytest.mark.gpu
+
+gp = pytest.importorskip("grpo_policy_loss_amd")
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ok(code):
+    assert code == 0, gp.lib().grpo_last_error().decode()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_plain_entry_points_equal_the_ex_forms_bitwise(dtype):
+    _need_gpu()
+    w = workloads.WORKLOADS[0].scaled(name="plain", prompts=2, G=3, L=100, d=320, V=1000,
+                                      dtype=dtype, chunk=256, len_lo=30, len_hi=100)
+    print(f"[plain] {dtype}", flush=True)
+    inp = workloads.generate(w, seed=31, device="cuda")
+    ex = gpu_chain(inp, w)                       # the binding: _ex forms, opts NULL
+    L = gp.lib()
+    dt = gp.GRPO_F32 if dtype == "f32" else gp.GRPO_BF16
+    N, d, V = w.N, w.d, w.V
+    dev = "cuda"
+    ws_f = torch.empty(gp.grpo_workspace_bytes(gp.GRPO_OP_FWD, N, d, V, dt, w.chunk),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(gp.grpo_workspace_bytes(gp.GRPO_OP_BWD, N, d, V, dt, w.chunk),
+                       dtype=torch.uint8, device=dev)
+    ref = torch.empty(N, device=dev)
+    loss = torch.empty(1, device=dev)
+    lp, kl, lse = (torch.empty(N, device=dev) for _ in range(3))
+    dH = torch.empty_like(inp["H"])
+    dW = torch.zeros(V, d, device=dev)
+    adv = ex["adv"]
+    _ok(L.grpo_ref_logprobs(_p(inp["H_ref"]), _p(inp["W"]), _p(inp["y"]), N, d, V, dt, w.chunk,
+                            _p(ref), _p(ws_f), ws_f.numel(), _stream()))
+    _ok(L.grpo_loss_fwd(_p(inp["H"]), _p(inp["W"]), _p(inp["y"]), _p(inp["mask"]), _p(adv),
+                        _p(ref), w.B, w.L, d, V, dt, BETA, w.chunk, _p(loss), _p(lp), _p(kl),
+                        _p(lse), _p(ws_f), ws_f.numel(), _stream()))
+    _ok(L.grpo_loss_bwd(_p(inp["H"]), _p(inp["W"]), _p(inp["y"]), _p(inp["mask"]), _p(adv),
+                        _p(ref), _p(lp), _p(lse), w.B, w.L, d, V, dt, BETA, 1.0, w.chunk, _p(dH),
+                        _p(dW), _p(ws_b), ws_b.numel(), _stream()))
+    torch.cuda.synchronize()
+    for k, got in (("ref", ref), ("loss", loss), ("lp", lp), ("kl", kl), ("lse", lse),
+                   ("dH", dH), ("dW", dW)):
+        assert torch.equal(got, ex[k]), k
+
+
+def test_tiny_f32_workload_exact_shape():
+    _need_gpu()
+    w = workloads.BY_NAME["tiny-f32"]
+    print(f"[tiny] N={w.N} d={w.d} V={w.V} chunk={w.chunk}", flush=True)
+    for seed in (0, 1):
+        inp = workloads.generate(w, seed=seed, device="cuda")
+        g = gpu_chain(inp, w)
+        o = oracle_chain(inp, w)
+        np.testing.assert_allclose(to64(g["adv"]), o["adv"], rtol=1e-6, atol=1e-6)
+        np.testing.assert_allclose(to64(g["lp"]), o["lp"], rtol=1e-5, atol=0)
+        np.testing.assert_allclose(to64(g["ref"]), o["ref"], rtol=1e-5, atol=0)
+        assert abs(g["loss"].item() - o["loss"]) <= 1e-5 * abs(o["loss"])
+        assert max_abs_rel(to64(g["dH"]), o["dH"]) <= 1e-4
+        assert max_abs_rel(to64(g["dW"]), o["dW"]) <= 1e-4
+
+
+def test_nan_reward_stays_in_its_group():
+    _need_gpu()
+    r = torch.tensor([0, 1, 2, 3, 1, float("nan"), 2, 0, 3, 3, 1, 0], dtype=torch.float32,
+                     device="cuda")
+    got = to64(gp.grpo_advantages(r, 4, EPS))
+    assert np.all(np.isnan(got[4:8]))
+    want = oracle.group_advantages(r.cpu().numpy(), 4, EPS)
+    np.testing.assert_allclose(got[:4], want[:4], rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(got[8:], want[8:], rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_out_of_range_target_gives_nan_lp_only_there(dtype):
+    _need_gpu()
+    w = workloads.WORKLOADS[0].scaled(name="oor", prompts=1, G=2, L=300, d=64, V=700,
+                                      dtype=dtype, chunk=256, len_lo=100, len_hi=300)
+    inp = workloads.generate(w, seed=32, device="cuda")
+    bad = torch.tensor([0, 5, 299, 300, 599], device="cuda")
+    y_bad = inp["y"].clone()
+    y_bad[bad] = torch.tensor([-1, w.V, w.V + 1000, -7, w.V], dtype=torch.int32, device="cuda")
+    adv = gp.grpo_advantages(inp["rewards"], w.G, EPS)
+    ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk)
+    ref_b = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], y_bad, w.chunk)
+    _, lp, _, lse = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, w.B,
+                                     w.L, BETA, w.chunk)
+    _, lp_b, _, lse_b = gp.grpo_loss_fwd(inp["H"], inp["W"], y_bad, inp["mask"], adv, ref, w.B,
+                                         w.L, BETA, w.chunk)
+    torch.cuda.synchronize()
+    good = torch.ones(w.N, dtype=torch.bool, device="cuda")
+    good[bad] = False
+    assert torch.all(torch.isnan(lp_b[bad])) and torch.all(torch.isnan(ref_b[bad]))
+    assert torch.equal(lp_b[good], lp[good]) and torch.equal(ref_b[good], ref[good])
+    assert torch.equal(lse_b, lse)           # the log-sum-exp does not involve the target

@@ -174,3 +174,71 @@ def test_fp8_full_size_sampled_parity():
     assert np.abs(g_ref - o_ref).max() <= 2e-4
     assert np.abs(g_lse - o_lse).max() <= 2e-4
     np.testing.assert_allclose(to64(kl)[rows], oracle.token_kl(g_ref, g_lp), rtol=1e-4, atol=1e-6)
+
+
+def test_fp8_full_size_backward_sampled_parity():
+    """Qwen2.5-1.5B shape through the fp8 forward and backward, in the launch
+    configuration `bench.py --fp8` times (chunk 4096): dH of 256 sampled active
+    rows of the dense run, and dW in full from a second backward whose mask keeps
+    a sparse set of tokens spread over every chunk, against the oracle on its own
+    dequantised H, H_ref and W."""
+    _need_gpu()
+    w = workloads.BY_NAME["qwen2.5-1.5b-bf16"]
+    print(f"[fp8-full-bwd] {w.name}", flush=True)
+    inp, Hq, Rq, Wq = _fp8_inputs(w, seed=25)
+    adv = gp.grpo_advantages(inp["rewards"], w.G, EPS)
+    ref = gp.grpo_ref_logprobs_fp8(Rq, Wq, inp["y"], w.chunk)
+    _, lp, _, lse = gp.grpo_loss_fwd_fp8(Hq, Wq, inp["y"], inp["mask"], adv, ref, w.B, w.L,
+                                         BETA, w.chunk)
+    dH, dW = gp.grpo_loss_bwd_fp8(Hq, Wq, inp["y"], inp["mask"], adv, ref, lp, lse, w.B, w.L,
+                                  BETA, 1.0, w.chunk)
+    rng = np.random.default_rng(26)
+    keep = set(int(x) for x in rng.choice(w.N, size=64, replace=False))
+    keep.update(c * w.chunk for c in range(w.N // w.chunk))
+    keep.add(w.N - 1)
+    keep = np.array(sorted(keep))
+    smask = torch.zeros(w.N, dtype=torch.uint8, device="cuda")
+    smask[torch.as_tensor(keep, device="cuda")] = 1
+    _, lp_s, _, lse_s = gp.grpo_loss_fwd_fp8(Hq, Wq, inp["y"], smask, adv, ref, w.B, w.L, BETA,
+                                             w.chunk)
+    dH_s, dW_s = gp.grpo_loss_bwd_fp8(Hq, Wq, inp["y"], smask, adv, ref, lp_s, lse_s, w.B, w.L,
+                                      BETA, 1.0, w.chunk)
+    torch.cuda.synchronize()
+
+    W64 = _oracle_w(inp["W"])
+    y = inp["y"].cpu().numpy().astype(np.int64)
+    mask = inp["mask"].cpu().numpy()
+    A = oracle.group_advantages(inp["rewards"].cpu().numpy(), w.G, EPS)
+
+    def rows64(X, rows):
+        return _oracle_deq(X[torch.as_tensor(rows, device="cuda")])
+
+    # dH rows of the dense run
+    act = np.nonzero(mask)[0]
+    drows = np.array(sorted(set(rng.choice(act, size=256, replace=False).tolist())))
+    H64 = np.zeros((w.N, w.d))
+    H64[drows] = rows64(inp["H"], drows)
+    ref64 = np.zeros(w.N)
+    ref64[drows], _ = oracle.token_logprobs(rows64(inp["H_ref"], drows), W64, y[drows])
+    o_dH, _ = oracle.loss_backward(H64, W64, y, mask, A, ref64, w.L, BETA, dh_rows=drows,
+                                   want_dW=False)
+    g_dH = to64(dH[torch.as_tensor(drows, device="cuda")])
+    print(f"[fp8-full-bwd] dH rows cos {cosine(g_dH, o_dH):.6f} "
+          f"maxrel {max_abs_rel(g_dH, o_dH):.2e}", flush=True)
+    assert cosine(g_dH, o_dH) >= 0.999
+    assert max_abs_rel(g_dH, o_dH) <= 1e-2
+    # full dW of the sparse-mask run
+    Hk = np.zeros((w.N, w.d))
+    Hk[keep] = rows64(inp["H"], keep)
+    refk = np.zeros(w.N)
+    refk[keep], _ = oracle.token_logprobs(rows64(inp["H_ref"], keep), W64, y[keep])
+    o_dHk, o_dW = oracle.loss_backward(Hk, W64, y, smask.cpu().numpy(), A, refk, w.L, BETA,
+                                       dh_rows=keep)
+    g_dW = to64(dW_s)
+    print(f"[fp8-full-bwd] dW cos {cosine(g_dW, o_dW):.6f} maxrel {max_abs_rel(g_dW, o_dW):.2e}",
+          flush=True)
+    assert cosine(g_dW, o_dW) >= 0.999
+    assert max_abs_rel(g_dW, o_dW) <= 1e-2
+    g_dHk = to64(dH_s[torch.as_tensor(keep, device="cuda")])
+    assert cosine(g_dHk, o_dHk) >= 0.999
+    assert max_abs_rel(g_dHk, o_dHk) <= 1e-2

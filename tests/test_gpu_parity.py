@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import workloads
-from tests.gpu_common import BETA, cosine, gpu_chain, max_abs_rel, oracle_chain, to64
+from tests.gpu_common import (BETA, bwd_workspace_for_slab, cosine, gpu_chain, max_abs_rel,
+                              oracle_chain, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,16 +77,17 @@ def test_advantages_match_oracle_and_degenerate_groups():
 
 
 # ----------------------------------------------------------------------------- full chain
-def test_chain_bf16_multiple_vocab_slabs(monkeypatch):
-    """bf16 path across slabs: with a 1 MiB slab budget a 256-token chunk holds at
-    most 2048 vocabulary rows, so V = 5000 needs three slabs (the last one ragged)
-    and the targets, uniform over V, fall in every slab."""
+@pytest.mark.parametrize("cols", [2048, 256])
+def test_chain_bf16_multiple_vocab_slabs(cols):
+    """bf16 path across slabs: a backward workspace with room for a slab of 2048
+    (or the minimum 256) vocabulary columns splits V = 5000 into three or more
+    slabs (the last one ragged), and the targets, uniform over V, fall in every
+    slab."""
     _need_gpu()
-    monkeypatch.setenv("GRPO_SLAB_MIB", "1")
     w = BASE.scaled(name="slabs-bf16", prompts=2, G=3, L=111, d=64, V=5000, dtype="bf16",
                     chunk=256, len_lo=50, len_hi=111)
     inp = inputs(w, seed=4)
-    g = gpu_chain(inp, w)
+    g = gpu_chain(inp, w, ws_bwd=bwd_workspace_for_slab(w, cols))
     o = oracle_chain(inp, w)
     assert abs(g["loss"].item() - o["loss"]) <= 2e-3 * abs(o["loss"])
     for k in ("dH", "dW"):
@@ -129,16 +131,15 @@ def test_chain_matches_oracle(dtype, chunk, d):
     assert np.all(to64(g["dH"])[~m] == 0.0)
 
 
-def test_chain_multiple_vocab_slabs_and_chunks(monkeypatch):
-    """With a 256 MiB slab budget a chunk of 8192 f32 tokens limits the dZ slab to
-    8192 vocabulary rows, so V = 20000 needs three slabs (the last one ragged);
-    8492 tokens need two chunks."""
+def test_chain_multiple_vocab_slabs_and_chunks():
+    """A backward workspace with room for 8192 vocabulary columns of a chunk of
+    8192 f32 tokens splits V = 20000 into three or more slabs (the last one
+    ragged); 8492 tokens need two chunks."""
     _need_gpu()
-    monkeypatch.setenv("GRPO_SLAB_MIB", "256")
     w = BASE.scaled(name="slabs", prompts=1, G=4, L=2123, d=32, V=20000, dtype="f32",
                     chunk=8192, len_lo=1000, len_hi=2123)
     inp = inputs(w, seed=2)
-    g = gpu_chain(inp, w)
+    g = gpu_chain(inp, w, ws_bwd=bwd_workspace_for_slab(w, 8192))
     o = oracle_chain(inp, w)
     np.testing.assert_allclose(to64(g["lp"]), o["lp"], rtol=1e-5, atol=0)
     assert abs(g["loss"].item() - o["loss"]) <= 1e-5 * abs(o["loss"])
