@@ -54,6 +54,9 @@ SIGNATURES = {
     "grpo_loss_bwd_ex": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                 _int, _f32, _f32, _i64, _OPTS_P, _vp, _vp, _vp, _sz, _vp]),
     "grpo_gemm_nt": (_int, [_vp, _vp, _i64, _i64, _i64, _int, _vp, _vp]),
+    "grpo_noalloc_scratch_bytes": (_sz, []),
+    "grpo_loss_fwd_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _int,
+                                     _f32, _i64, _OPTS_P, _vp, _vp, _vp, _vp, _vp]),
     "grpo_auto_chunk": (_i64, [_i64, _i64, _i64, _i64, _int, _sz]),
     "grpo_quantize_fp8_workspace_bytes": (_sz, []),
     "grpo_quantize_fp8": (_int, [_vp, _int, _i64, _i64, _int, _vp, _vp, _vp, _sz, _vp]),

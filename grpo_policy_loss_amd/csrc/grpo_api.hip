@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/grpo.h"
 #include "kernels.hpp"
@@ -756,6 +757,69 @@ int grpo_loss_bwd_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8
   f8.hs_act = (float*)(ws + p.o_hsact);
   return bwd_pass<__bf16>(Hb, Wb, y, mask, adv, ref_lp, lp, lse, N, L, d, V, beta, grad_loss, chunk,
                           xf, lv, (__bf16*)dH, dW, p.b, ws + p.o_bf16, s, f8);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- forward without allocation
+// grpo_loss_fwd_noalloc keeps the forward's per-chunk scratch (split partials,
+// target logits, loss block sums, per-sequence counts) in this file-scope
+// device array instead of a caller's workspace.  Each device that runs the
+// library holds its own copy, at its own address, until the process ends.
+// In host code `scratch` names a host-side stand-in: only the address from
+// hipGetSymbolAddress, taken once per device with that device current, is
+// ever handed to a kernel.
+namespace {
+constexpr size_t kScratchBytes = 64ull << 20;
+__device__ __align__(256) char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices];
+
+int device_scratch(char** out) {
+  int dev = -1;
+  GRPO_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(GRPO_ERR_UNSUPPORTED, "device %d is past the %d devices this library serves", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    GRPO_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (p == nullptr) return fail(GRPO_ERR_HIP, "hipGetSymbolAddress gave a null scratch address");
+    g_scratch_ptr[dev] = (char*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GRPO_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t grpo_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int grpo_loss_fwd_noalloc(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                          const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
+                          int64_t V, int dtype, float beta, int64_t chunk, const grpo_opts* opts,
+                          float* loss, float* lp, float* kl, float* lse, void* stream) {
+  g_last_error[0] = 0;
+  if (B <= 0 || L <= 0) return fail(GRPO_ERR_INVALID_ARG, "B and L must be positive");
+  if (B > INT32_MAX / L) return fail(GRPO_ERR_UNSUPPORTED, "B*L exceeds int32");
+  const int st = check_shape(B * L, d, V, dtype, chunk);
+  if (st != GRPO_OK) return st;
+  const size_t need = plan_fwd(B * L, V, chunk).total;
+  if (need > kScratchBytes)
+    return fail(GRPO_ERR_WORKSPACE,
+                "the forward needs %zu bytes of scratch at this V and chunk; the static scratch "
+                "holds %zu (use a smaller chunk, or grpo_loss_fwd with a workspace)",
+                need, kScratchBytes);
+  char* ws = nullptr;
+  const int sc = device_scratch(&ws);
+  if (sc != GRPO_OK) return sc;
+  // every scratch slot the kernels read is written earlier in the same call, so
+  // nothing needs clearing between calls
+  return grpo_loss_fwd_ex(H, W, y, mask, adv, ref_lp, B, L, d, V, dtype, beta, chunk, opts, loss,
+                          lp, kl, lse, ws, kScratchBytes, stream);
 }
 
 int grpo_gemm_nt(const void* A, const void* B, int64_t M, int64_t N, int64_t K, int dtype,

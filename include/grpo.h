@@ -303,6 +303,29 @@ int grpo_loss_bwd_fp8(const uint8_t* H8, const float* h_scale, const uint8_t* W8
                       size_t workspace_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * grpo_loss_fwd_ex without a workspace argument.  Its scratch is a static
+ * device array of grpo_noalloc_scratch_bytes() (64 MiB) that each GPU holds
+ * for the life of the process; it is located once per device (on the first
+ * call there, with that device current) and nothing is allocated, by the
+ * library or on its behalf, in any call.  Shapes whose forward workspace
+ * (grpo_workspace_bytes(GRPO_OP_FWD, ...)) exceeds it are rejected with
+ * GRPO_ERR_WORKSPACE before anything is enqueued; that allows chunks of up
+ * to 13 824 tokens at a 151 936-token vocabulary (10 496 at 201 088) for up to
+ * 163 840 flattened tokens.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and give undefined results.  Nothing in the scratch needs to
+ * start at zero.  Arguments and results are otherwise exactly those of
+ * grpo_loss_fwd_ex, whose kernels it runs.
+ */
+size_t grpo_noalloc_scratch_bytes(void);
+int grpo_loss_fwd_noalloc(const void* H, const void* W, const int32_t* y, const uint8_t* mask,
+                          const float* adv, const float* ref_lp, int64_t B, int64_t L, int64_t d,
+                          int64_t V, int dtype, float beta, int64_t chunk, const grpo_opts* opts,
+                          float* loss, float* lp, float* kl, float* lse, void* stream);
+
+/*
  * Diagnostic: C[M, N] (float32, row-major, written) = A[M, K] . B[N, K]^T,
  * through the same MFMA tile main loop the loss kernels use (A, B dtype
  * elements, both rows contiguous along K).  K times the element size must be
