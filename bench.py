@@ -189,6 +189,104 @@ def cpu_model():
     return "unknown"
 
 
+GEMM_KERNELS = ("lse_partials", "dz", "dh_gemm", "dw_gemm")
+NUM_SIMDS = 1024          # MI355X: 256 CUs x 4 SIMDs
+
+
+def summarize_counters(csv_paths, workload, steps, warmup, out_name):
+    """Per-kernel averages of the counters in one or more rocprofv3 --pmc runs of
+    this benchmark (each counter summed over its hardware instances per
+    dispatch, then averaged over the kernel's dispatches), with the derived
+    MFMA figures: executed MFMA flops (SQ_INSTS_VALU_MFMA_MOPS_BF16 counts 512
+    flops) against the algorithmic flops of a dispatch, the fraction of SIMD
+    cycles the matrix core is busy (SQ_VALU_MFMA_BUSY_CYCLES over NUM_SIMDS x
+    GRBM_GUI_ACTIVE of one XCD: rocprofv3 reports the sum over the 8), and the LDS
+    bank-conflict cycles per active LDS cycle."""
+    import workloads
+
+    w = workloads.BY_NAME[workload]
+    per = {}          # (kernel, dispatch) -> {counter: value}
+    for path in csv_paths:
+        for r in csv.DictReader(open(path)):
+            # demangled ("ns::k_name(...)") or mangled ("..._114k_nameIDF16b...") names
+            m = re.search(r"(?<![a-z])k_([a-z0-9_]+)", r["Kernel_Name"])
+            if not m:
+                continue
+            key = (m.group(1), int(r["Dispatch_Id"]), path)
+            d = per.setdefault(key, {})
+            if "Start_Timestamp" in r and r["Start_Timestamp"]:
+                d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+            c = r["Counter_Name"]
+            d[c] = d.get(c, 0.0) + float(r["Counter_Value"])
+            if c == "GRBM_GUI_ACTIVE":
+                d["_gui_n"] = d.get("_gui_n", 0) + 1
+                d["_xcd"] = 8          # one value summed over the 8 XCDs
+    kern = {}
+    for (k, _, _), d in per.items():
+        agg = kern.setdefault(k, {})
+        for c, v in d.items():
+            if c in ("_gui_n", "_xcd") or (c == "_ns" and "GRBM_GUI_ACTIVE" not in d):
+                continue
+            if c == "GRBM_GUI_ACTIVE":
+                v = v / d["_xcd"]       # cycles of one XCD
+            agg.setdefault(c, []).append(v)
+    N_act = None
+    lines = [f"# Hardware counters per kernel on the {workload} workload", "",
+             f"Workload: {w.N:,} flattened tokens, d = {w.d}, V = {w.V:,}, chunk {w.chunk}; "
+             f"{steps} step(s) after {warmup} warm-up, every dispatch of the library's kernels "
+             "counted (launches of the backward past the last active chunk do no work and are "
+             "left out of the averages).", "",
+             "Commands (repo root on the GPU box, `R` = repo root), one counter set per run:", "", "```",
+             "cd /tmp && export TMPDIR=/tmp"]
+    for i, pth in enumerate(csv_paths):
+        lines.append(f"rocprofv3 --pmc <set {i + 1}> --output-format csv -d $R/gpurun_out/pmc{i + 1} "
+                     f"-o run -- python3 $R/bench.py --workload {workload} --steps {steps} "
+                     f"--warmup {warmup} --no-cpu-baseline")
+    lines.append(f"python3 $R/bench.py --summarize-counters <the csv files> --workload {workload} "
+                 f"--steps {steps} --warmup {warmup} --counters-name {out_name}")
+    lines += ["```", ""]
+    counters = sorted({c for agg in kern.values() for c in agg if not c.startswith("_")})
+    lines.append("Counter sets: " + ", ".join(f"`{c}`" for c in counters))
+    lines += ["", "| kernel | dispatches | " + " | ".join(counters) + " |",
+              "|---|---|" + "---|" * len(counters)]
+    rows = {}
+    for k in sorted(kern):
+        agg = kern[k]
+        # drop dispatches that did no MFMA work (backward launches past the last active chunk)
+        mops = agg.get("SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        def mean(c):
+            v = agg[c]
+            if mops is not None and len(mops) == len(v) and k in GEMM_KERNELS:
+                v = [x for x, mm in zip(v, mops) if mm > 0] or v
+            return sum(v) / len(v)
+        n = len(next(iter(agg.values())))
+        rows[k] = {c: mean(c) for c in agg}
+        lines.append(f"| `k_{k}` | {n} | " + " | ".join(
+            f"{rows[k][c]:.4g}" if c in rows[k] else "" for c in counters) + " |")
+    if any("SQ_INSTS_VALU_MFMA_MOPS_BF16" in r for r in rows.values()):
+        lines += ["", "Derived, per dispatch that did work:", "",
+                  "| kernel | executed MFMA TFLOP | matrix core busy | clock (GHz, GUI cycles / time) | LDS bank-conflict cycles per LDS cycle |",
+                  "|---|---|---|---|---|"]
+        for k, r in rows.items():
+            if k not in GEMM_KERNELS:
+                continue
+            ex = r.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512 / 1e12
+            busy = (r["SQ_VALU_MFMA_BUSY_CYCLES"] / (NUM_SIMDS * r["GRBM_GUI_ACTIVE"])
+                    if "SQ_VALU_MFMA_BUSY_CYCLES" in r and r.get("GRBM_GUI_ACTIVE") else None)
+            conf = (r["SQ_LDS_BANK_CONFLICT"] / r["SQ_LDS_IDX_ACTIVE"]
+                    if r.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in r else None)
+            clk = (r["GRBM_GUI_ACTIVE"] / r["_ns"]) if r.get("_ns") and "GRBM_GUI_ACTIVE" in r else None
+            lines.append(f"| `k_{k}` | {ex:.4f} | " + (f"{busy:.1%}" if busy is not None else "") +
+                         " | " + (f"{clk:.2f}" if clk else "") + " | " +
+                         (f"{conf:.3f}" if conf is not None else "") + " |")
+    lines.append("")
+    lines.append("source_hash: " + kernel_source_hash())
+    path = os.path.join(PROFILES, f"counters_{out_name}.md")
+    with open(path, "w") as fo:
+        fo.write("\n".join(lines) + "\n")
+    print(path)
+
+
 def alg_flops(kind, d, V, N, N_act):
     """Algorithmic MFMA flops of one step's launches of a kernel kind."""
     if kind == "lse_partials":          # reference pass + loss forward: 2 d V per token each
@@ -276,6 +374,11 @@ def main():
                     help="run a 1 GiB calibration copy and one reference pass, then exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two counter runs of --traffic-probe")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_CSV",
+                    help="write profiles/counters_<name>.md from rocprofv3 --pmc runs of this "
+                         "benchmark")
+    ap.add_argument("--counters-name", default=None,
+                    help="file stem for --summarize-counters (default: the workload name)")
     ap.add_argument("--summarize-stats", metavar="STATS_CSV",
                     help="write the kernel statistics summary from a rocprofv3 --stats run of "
                          "this benchmark (with the --workload/--steps/--warmup it ran with)")
@@ -287,6 +390,11 @@ def main():
                                ("kl_estimator", args.kl_estimator),
                                ("no_detach", int(args.no_detach)),
                                ("aggregation", int(args.sequence_mean))) if v} or None
+
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload, args.steps, args.warmup,
+                           args.counters_name or args.workload)
+        return
 
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.workload, args.steps, args.warmup, args.fp8)

@@ -193,8 +193,9 @@ int check_shape(int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk, bool 
   if (d % vec != 0)
     return fail(GRPO_ERR_UNSUPPORTED, "d=%lld must be a multiple of %lld for this dtype",
                 (long long)d, (long long)vec);
-  if (N > INT32_MAX || V > INT32_MAX || chunk > (1 << 24))
-    return fail(GRPO_ERR_UNSUPPORTED, "N, V must fit int32 and chunk <= 2^24");
+  if (N > INT32_MAX || V > INT32_MAX || d > INT32_MAX || chunk > (1 << 24))
+    return fail(GRPO_ERR_UNSUPPORTED, "N, V, d must fit int32 and chunk <= 2^24");
+  // every factor is below 2^31 here, so the product cannot overflow
   const int64_t cpad = round_up(std::min(chunk, N), grpo::kBN);
   const int64_t row_span = 256 * std::max<int64_t>(std::max(d, round_up(V, 256)), cpad) * 4;
   if (row_span >= (1ll << 31))

@@ -33,24 +33,31 @@ ScopedKernelTimer::ScopedKernelTimer(int kind, hipStream_t s) : kind_(kind), s_(
     start_ = nullptr;
     return;
   }
-  hipEventRecord(start_, s_);
+  if (hipEventRecord(start_, s_) != hipSuccess) {
+    (void)hipEventDestroy(start_);
+    start_ = nullptr;
+  }
 }
 
 ScopedKernelTimer::~ScopedKernelTimer() {
   if (start_ == nullptr) return;
   hipEvent_t stop = nullptr;
   if (hipEventCreate(&stop) != hipSuccess) {
-    hipEventDestroy(start_);
+    (void)hipEventDestroy(start_);
     return;
   }
-  hipEventRecord(stop, s_);
+  if (hipEventRecord(stop, s_) != hipSuccess) {   // an unrecorded pair is dropped
+    (void)hipEventDestroy(start_);
+    (void)hipEventDestroy(stop);
+    return;
+  }
   g_state.recs.push_back({kind_, start_, stop});
 }
 
 bool timing_begin() {
   for (auto& r : g_state.recs) {
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
   }
   g_state.recs.clear();
   g_state.on = true;
@@ -62,14 +69,14 @@ int timing_end(const char** names, int* launches, double* total_ms, int max) {
   int cnt[KK_COUNT] = {0};
   double ms[KK_COUNT] = {0.0};
   for (auto& r : g_state.recs) {
-    hipEventSynchronize(r.stop);
     float t = 0.f;
-    if (hipEventElapsedTime(&t, r.start, r.stop) == hipSuccess) {
+    if (hipEventSynchronize(r.stop) == hipSuccess &&
+        hipEventElapsedTime(&t, r.start, r.stop) == hipSuccess) {
       ms[r.kind] += t;
       cnt[r.kind] += 1;
     }
-    hipEventDestroy(r.start);
-    hipEventDestroy(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
   }
   g_state.recs.clear();
   int n = 0;
