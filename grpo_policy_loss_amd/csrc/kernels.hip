@@ -13,7 +13,9 @@
 // Backward (per chunk of ACTIVE tokens, per vocabulary slab):
 //   k_dz: the same tile recomputed; the epilogue forms
 //     dZ = c_t (onehot(y_t) - exp(z - lse_t)) in registers and stores it once,
-//     in H's dtype, into a bounded token-major [chunk x slab] buffer.
+//     in H's dtype, into a bounded [chunk x slab] buffer laid out in strips of
+//     256 vocabulary columns: strip s holds [cpad tokens][256] contiguously, so
+//     a tile's 256 x 256 block is one contiguous 128 KB store.
 //   k_dh_gemm: dH_acc[t][:] (+)= sum_v dZ[t][v] W[v][:]   (MFMA, fp32 acc;
 //     W read K-major straight from the caller's [V, d] array)
 //   k_dw_gemm: dW[v][:]     +=  sum_t dZ[t][v] h_t[:]     (MFMA, fp32 RMW;
@@ -722,7 +724,7 @@ __global__ void __launch_bounds__(kThreads, 1)
 #pragma unroll
         for (int u = 0; u < kAcc; ++u)
           q[u] = dz_value<SC>(acc[i][j][u], ct[j], lb[j], v + u, yl[j], vs_valid, xf);
-        store4(dZ + (int64_t)t * vs + v, q[0], q[1], q[2], q[3]);
+        store4(dZ + ((int64_t)(v >> 8) * cpad + t) * 256 + (v & 255), q[0], q[1], q[2], q[3]);
       }
     }
     return;
@@ -746,16 +748,17 @@ __global__ void __launch_bounds__(kThreads, 1)
       *(__bf16 GRPO_LDS*)(lds + tl * kStagePitch + yr * 2) = (__bf16)tgt_c[n0 + tl];
   }
   __syncthreads();
-  // 3. dZ rows (token-major, vocabulary contiguous), 16 bytes per thread: each
-  // token's 512 bytes are written whole by 32 consecutive threads.  The slab is
-  // read back only after the whole launch, so its stores are non-temporal: they
-  // do not evict the W panels the other tiles re-read.
+  // 3. The tile: tokens n0 .. n0 + 255 of strip m0 / 256, one contiguous
+  // 128 KB block (512 bytes per token), 16 bytes per thread.  The slab is read
+  // back only after the whole launch, so its stores are non-temporal: they do
+  // not evict the W panels the other tiles re-read.
+  typename DzOut<T>::type* const blk = dZ + ((int64_t)(m0 >> 8) * cpad + n0) * 256;
 #pragma unroll 8
   for (int it = 0; it < kBN * 32 / kThreads; ++it) {
     const int idx = it * kThreads + (int)threadIdx.x;
     const int r = idx >> 5, c = idx & 31;
     __builtin_nontemporal_store(*(const i32x4_t GRPO_LDS*)(lds + r * kStagePitch + c * 16),
-                                (i32x4_t*)(dZ + (int64_t)(n0 + r) * vs + m0 + c * 8));
+                                (i32x4_t*)(blk + r * 256 + c * 8));
   }
 }
 
@@ -858,10 +861,16 @@ __global__ void __launch_bounds__(kThreads, 1)
             (int)((d - m0) < kBM ? (d - m0) : kBM), 0};
   A.k_rows = (uint32_t)klen;
   A.range = klen > 0 ? (uint32_t)((int64_t)klen * ldw - m0 * (int64_t)sizeof(T)) : 0u;
-  const Operand B{(const char*)(dZ + (int64_t)n0 * vs + k0), (uint32_t)(vs * (int64_t)sizeof(T)),
-                  n_act - n0, kb};
+  // B: the slab's tokens n0 .. (rows), vocabulary columns from k0 (a multiple of
+  // 256: strip k0 / 256), read strip by strip
+  const int64_t strip = (int64_t)cpad * 256;   // elements of one 256-column strip
+  Operand B{(const char*)(dZ + (k0 >> 8) * strip + (int64_t)n0 * 256),
+            (uint32_t)(256 * sizeof(T)), n_act - n0, kb};
+  B.blk_stride = (uint32_t)(strip * (int64_t)sizeof(T));
+  const int64_t rest = ((int64_t)(vs >> 8) - (k0 >> 8)) * strip - (int64_t)n0 * 256;
+  B.range = rest > 0 ? (uint32_t)(rest * (int64_t)sizeof(T)) : 0u;   // 0: empty split
   Acc acc;
-  tile_mainloop<T, true, false>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
+  tile_mainloop<T, true, false, false, true>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
   if (klen == 0 && !first) return;
 
   const int rows = (n_act - n0) < kBN ? (n_act - n0) : kBN;
@@ -888,10 +897,11 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int m0 = mt * kBM;                  // first vocabulary row of the slab
   const int64_t n0 = (int64_t)nt * kBN;     // first hidden column
   const uint32_t kb = (uint32_t)(((int64_t)n_act * (int64_t)sizeof(T) + 15) & ~(int64_t)15);
-  const int64_t ldz = (int64_t)vs * (int64_t)sizeof(T);
-  Operand A{(const char*)(dZ + m0), (uint32_t)ldz, vs_valid - m0, 0};
+  // A: strip m0 / 256 of the slab, [tokens][256 vocabulary columns], K-major
+  const int64_t ldz = 256 * (int64_t)sizeof(T);
+  Operand A{(const char*)(dZ + (int64_t)(m0 >> 8) * cpad * 256), (uint32_t)ldz, vs_valid - m0, 0};
   A.k_rows = (uint32_t)n_act;
-  A.range = (uint32_t)((int64_t)n_act * ldz - (int64_t)m0 * (int64_t)sizeof(T));
+  A.range = (uint32_t)((int64_t)n_act * ldz);
   const uint32_t ldb = (uint32_t)(cpad * (int64_t)sizeof(T));
   const Operand B{(const char*)(HT + n0 * cpad), ldb, (int)((d - n0) < kBN ? (d - n0) : kBN), kb};
   Acc acc;
@@ -1210,8 +1220,8 @@ hipError_t launch_dh_gemm(const T* W, int64_t v0, int vs_valid, const T* dZ, int
                           float* dH_acc, hipStream_t s) {
   ScopedKernelTimer timer_(KK_DH_GEMM, s);
   const int tm = cdiv(d, kBM), tn = cdiv(C, kBN);
-  // K range per split: a whole number of 64-element (128-byte bf16) slices
-  const int kchunk = (int)(((int64_t)cdiv(vs_valid, nsplit) + 63) / 64 * 64);
+  // K range per split: a whole number of the slab's 256-column strips
+  const int kchunk = (int)(((int64_t)cdiv(vs_valid, nsplit) + 255) / 256 * 256);
   hipLaunchKernelGGL(k_dh_gemm<T>, dim3(tm * tn * nsplit), dim3(kThreads), 0, s, W, v0, vs_valid,
                      dZ, vs, d, count, c0, C, cpad, tm, tn, nsplit, kchunk, first, dH_acc);
   return hipGetLastError();

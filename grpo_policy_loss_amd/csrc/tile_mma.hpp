@@ -123,21 +123,41 @@ struct Operand {
   int rows_valid;        // rows of this tile that exist (may be <= 0)
   uint32_t k_bytes;      // K-contiguous: valid k extent in bytes (multiple of 16)
   uint32_t k_rows = 0;   // K-major: valid k
-  uint32_t range = 0;    // K-major: readable bytes from base
+  uint32_t range = 0;    // K-major, and K-contiguous with blk_stride: readable bytes from base
+  // K-contiguous, blocked along k: k is stored in blocks of 256 elements, block
+  // b of a row at base + b * blk_stride + row * ld_bytes (0: one block).  Rows
+  // are then read unmasked within `range` (they feed only output rows the
+  // caller does not store).
+  uint32_t blk_stride = 0;
 };
 
 // Each wave copies 64 rows of an operand slice: 8 DMA instructions, each
 // moving 8 rows x 128 B (lane i fills slot i & 7 of row i >> 3 of the group).
+// BLK: the operand is blocked along k (Operand::blk_stride).
+template <bool BLK = false>
 struct Loader {
   __amdgpu_buffer_rsrc_t rsrc;
   uint32_t chunk_bytes;     // logical 16-byte chunk this lane copies, even 8-row groups
   uint32_t chunk_bytes_odd; // the same for odd 8-row groups (f(r) flips bit 0)
   uint32_t k_bytes;
+  uint32_t blk_stride;      // blocked k (see Operand); 0 for one block
+  int blk_shift;            // log2 of the slices per block
   uint32_t voff[8];         // byte offset of this lane's row j plus its chunk (kOOB if absent)
 
-  __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
+  // byte offset of slice kt from the row start
+  __device__ __forceinline__ uint32_t slice_off(int kt) const {
+    if (!BLK) return (uint32_t)kt * kBKB;
+    return (uint32_t)(kt >> blk_shift) * blk_stride +
+           (uint32_t)(kt & ((1 << blk_shift) - 1)) * kBKB;
+  }
+  __device__ __forceinline__ void init(const Operand& op, int wave, int lane, int elem_bytes) {
     int rv = op.rows_valid < 0 ? 0 : (op.rows_valid > kBM ? kBM : op.rows_valid);
-    rsrc = make_rsrc(op.base, (uint32_t)rv * op.ld_bytes);
+    if (BLK) {
+      blk_stride = (uint32_t)__builtin_amdgcn_readfirstlane(op.blk_stride);
+      blk_shift = elem_bytes == 4 ? 3 : 2;   // a 256-element block is 8 (f32) or 4 (bf16) slices
+      rv = kBM;                              // unmasked rows, bounded by the range
+    }
+    rsrc = make_rsrc(op.base, BLK ? op.range : (uint32_t)rv * op.ld_bytes);
     const int r_in = lane >> 3;                          // row within an 8-row group
     chunk_bytes = (uint32_t)(((lane & 7) ^ r_in) << 4);  // slot lane & 7 holds chunk slot ^ f(r)
     chunk_bytes_odd = chunk_bytes ^ 16u;
@@ -154,7 +174,7 @@ struct Loader {
   // A slice past the end reads as zeros.
   __device__ __forceinline__ void issue1(int kt, int j, char GRPO_LDS* tile, int wave) const {
     const uint32_t kb = (uint32_t)kt * kBKB + ((j & 1) ? chunk_bytes_odd : chunk_bytes);
-    const uint32_t off = kb < k_bytes ? voff[j] + (uint32_t)kt * kBKB : kOOB;
+    const uint32_t off = kb < k_bytes ? voff[j] + slice_off(kt) : kOOB;
     char GRPO_LDS* dst = tile + (wave * 64 + j * 8) * kBKB;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, off, 0, 0, kCopyPolicy);
   }
@@ -164,8 +184,8 @@ struct Loader {
   // check counts the scalar offset.
   __device__ __forceinline__ void issue1_full(int kt, int j, char GRPO_LDS* tile, int wave) const {
     char GRPO_LDS* dst = tile + (wave * 64 + j * 8) * kBKB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, voff[j], kt * kBKB, 0,
-                                             kCopyPolicy);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (GRPO_LDS void*)dst, 16, voff[j],
+                                             (int)slice_off(kt), 0, kCopyPolicy);
   }
   __device__ __forceinline__ void issue(int kt, char GRPO_LDS* tile, int wave) const {
 #pragma unroll
@@ -197,7 +217,7 @@ struct LoaderK {
   uint32_t slice_bytes;     // global bytes between consecutive slices
   uint32_t voff[8];         // byte offset of this lane's chunk in slice 0
 
-  __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
+  __device__ __forceinline__ void init(const Operand& op, int wave, int lane, int) {
     rsrc = make_rsrc(op.base, op.range);
     slice_bytes = (uint32_t)__builtin_amdgcn_readfirstlane(kKS * op.ld_bytes);
 #pragma unroll
@@ -250,7 +270,7 @@ struct LoaderK<__bf16> {
   __device__ __forceinline__ static uint32_t row_of(int j) {   // k-row offset of copy j
     return (uint32_t)(4 * (j & 1) + 16 * ((j >> 1) & 1) + 32 * (j >> 2));
   }
-  __device__ __forceinline__ void init(const Operand& op, int wave, int lane) {
+  __device__ __forceinline__ void init(const Operand& op, int wave, int lane, int) {
     rsrc = make_rsrc(op.base, op.range);
     ld = (uint32_t)__builtin_amdgcn_readfirstlane(op.ld_bytes);
     const uint32_t h = (uint32_t)(lane >> 5), c = (uint32_t)(lane & 31);
@@ -383,8 +403,8 @@ template <> struct Reader<float, true> {
   }
 };
 
-template <typename T, bool KM> struct LoaderOf { typedef Loader type; };
-template <typename T> struct LoaderOf<T, true> { typedef LoaderK<T> type; };
+template <typename T, bool KM, bool BLK = false> struct LoaderOf { typedef Loader<BLK> type; };
+template <typename T, bool BLK> struct LoaderOf<T, true, BLK> { typedef LoaderK<T> type; };
 
 template <typename T, bool KM>
 __device__ __forceinline__ int full_slices(const Operand& op) {
@@ -432,14 +452,15 @@ __device__ __forceinline__ void kstep(Acc& acc, const typename Frag<T>::type (&a
 }
 
 // The main loop.  `lds` must be kLdsBytes of workgroup memory.  AK / BK: the
-// A / B operand is K-major (see Operand).  k_slices is the number of 128-byte
+// A / B operand is K-major (see Operand); BBLK: B is K-contiguous and blocked
+// along k (Operand::blk_stride).  k_slices is the number of 128-byte
 // K slices (both operands must agree).  SWAP: every 16 x 16 block is computed
 // transposed, so lane l of wave w holds, in block (i, j), element e,
 //   C[128 (w / 2) + 16 i + l % 16][128 (w % 2) + 16 j + 4 (l / 16) + e]
 // (four consecutive B rows at one A row; the default layout is stated at the
 // top of this file).  On return no copy is in flight; the caller must barrier
 // before reusing LDS.
-template <typename T, bool AK = false, bool BK = false, bool SWAP = false>
+template <typename T, bool AK = false, bool BK = false, bool SWAP = false, bool BBLK = false>
 __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const Operand& B,
                                               int k_slices, char GRPO_LDS* lds) {
   typedef typename Frag<T>::type F;
@@ -453,9 +474,9 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
       for (int e = 0; e < kAcc; ++e) acc[i][j][e] = 0.f;
   if (k_slices <= 0) return;
   typename LoaderOf<T, AK>::type la;
-  typename LoaderOf<T, BK>::type lb;
-  la.init(A, wave, lane);
-  lb.init(B, wave, lane);
+  typename LoaderOf<T, BK, BBLK>::type lb;
+  la.init(A, wave, lane, (int)sizeof(T));
+  lb.init(B, wave, lane, (int)sizeof(T));
   Reader<T, AK> ra;
   Reader<T, BK> rb;
   ra.init(lane, (wave >> 1) * 128);
@@ -551,7 +572,7 @@ template <bool PAR, bool READ, bool COPY, bool FULL, int RS, int CS>
 __device__ __forceinline__ void kstep_fp8(Acc& acc, i32x8_t (&fa)[9], const i32x8_t (&fbc)[8],
                                           i32x8_t (&fbn)[8], const char GRPO_LDS* lds,
                                           uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
-                                          const Loader& la, const Loader& lb, int ckt, int wave) {
+                                          const Loader<>& la, const Loader<>& lb, int ckt, int wave) {
   constexpr int kAoff = RS * kTileBytes, kBoff = (2 + RS) * kTileBytes;
   char GRPO_LDS* cstA = (char GRPO_LDS*)lds + CS * kTileBytes;
   char GRPO_LDS* cstB = (char GRPO_LDS*)lds + (2 + CS) * kTileBytes;
@@ -604,7 +625,7 @@ template <bool PAR, bool FULL>
 __device__ __forceinline__ void fp8_iter(Acc& acc, i32x8_t (&fa)[9], i32x8_t (&fbA)[8],
                                          i32x8_t (&fbB)[8], char GRPO_LDS* lds, int kt,
                                          uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1,
-                                         const Loader& la, const Loader& lb, int wave) {
+                                         const Loader<>& la, const Loader<>& lb, int wave) {
   // this iteration's stage is PAR (= kt & 1): it reads the other and refills its own
   slice_barrier();
   if (PAR)
@@ -628,9 +649,9 @@ __device__ __forceinline__ void tile_mainloop_fp8(Acc& acc, const Operand& A, co
 #pragma unroll
       for (int e = 0; e < kAcc; ++e) acc[i][j][e] = 0.f;
   if (k_slices <= 0) return;
-  Loader la, lb;
-  la.init(A, wave, lane);
-  lb.init(B, wave, lane);
+  Loader<> la, lb;
+  la.init(A, wave, lane, 1);
+  lb.init(B, wave, lane, 1);
   const uint32_t abase = (uint32_t)((wave >> 1) * 128 + (lane & 15)) * kBKB;
   const uint32_t bbase = (uint32_t)((wave & 1) * 128 + (lane & 15)) * kBKB;
   const uint32_t fr = (uint32_t)((lane & 7) ^ ((lane >> 3) & 1));
