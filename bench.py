@@ -81,7 +81,14 @@ def read_traffic(kernel, workload):
 def summarize_traffic(fetch_csv, write_csv, workload, kernel="lse_partials"):
     """Turn two rocprofv3 --pmc runs of `bench.py --traffic-probe` (FETCH_SIZE,
     then WRITE_SIZE, in KiB per dispatch) into profiles/traffic_<kernel>_<workload>.md.
-    Each counter is scaled by what it reads for the 1 GiB calibration copy."""
+    Each counter is scaled by what it reads for the 1 GiB calibration copy.
+    kernel "all": one file for each of the four GEMM kernels.  Launches of the
+    backward past the last active chunk do no work (and fetch almost nothing);
+    launches fetching under 1 % of the kernel's largest are left out."""
+    if kernel == "all":
+        for k in GEMM_KERNELS:
+            summarize_traffic(fetch_csv, write_csv, workload, k)
+        return
     def per_dispatch(path, counter):
         vals = {}
         for r in csv.DictReader(open(path)):
@@ -94,11 +101,16 @@ def summarize_traffic(fetch_csv, write_csv, workload, kernel="lse_partials"):
     w = per_dispatch(write_csv, "WRITE_SIZE")
     def pick(vals, pat):
         return [v for (d, n), v in sorted(vals.items(), key=lambda kv: int(kv[0][0])) if pat in n]
-    kpat = "k_" + kernel
+    kpat = "k_" + kernel + "<"
+    kmangled = "k_" + kernel + "I"
     copy_f, copy_w = pick(f, "copyBuffer"), pick(w, "copyBuffer")
-    kf, kw = pick(f, kpat), pick(w, kpat)
+    kf = pick(f, kpat) or pick(f, kmangled)
+    kw = pick(w, kpat) or pick(w, kmangled)
     if not (copy_f and copy_w and kf and kw):
         raise SystemExit("counter CSVs lack the calibration copy or the kernel")
+    if len(kf) == len(kw):
+        keep = [i for i, v in enumerate(kf) if v >= 0.01 * max(kf)]
+        kf, kw = [kf[i] for i in keep], [kw[i] for i in keep]
     scale_f = copy_f[-1] * 1024 / COPY_BYTES          # KiB counted per true byte read
     scale_w = copy_w[-1] * 1024 / COPY_BYTES
     fetch = sum(kf) / len(kf) * 1024 / scale_f
@@ -109,17 +121,17 @@ def summarize_traffic(fetch_csv, write_csv, workload, kernel="lse_partials"):
            "copy_fetch_scale": round(scale_f, 4), "copy_write_scale": round(scale_w, 4)}
     lines = [f"# HBM traffic of `k_{kernel}` on the {workload} workload", "",
              "Two counter runs of `bench.py --traffic-probe` (a 1 GiB device copy for calibration,",
-             "then one reference log-prob pass = one launch of the kernel per chunk), then this summary:", "",
+             "then one step: reference log-probs, loss forward, loss backward), then this summary:", "",
              "```",
              "cd /tmp && export TMPDIR=/tmp",
              f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/tf -o run -- python3 $R/bench.py --traffic-probe --workload {workload}",
              f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/tw -o run -- python3 $R/bench.py --traffic-probe --workload {workload}",
-             f"python3 $R/bench.py --summarize-traffic $R/gpurun_out/tf/run_counter_collection.csv $R/gpurun_out/tw/run_counter_collection.csv --workload {workload}",
+             f"python3 $R/bench.py --summarize-traffic $R/gpurun_out/tf/run_counter_collection.csv $R/gpurun_out/tw/run_counter_collection.csv --workload {workload} --traffic-kernel all",
              "```", "",
              "| quantity | value |", "|---|---|",
              f"| calibration copy: FETCH_SIZE KiB counted per true KiB read | {scale_f:.4f} |",
              f"| calibration copy: WRITE_SIZE KiB counted per true KiB written | {scale_w:.4f} |",
-             f"| launches measured | {len(kf)} |",
+             f"| launches measured (that did work) | {len(kf)} |",
              f"| FETCH_SIZE per launch (scaled) | {fetch / 1e6:.1f} MB |",
              f"| WRITE_SIZE per launch (scaled) | {write / 1e6:.1f} MB |",
              f"| HBM bytes per launch | {(fetch + write) / 1e6:.1f} MB |", "",
@@ -371,7 +383,7 @@ def main():
     ap.add_argument("--sequence-mean", action="store_true",
                     help="per-sequence mean aggregation instead of the token mean")
     ap.add_argument("--traffic-probe", action="store_true",
-                    help="run a 1 GiB calibration copy and one reference pass, then exit")
+                    help="run a 1 GiB calibration copy and one step, then exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the traffic summary from two counter runs of --traffic-probe")
     ap.add_argument("--summarize-counters", nargs="+", metavar="PMC_CSV",
@@ -379,6 +391,8 @@ def main():
                          "benchmark")
     ap.add_argument("--counters-name", default=None,
                     help="file stem for --summarize-counters (default: the workload name)")
+    ap.add_argument("--traffic-kernel", default="lse_partials",
+                    help="kernel for --summarize-traffic (without k_), or all four GEMM kernels")
     ap.add_argument("--summarize-stats", metavar="STATS_CSV",
                     help="write the kernel statistics summary from a rocprofv3 --stats run of "
                          "this benchmark (with the --workload/--steps/--warmup it ran with)")
@@ -401,7 +415,8 @@ def main():
         return
 
     if args.summarize_traffic:
-        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload)
+        summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.workload,
+                          args.traffic_kernel)
         return
 
     if args.gpus != 1:
@@ -441,19 +456,6 @@ def main():
     dW = torch.zeros(V, d, dtype=torch.float32, device=dev)
     dH = torch.empty_like(inp["H"])
     stream = torch.cuda.current_stream()
-
-    if args.traffic_probe:
-        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk, workspace=ws_f,
-                             opts=xopts)
-        torch.cuda.synchronize()
-        log("[bench] traffic probe done")
-        return
 
     def step_fp8(ev=None):
         if ev is not None:
@@ -500,6 +502,18 @@ def main():
         if ev is not None:
             ev[3].record(stream)
         return loss
+
+    if args.traffic_probe:
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        step()
+        torch.cuda.synchronize()
+        log("[bench] traffic probe done")
+        return
 
     for i in range(args.warmup):
         step()

@@ -87,3 +87,44 @@ def test_summarize_stats_table(tmp_path, monkeypatch):
 def test_committed_profiles_name_their_command(name):
     text = open(os.path.join(ROOT, "profiles", f"kernel_stats_{name}.md")).read()
     assert "rocprofv3 --kernel-trace --stats" in text and f"--workload {name}" in text
+
+
+def test_summarize_traffic_all_kernels_skips_idle_backward_launches(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    gib_kib = bench.COPY_BYTES / 1024
+    names = {k: f"_ZN4grpo12_GLOBAL__N_19k_{k}IDF16bEEvPKT_" for k in bench.GEMM_KERNELS}
+    rows_f = [(1, "__amd_rocclr_copyBuffer", gib_kib)]
+    rows_w = [(1, "__amd_rocclr_copyBuffer", gib_kib)]
+    disp = 2
+    for k, n in names.items():
+        # two working launches and one idle one (a backward chunk past the active tokens)
+        for val in (5000, 7000, 3):
+            rows_f.append((disp, n, val))
+            rows_w.append((disp, n, val / 10))
+            disp += 1
+    _counter_csv(tmp_path / "f.csv", "FETCH_SIZE", rows_f)
+    _counter_csv(tmp_path / "w.csv", "WRITE_SIZE", rows_w)
+    bench.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "wl", "all")
+    for k in bench.GEMM_KERNELS:
+        rec = json.loads(open(tmp_path / f"traffic_{k}_wl.md").read().split("traffic_record: ")[1])
+        assert rec["launches"] == 2
+        assert rec["fetch_bytes_per_launch"] == 6000 * 1024
+        assert rec["write_bytes_per_launch"] == 600 * 1024
+
+
+def test_summarize_counters_derives_mfma_busy_and_clock(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    n = "_ZN4grpo12_GLOBAL__N_114k_lse_partialsIDF16bLb0EEEvPKT_"
+    path = tmp_path / "pmc.csv"
+    with open(path, "w") as f:
+        f.write("Dispatch_Id,Kernel_Name,Counter_Name,Counter_Value,Start_Timestamp,End_Timestamp\n")
+        # one dispatch of 1 ms: 8 XCDs x 1.8e6 GUI cycles summed (1.8 GHz), matrix cores
+        # busy 1.2e6 cycles on each of the 1024 SIMDs, 1e9 MFMA flops
+        for c, v in (("GRBM_GUI_ACTIVE", 8 * 1.8e6), ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1.2e6),
+                     ("SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e9 / 512), ("SQ_LDS_IDX_ACTIVE", 100),
+                     ("SQ_LDS_BANK_CONFLICT", 25)):
+            f.write(f'7,"{n}",{c},{v},1000000,2000000\n')
+    bench.summarize_counters([str(path)], "tiny-f32", 1, 1, "wl")
+    text = open(tmp_path / "counters_wl.md").read()
+    row = [l for l in text.splitlines() if l.startswith("| `k_lse_partials` | 0.0010")][0]
+    assert "66.7%" in row and "1.80" in row and "0.250" in row
