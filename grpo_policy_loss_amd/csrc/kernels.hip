@@ -342,9 +342,9 @@ __global__ void __launch_bounds__(kThreads, 1)
 
   Acc acc;
   if constexpr (kFp8)
-    tile_mainloop_fp8(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+    tile_mainloop_fp8(acc, A, B, k_slices_of(rowb), lds);
   else
-    tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+    tile_mainloop<T>(acc, A, B, k_slices_of(rowb), lds);
   int yv[kWN];
   load_targets<kFp8>(y, n0, n_tok, yv);
   lse_epilogue<T, SC>(acc, mt, m0, mvalid, n0, n_tok, cpad, xf, w_scale, h_scale, yv,
@@ -696,9 +696,9 @@ __global__ void __launch_bounds__(kThreads, 1)
   const Operand B{(const char*)(H_act + (int64_t)n0 * d), rowb, n_act - n0, rowb};
   Acc acc;
   if constexpr (kFp8)
-    tile_mainloop_fp8(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+    tile_mainloop_fp8(acc, A, B, k_slices_of(rowb), lds);
   else
-    tile_mainloop<T>(acc, A, B, (int)((rowb + kBKB - 1) / kBKB), lds);
+    tile_mainloop<T>(acc, A, B, k_slices_of(rowb), lds);
 
   const int lane = kFp8 ? lane_fresh() : (int)(threadIdx.x & 63), wave = wave_id();
   float ct[kWN], lb[kWN], cs[kWN];
@@ -870,7 +870,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   const int64_t rest = ((int64_t)(vs >> 8) - (k0 >> 8)) * strip - (int64_t)n0 * 256;
   B.range = rest > 0 ? (uint32_t)(rest * (int64_t)sizeof(T)) : 0u;   // 0: empty split
   Acc acc;
-  tile_mainloop<T, true, false, false, true>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
+  tile_mainloop<T, true, false, false, true>(acc, A, B, k_slices_of(kb), lds);
   if (klen == 0 && !first) return;
 
   const int rows = (n_act - n0) < kBN ? (n_act - n0) : kBN;
@@ -905,7 +905,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   const uint32_t ldb = (uint32_t)(cpad * (int64_t)sizeof(T));
   const Operand B{(const char*)(HT + n0 * cpad), ldb, (int)((d - n0) < kBN ? (d - n0) : kBN), kb};
   Acc acc;
-  tile_mainloop<T, true, false, true>(acc, A, B, (int)((kb + kBKB - 1) / kBKB), lds);
+  tile_mainloop<T, true, false, true>(acc, A, B, k_slices_of(kb), lds);
 
   const int rows = (vs_valid - m0) < kBM ? (vs_valid - m0) : kBM;
   store_tile_f32<true>(dW + (v0 + m0) * d, rows, n0, d, acc, true);
@@ -950,7 +950,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   const Operand Ao{(const char*)(A + m0 * K), rowb, (int)((M - m0) < kBM ? (M - m0) : kBM), rowb};
   const Operand Bo{(const char*)(B + n0 * K), rowb, (int)((N - n0) < kBN ? (N - n0) : kBN), rowb};
   Acc acc;
-  tile_mainloop<T>(acc, Ao, Bo, (int)((rowb + kBKB - 1) / kBKB), lds);
+  tile_mainloop<T>(acc, Ao, Bo, k_slices_of(rowb), lds);
   const int lane = threadIdx.x & 63, wave = wave_id();
 #pragma unroll
   for (int i = 0; i < kWM; ++i)

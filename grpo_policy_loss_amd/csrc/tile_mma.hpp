@@ -14,14 +14,22 @@
 //  * K advances in 128-byte slices (64 bf16 or 32 f32), two k-steps of 64 bytes
 //    each.  Each slice of A and B (256 rows x 128 B = 32 KB each) is copied
 //    global -> LDS by the buffer unit directly (buffer_load_dwordx4 ... lds):
-//    no VGPR staging.  LDS is double buffered (2 x 64 KB).
-//  * Every instruction of a k-step is placed by hand (scheduling fences): the
-//    64 MFMAs of the step, one LDS fragment read for the next k-step after each
-//    even MFMA of its first half, and -- in the step after the slice barrier --
-//    one slice copy after every third MFMA from the first.  Left to itself the
-//    compiler clusters the copies (each needs its own M0 write) and the matrix
-//    core idles; the fixed order measured +8 points of bf16 peak over the
-//    compiler's schedule of the same loop.
+//    no VGPR staging.  A has three slice slots and B two (160 KB in all).
+//  * Slice kt: k-step 0 runs its 64 MFMAs, reads the fragments of k-step 1
+//    and copies A's slice kt + 2 into the third A slot (free since slice
+//    kt - 1 was consumed); then the slice barrier; k-step 1 runs its MFMAs,
+//    reads the fragments of slice kt + 1's k-step 0, and copies B's slice
+//    kt + 2 into the B slot that slice kt just left.  Each k-step thus carries
+//    8 copies and 16 fragment reads per wave, and every copy moves whole
+//    128-byte lines.  (With two slots for each operand all 16 copies of a
+//    slice fall into k-step 1, which then has twice the LDS and buffer-unit
+//    traffic of k-step 0; the even spread measured 3 to 6 % less kernel time.
+//    Four stages of one 64-byte k-step each spread the copies as well, but
+//    fetch half lines of K-contiguous rows and were 5 % slower there.)
+//  * Every instruction of a k-step is placed by hand (scheduling fences): a
+//    fragment read after each even MFMA of its first half and a copy after
+//    every eighth MFMA.  Left to itself the compiler clusters the copies (each
+//    needs its own M0 write) and the matrix core idles.
 //  * With one wave per SIMD, whatever sits between two MFMAs must issue within
 //    the 16 cycles of the first one.  A copy of a slice that lies wholly inside
 //    k therefore costs no vector instruction: each lane's row-and-chunk offset
@@ -30,10 +38,9 @@
 //    per copy, measured 3 to 5 points of peak) is left to the slices at and
 //    past the k tail.
 //  * Slice barrier after the first k-step: every wave then holds the slice's
-//    last fragments, so the stage is free for the copy of slice kt + 2, and
-//    (after each wave's own vmcnt wait) slice kt + 1 is visible.  Copies of
-//    slice kt + 2 go out during the second k-step of slice kt and are waited
-//    for one k-step later at the earliest.
+//    last fragments, so its B slot is free for the copy of slice kt + 2, and
+//    (after each wave's own vmcnt wait) slice kt + 1 is visible.  A copy of
+//    A is waited for three k-steps after it is issued, one of B two.
 //  * Out-of-range rows and k-columns read as zero: each operand is addressed
 //    through a buffer resource whose range ends at its last valid row, and an
 //    invalid row or column gets an offset past that range.  Tails in M, N
@@ -83,8 +90,9 @@ constexpr int kWM = 8;            // 16-row MFMA blocks per wave
 constexpr int kWN = 8;            // 16-col MFMA blocks per wave
 constexpr int kAcc = 4;           // accumulator values per block and lane
 constexpr int kTileBytes = kBM * kBKB;   // one operand slice in LDS: 32 KB
-constexpr int kStageBytes = 2 * kTileBytes;
-constexpr int kLdsBytes = 2 * kStageBytes;  // double buffered A + B: 128 KB
+constexpr int kASlots = 3, kBSlots = 2;
+constexpr int kBRegion = kASlots * kTileBytes;                // B's slots follow A's
+constexpr int kLdsBytes = (kASlots + kBSlots) * kTileBytes;   // 160 KB
 constexpr uint32_t kOOB = 0x80000000u;   // an offset past every resource range
 // Cache policy of the slice copies: sc1 (device scope) takes them past the per-CU L1.
 // Each workgroup streams its panels once per slice, so L1 allocation buys nothing;
@@ -93,6 +101,11 @@ constexpr uint32_t kOOB = 0x80000000u;   // an offset past every resource range
 constexpr int kCopyPolicy = 16;
 
 typedef f32x4_t Acc[kWM][kWN];
+
+// Number of 128-byte K slices that cover `bytes` of k.
+__host__ __device__ constexpr int k_slices_of(int64_t bytes) {
+  return (int)((bytes + kBKB - 1) / kBKB);
+}
 
 // Raw buffer resource: base, no stride, `bytes` valid bytes from base.  The
 // inputs are workgroup-uniform; readfirstlane makes that visible to the
@@ -312,12 +325,27 @@ __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC0
 
 #define GRPO_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// 32 wait states: more than any MFMA needs before a VALU or memory
+// instruction may read its result registers.
+__device__ __forceinline__ void mfma_drain() {
+  GRPO_FENCE();
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+  GRPO_FENCE();
+}
+
 template <typename T> struct Frag;
 template <> struct Frag<__bf16> { typedef bf16x8_t type; };
 template <> struct Frag<float> { typedef f32x4_t type; };
 
+// The bf16 MFMA accumulates in place: its result takes the accumulator's own
+// registers.  (With all 256 AGPRs holding accumulators, the compiler's free
+// choice of a result register other than the accumulator's leaves it
+// permuting accumulators through VGPRs inside the loop.)  The compiler does
+// not see this instruction as an MFMA, so it inserts no wait states for
+// reads of its result: the main loop ends with them (mfma_drain).
 __device__ __forceinline__ f32x4_t mfma_block(f32x4_t c, const bf16x8_t& a, const bf16x8_t& b) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  return c;
 }
 __device__ __forceinline__ f32x4_t mfma_block(f32x4_t c, const f32x4_t& a, const f32x4_t& b) {
 #pragma unroll
@@ -412,20 +440,23 @@ __device__ __forceinline__ int full_slices(const Operand& op) {
   else return (int)(op.k_bytes / kBKB);
 }
 
+// Position of the copies within a k-step: after MFMA q with q % 8 == kCopyAt.
+constexpr int kCopyAt = 4;
+
 // One 64-byte k-step of the wave's 8 x 8 blocks, in a fixed order.  After
 // block q: for READ and even q < 32, fragment q / 2 of k-step `rs` (a0..a7,
-// then b0..b7) from stage `rst`; for COPY and q % 3 == 0, q < 48, copy
-// instruction q / 3 of slice `ckt` into stage `cst` (A rows for q / 3 < 8,
-// then B rows), unchecked when FULL.  SWAP: each block is the MFMA of
-// (b[j], a[i]) instead of (a[i], b[j]), i.e. the block's transpose.
-template <typename T, bool READ, bool COPY, bool FULL, bool SWAP, typename LA, typename LB,
+// then b0..b7) from A's slot `ra_at` and B's slot `rb_at`; for q % 8 ==
+// kCopyAt, copy instruction q / 8 of slice `ckt` of A (COPY = 1) or of B
+// (COPY = 2) into slot `cst`, unchecked when FULL.  SWAP: each block is the
+// MFMA of (b[j], a[i]) instead of (a[i], b[j]), i.e. the block's transpose.
+template <typename T, bool READ, int COPY, bool FULL, bool SWAP, typename LA, typename LB,
           typename RA, typename RB>
 __device__ __forceinline__ void kstep(Acc& acc, const typename Frag<T>::type (&a)[kWM],
                                       const typename Frag<T>::type (&b)[kWN],
                                       typename Frag<T>::type (&na)[kWM], typename Frag<T>::type (&nb)[kWN],
-                                      const char GRPO_LDS* rst, int rs, const RA& ra, const RB& rb,
-                                      const LA& la, const LB& lb, int ckt, char GRPO_LDS* cst,
-                                      int wave) {
+                                      const char GRPO_LDS* ra_at, const char GRPO_LDS* rb_at, int rs,
+                                      const RA& ra, const RB& rb, const LA& la, const LB& lb, int ckt,
+                                      char GRPO_LDS* cst, int wave) {
 #pragma unroll
   for (int q = 0; q < kWM * kWN; ++q) {
     const int i = q / kWN, j = q % kWN;
@@ -433,22 +464,45 @@ __device__ __forceinline__ void kstep(Acc& acc, const typename Frag<T>::type (&a
     GRPO_FENCE();
     if (READ && (q & 1) == 0 && q < 32) {
       const int f = q >> 1;
-      if (f < kWM) ra.read(na[f], f, rst, rs);
-      else rb.read(nb[f - kWM], f - kWM, rst + kTileBytes, rs);
+      if (f < kWM) ra.read(na[f], f, ra_at, rs);
+      else rb.read(nb[f - kWM], f - kWM, rb_at, rs);
       GRPO_FENCE();
     }
-    if (COPY && q % 3 == 0 && q < 48) {
-      const int c = q / 3;
-      if (FULL) {
-        if (c < 8) la.issue1_full(ckt, c, cst, wave);
-        else lb.issue1_full(ckt, c - 8, cst + kTileBytes, wave);
+    if (COPY && (q & 7) == kCopyAt) {
+      const int c = q >> 3;
+      if (COPY == 1) {
+        if (FULL) la.issue1_full(ckt, c, cst, wave);
+        else la.issue1(ckt, c, cst, wave);
       } else {
-        if (c < 8) la.issue1(ckt, c, cst, wave);
-        else lb.issue1(ckt, c - 8, cst + kTileBytes, wave);
+        if (FULL) lb.issue1_full(ckt, c, cst, wave);
+        else lb.issue1(ckt, c, cst, wave);
       }
       GRPO_FENCE();
     }
   }
+}
+
+// The slice barrier: this wave's copies of slice kt + 1 have landed (the 8 of
+// A's slice kt + 2 may still fly) and its fragment reads are done.
+__device__ __forceinline__ void slice_sync() {
+  __builtin_amdgcn_s_waitcnt(0x0F78);   // vmcnt(8)
+  wait_lds_all();
+  __builtin_amdgcn_s_barrier();
+  GRPO_FENCE();
+}
+
+// One slice kt of the main loop (see the top of this file).  as/bs: the slots
+// of slices kt (A and B), an/bn: of slice kt + 1, af: A's free slot.
+template <typename T, bool FULL, bool SWAP, typename LA, typename LB, typename RA, typename RB,
+          typename F>
+__device__ __forceinline__ void slice_step(Acc& acc, F (&fa0)[kWM], F (&fb0)[kWN], F (&fa1)[kWM],
+                                           F (&fb1)[kWN], char GRPO_LDS* as, char GRPO_LDS* bs,
+                                           char GRPO_LDS* an, char GRPO_LDS* bn,
+                                           char GRPO_LDS* af, const RA& ra, const RB& rb,
+                                           const LA& la, const LB& lb, int kt, int wave) {
+  kstep<T, true, 1, FULL, SWAP>(acc, fa0, fb0, fa1, fb1, as, bs, 1, ra, rb, la, lb, kt + 2, af, wave);
+  slice_sync();
+  kstep<T, true, 2, FULL, SWAP>(acc, fa1, fb1, fa0, fb0, an, bn, 0, ra, rb, la, lb, kt + 2, bs, wave);
 }
 
 // The main loop.  `lds` must be kLdsBytes of workgroup memory.  AK / BK: the
@@ -458,8 +512,8 @@ __device__ __forceinline__ void kstep(Acc& acc, const typename Frag<T>::type (&a
 // transposed, so lane l of wave w holds, in block (i, j), element e,
 //   C[128 (w / 2) + 16 i + l % 16][128 (w % 2) + 16 j + 4 (l / 16) + e]
 // (four consecutive B rows at one A row; the default layout is stated at the
-// top of this file).  On return no copy is in flight; the caller must barrier
-// before reusing LDS.
+// top of this file).  On return no copy is in flight and the accumulators may
+// be read; the caller must barrier before reusing LDS.
 template <typename T, bool AK = false, bool BK = false, bool SWAP = false, bool BBLK = false>
 __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const Operand& B,
                                               int k_slices, char GRPO_LDS* lds) {
@@ -481,54 +535,48 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
   Reader<T, BK> rb;
   ra.init(lane, (wave >> 1) * 128);
   rb.init(lane, (wave & 1) * 128);
+  char GRPO_LDS* const lb0 = lds + kBRegion;
 
   // slices 0 and 1 (slice 1 reads as zeros when there is none)
   la.issue(0, lds, wave);
-  lb.issue(0, lds + kTileBytes, wave);
-  la.issue(1, lds + kStageBytes, wave);
-  lb.issue(1, lds + kStageBytes + kTileBytes, wave);
+  lb.issue(0, lb0, wave);
+  la.issue(1, lds + kTileBytes, wave);
+  lb.issue(1, lb0 + kTileBytes, wave);
   wait_vmem_but_one_slice();
   __builtin_amdgcn_s_barrier();
   F fa0[kWM], fb0[kWN], fa1[kWM], fb1[kWN];
 #pragma unroll
   for (int f = 0; f < kWM; ++f) ra.read(fa0[f], f, lds, 0);
 #pragma unroll
-  for (int f = 0; f < kWN; ++f) rb.read(fb0[f], f, lds + kTileBytes, 0);
+  for (int f = 0; f < kWN; ++f) rb.read(fb0[f], f, lb0, 0);
 
+  // Slot offsets (workgroup-uniform), rotated per slice: A's slices kt,
+  // kt + 1 and the free slot; B's slices kt and kt + 1.
+  uint32_t ac = 0, an = kTileBytes, af = 2 * kTileBytes, bc = 0, bn = kTileBytes;
   int kt = 0;
-  // Slices wholly inside k in both operands take unchecked copies; the k tail
-  // and the zero slices past it take the checked ones.
+  // Slices whose copies (slice kt + 2) lie wholly inside k in both operands
+  // take unchecked copies; the k tail and the zero slices past it take the
+  // checked ones.
   const int full_a = full_slices<T, AK>(A), full_b = full_slices<T, BK>(B);
   const int full = full_a < full_b ? full_a : full_b;
   for (; kt + 2 < full; ++kt) {
-    char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
-    char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    // k-step 0: read k-step 1's fragments of this slice
-    kstep<T, true, false, false, SWAP>(acc, fa0, fb0, fa1, fb1, cur, 1, ra, rb, la, lb, 0, cur, wave);
-    wait_vmem_all();   // this wave's copies of slice kt + 1 have landed
-    wait_lds_all();
-    __builtin_amdgcn_s_barrier();
-    GRPO_FENCE();
-    // k-step 1: read slice kt + 1's first fragments; copy slice kt + 2 into this
-    // slice's stage
-    kstep<T, true, true, true, SWAP>(acc, fa1, fb1, fa0, fb0, nxt, 0, ra, rb, la, lb, kt + 2, cur, wave);
+    slice_step<T, true, SWAP>(acc, fa0, fb0, fa1, fb1, lds + ac, lb0 + bc, lds + an, lb0 + bn,
+                              lds + af, ra, rb, la, lb, kt, wave);
+    const uint32_t t = ac; ac = an; an = af; af = t;
+    const uint32_t u = bc; bc = bn; bn = u;
   }
   for (; kt + 1 < k_slices; ++kt) {
-    char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
-    char GRPO_LDS* nxt = lds + ((kt + 1) & 1) * kStageBytes;
-    kstep<T, true, false, false, SWAP>(acc, fa0, fb0, fa1, fb1, cur, 1, ra, rb, la, lb, 0, cur, wave);
-    wait_vmem_all();
-    wait_lds_all();
-    __builtin_amdgcn_s_barrier();
-    GRPO_FENCE();
-    // as above, checked (zeros past the end, drained below)
-    kstep<T, true, true, false, SWAP>(acc, fa1, fb1, fa0, fb0, nxt, 0, ra, rb, la, lb, kt + 2, cur, wave);
+    slice_step<T, false, SWAP>(acc, fa0, fb0, fa1, fb1, lds + ac, lb0 + bc, lds + an, lb0 + bn,
+                               lds + af, ra, rb, la, lb, kt, wave);
+    const uint32_t t = ac; ac = an; an = af; af = t;
+    const uint32_t u = bc; bc = bn; bn = u;
   }
-  {
-    char GRPO_LDS* cur = lds + (kt & 1) * kStageBytes;
-    kstep<T, true, false, false, SWAP>(acc, fa0, fb0, fa1, fb1, cur, 1, ra, rb, la, lb, 0, cur, wave);
-    kstep<T, false, false, false, SWAP>(acc, fa1, fb1, fa0, fb0, cur, 0, ra, rb, la, lb, 0, cur, wave);
-  }
+  // the last slice: copies nothing, and its k-step 1 reads nothing
+  kstep<T, true, 0, false, SWAP>(acc, fa0, fb0, fa1, fb1, lds + ac, lb0 + bc, 1, ra, rb, la, lb, 0,
+                                 lds, wave);
+  kstep<T, false, 0, false, SWAP>(acc, fa1, fb1, fa0, fb0, lds + ac, lb0 + bc, 0, ra, rb, la, lb, 0,
+                                  lds, wave);
+  mfma_drain();
   wait_vmem_all();
 }
 
