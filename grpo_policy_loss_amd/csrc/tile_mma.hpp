@@ -326,10 +326,18 @@ __device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC0
 #define GRPO_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 // 32 wait states: more than any MFMA needs before a VALU or memory
-// instruction may read its result registers.
-__device__ __forceinline__ void mfma_drain() {
+// instruction may read its result registers.  Then every accumulator passes
+// through an empty statement that takes it in place in its AGPRs: whatever
+// reads the accumulators afterwards reads values defined after the wait
+// states, so the compiler cannot place a copy of one (to VGPRs, or to
+// scratch) right behind the MFMA that writes it.
+__device__ __forceinline__ void mfma_drain(Acc& acc) {
   GRPO_FENCE();
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+  for (int i = 0; i < kWM; ++i)
+    asm volatile("" : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]),
+                      "+a"(acc[i][4]), "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
   GRPO_FENCE();
 }
 
@@ -441,7 +449,7 @@ __device__ __forceinline__ int full_slices(const Operand& op) {
 }
 
 // Position of the copies within a k-step: after MFMA q with q % 8 == kCopyAt.
-constexpr int kCopyAt = 4;
+constexpr int kCopyAt = 5;
 
 // One 64-byte k-step of the wave's 8 x 8 blocks, in a fixed order.  After
 // block q: for READ and even q < 32, fragment q / 2 of k-step `rs` (a0..a7,
@@ -491,18 +499,19 @@ __device__ __forceinline__ void slice_sync() {
   GRPO_FENCE();
 }
 
-// One slice kt of the main loop (see the top of this file).  as/bs: the slots
-// of slices kt (A and B), an/bn: of slice kt + 1, af: A's free slot.
+// One slice of the main loop (see the top of this file), copying slice `ck`
+// (normally the slice after next).  as/bs: the slots of this slice (A and B),
+// an/bn: of the next, af: A's free slot.
 template <typename T, bool FULL, bool SWAP, typename LA, typename LB, typename RA, typename RB,
           typename F>
 __device__ __forceinline__ void slice_step(Acc& acc, F (&fa0)[kWM], F (&fb0)[kWN], F (&fa1)[kWM],
                                            F (&fb1)[kWN], char GRPO_LDS* as, char GRPO_LDS* bs,
                                            char GRPO_LDS* an, char GRPO_LDS* bn,
                                            char GRPO_LDS* af, const RA& ra, const RB& rb,
-                                           const LA& la, const LB& lb, int kt, int wave) {
-  kstep<T, true, 1, FULL, SWAP>(acc, fa0, fb0, fa1, fb1, as, bs, 1, ra, rb, la, lb, kt + 2, af, wave);
+                                           const LA& la, const LB& lb, int ck, int wave) {
+  kstep<T, true, 1, FULL, SWAP>(acc, fa0, fb0, fa1, fb1, as, bs, 1, ra, rb, la, lb, ck, af, wave);
   slice_sync();
-  kstep<T, true, 2, FULL, SWAP>(acc, fa1, fb1, fa0, fb0, an, bn, 0, ra, rb, la, lb, kt + 2, bs, wave);
+  kstep<T, true, 2, FULL, SWAP>(acc, fa1, fb1, fa0, fb0, an, bn, 0, ra, rb, la, lb, ck, bs, wave);
 }
 
 // The main loop.  `lds` must be kLdsBytes of workgroup memory.  AK / BK: the
@@ -561,13 +570,13 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
   const int full = full_a < full_b ? full_a : full_b;
   for (; kt + 2 < full; ++kt) {
     slice_step<T, true, SWAP>(acc, fa0, fb0, fa1, fb1, lds + ac, lb0 + bc, lds + an, lb0 + bn,
-                              lds + af, ra, rb, la, lb, kt, wave);
+                              lds + af, ra, rb, la, lb, kt + 2, wave);
     const uint32_t t = ac; ac = an; an = af; af = t;
     const uint32_t u = bc; bc = bn; bn = u;
   }
   for (; kt + 1 < k_slices; ++kt) {
     slice_step<T, false, SWAP>(acc, fa0, fb0, fa1, fb1, lds + ac, lb0 + bc, lds + an, lb0 + bn,
-                               lds + af, ra, rb, la, lb, kt, wave);
+                               lds + af, ra, rb, la, lb, kt + 2, wave);
     const uint32_t t = ac; ac = an; an = af; af = t;
     const uint32_t u = bc; bc = bn; bn = u;
   }
@@ -576,7 +585,7 @@ __device__ __forceinline__ void tile_mainloop(Acc& acc, const Operand& A, const 
                                  lds, wave);
   kstep<T, false, 0, false, SWAP>(acc, fa1, fb1, fa0, fb0, lds + ac, lb0 + bc, 0, ra, rb, la, lb, 0,
                                   lds, wave);
-  mfma_drain();
+  mfma_drain(acc);
   wait_vmem_all();
 }
 
