@@ -91,7 +91,7 @@ FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
 // (cpad x vs elements) and the dH GEMM reads W the same way (vs x d elements),
 // and a resource spans less than 2^31 bytes.
 constexpr int64_t kSlabBytesDefault = 2048ll << 20;
-constexpr int64_t kCUs = 256;  // MI355X compute units (one GEMM workgroup each: 128 KB LDS, 4 full-register waves)
+constexpr int64_t kCUs = 256;  // MI355X compute units (one GEMM workgroup each: 160 KB LDS, 4 full-register waves)
 
 struct BwdPlan {
   bool ok;

@@ -80,11 +80,13 @@ typedef enum {
  * per-token split partials of one chunk; the backward one chunk of hidden
  * states (and its transpose), per-token scalars, float32 dH partials of one
  * chunk, 8 bytes per token (active-token list, per-sequence counts) and one
- * dZ slab: the token-major [chunk x V_s] gradient of V_s vocabulary columns of
- * the chunk's logits, in H's dtype (bf16 for fp8), stored once.
- * The backward plans V_s from the workspace_bytes it is passed: the widest
- * multiple of 256 columns (up to the whole vocabulary) that fits, so a
- * caller trades speed for memory by passing any size from
+ * dZ slab: the gradient of V_s vocabulary columns of the chunk's logits, in
+ * H's dtype (bf16 for fp8), stored once, in strips of 256 columns that each
+ * hold every active token's 256 values contiguously.
+ * The backward plans V_s from the workspace_bytes it is passed: a multiple of
+ * 256 columns (up to the whole vocabulary) that fits, the widest one or a
+ * narrower one down to half of it where that wastes fewer waves of
+ * workgroups, so a caller trades speed for memory by passing any size from
  * grpo_workspace_bytes(GRPO_OP_BWD_MIN, ...) (one 256-column slab) up.
  * GRPO_OP_BWD sizes a slab of at most 2 GiB (the whole vocabulary at the
  * usual LM-head shapes and chunks up to 8192 tokens).  The slab's bytes
