@@ -76,8 +76,9 @@ FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
 // Backward workspace: the fixed part (active-token index list, one chunk of
 // gathered hidden states and its transpose, the chunk's per-token coefficient /
 // lse / target id / target dZ entry, nsplit float32 dH partials of the chunk,
-// per-sequence counts), then one dZ slab: the token-major [cpad x vs] bf16 (or
-// f32) gradient of `vs` vocabulary columns of the chunk's logits, stored once.
+// per-sequence counts), then one dZ slab: the bf16 (or f32) gradient of `vs`
+// vocabulary columns of the chunk's logits, stored once as vs / 256 strips of
+// [cpad tokens][256 columns].
 //
 // The slab width comes from the workspace the caller passes: the widest
 // multiple of 256 vocabulary columns (at most the padded vocabulary) that fits

@@ -879,7 +879,8 @@ __global__ void __launch_bounds__(kThreads, 1)
 
 // dW rows v0 + [m0, m0 + 256) (the GEMM's M = vocabulary) by hidden columns
 // [n0, n0 + 256) (N = hidden dimension), K = the chunk's active tokens: A is
-// the token-major dZ slab read K-major, B the transposed hidden-state chunk.
+// one 256-column strip of the dZ slab read K-major, B the transposed
+// hidden-state chunk.
 // The blocks are computed transposed (SWAP), so each lane holds four
 // consecutive hidden columns of one vocabulary row, as dW's rows are laid out.
 template <typename T>

@@ -93,7 +93,7 @@ hipError_t launch_bwd_prep(const T* H, int64_t d, const int32_t* idx, const int3
 template <typename T> struct DzOut { typedef T type; };
 template <> struct DzOut<uint8_t> { typedef __bf16 type; };
 
-// dZ: the token-major [cpad, vs] slab.  T = uint8_t: fp8 operands (w_scale,
+// dZ: the slab, vs / 256 strips of [cpad][256].  T = uint8_t: fp8 operands (w_scale,
 // hs_act as in k_lse_partials), bf16 dZ; other T: both scale pointers unused (null).
 template <typename T>
 hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v0, int vs_valid,
@@ -115,8 +115,8 @@ hipError_t launch_dh_gemm(const T* W, int64_t v0, int vs_valid, const T* dZ, int
                           const int32_t* count, int64_t c0, int C, int cpad, int nsplit, int first,
                           float* dH_acc, hipStream_t s);
 
-// dZ is the token-major [cpad, vs] slab (read K-major); C * vs * sizeof(T) must
-// be < 2^31.
+// dZ is the slab of strips [vs / 256][cpad][256] (each strip read K-major);
+// C * vs * sizeof(T) must be < 2^31.
 template <typename T>
 hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZ, int vs, int64_t d, int64_t v0,
                           int vs_valid, const int32_t* count, int64_t c0, int C, float* dW,
