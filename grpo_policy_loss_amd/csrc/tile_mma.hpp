@@ -23,13 +23,13 @@
 //    8 copies and 16 fragment reads per wave, and every copy moves whole
 //    128-byte lines.  (With two slots for each operand all 16 copies of a
 //    slice fall into k-step 1, which then has twice the LDS and buffer-unit
-//    traffic of k-step 0; the even spread measured 3 to 6 % less kernel time.
+//    traffic of k-step 0; the even spread measured 2 to 6 % less kernel time.
 //    Four stages of one 64-byte k-step each spread the copies as well, but
-//    fetch half lines of K-contiguous rows and were 5 % slower there.)
+//    fetch half lines of K-contiguous rows and were 5 to 6.5 % slower there.)
 //  * Every instruction of a k-step is placed by hand (scheduling fences): a
 //    fragment read after each even MFMA of its first half and a copy after
-//    every eighth MFMA.  Left to itself the compiler clusters the copies (each
-//    needs its own M0 write) and the matrix core idles.
+//    MFMA q for q mod 8 = kCopyAt.  Left to itself the compiler clusters the
+//    copies (each needs its own M0 write) and the matrix core idles.
 //  * With one wave per SIMD, whatever sits between two MFMAs must issue within
 //    the 16 cycles of the first one.  A copy of a slice that lies wholly inside
 //    k therefore costs no vector instruction: each lane's row-and-chunk offset
@@ -40,7 +40,8 @@
 //  * Slice barrier after the first k-step: every wave then holds the slice's
 //    last fragments, so its B slot is free for the copy of slice kt + 2, and
 //    (after each wave's own vmcnt wait) slice kt + 1 is visible.  A copy of
-//    A is waited for three k-steps after it is issued, one of B two.
+//    A has two to three k-steps to land before it is waited for, one of B
+//    one to two.
 //  * Out-of-range rows and k-columns read as zero: each operand is addressed
 //    through a buffer resource whose range ends at its last valid row, and an
 //    invalid row or column gets an offset past that range.  Tails in M, N
