@@ -59,6 +59,22 @@ def test_tile_gemm_matches_exact_product(dtype, M, N, K):
     assert err <= 1e-5 * np.abs(want).max() + 1e-5, err
 
 
+# K = 32 .. 832 bf16 elements: 1 to 13 slices of 128 bytes, whole or ending in a
+# half slice, so the main loop ends in every phase of its three A slots and two B
+# slots, with and without a k tail; M and N ragged.
+@pytest.mark.parametrize("K", [32, 64, 96, 160, 192, 224, 288, 352, 416, 480, 544, 608, 704, 832])
+def test_tile_gemm_every_slot_phase_and_k_tail(K):
+    _need_gpu()
+    g = torch.Generator(device="cuda").manual_seed(1000 + K)
+    A = torch.randn(300, K, device="cuda", generator=g).to(torch.bfloat16)
+    B = torch.randn(270, K, device="cuda", generator=g).to(torch.bfloat16)
+    C = gp.grpo_gemm_nt(A, B)
+    torch.cuda.synchronize()
+    want = to64(A) @ to64(B).T
+    err = np.abs(to64(C) - want).max()
+    assert err <= 1e-5 * np.abs(want).max() + 1e-5, (K, err)
+
+
 # ----------------------------------------------------------------------------- advantages
 def test_advantages_match_oracle_and_degenerate_groups():
     _need_gpu()
