@@ -567,6 +567,14 @@ def main():
                 "launches": dom_launches,
                 "avg_launch_ms": round(dom_ms / dom_launches, 4)}
 
+    # every GEMM kernel's algorithmic flops over its own measured time
+    kernels_frac = {}
+    for name, (_, ms) in kernels.items():
+        fl = alg_flops(name, d, V, N, N_act)
+        if fl is not None and ms > 0:
+            pk = PEAK_FLOPS["fp8"] if (args.fp8 and name == "lse_partials") else PEAK_FLOPS[w.dtype]
+            kernels_frac[name] = round(fl * args.steps / (ms * 1e-3) / pk, 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host ...")
@@ -601,6 +609,7 @@ def main():
                                 "total": round(total_hbm / 1e9, 3)},
         "full_fp32_logits_gb": round(N * V * 4 / 1e9, 2),
         "kernels_ms_per_step": {k: round(v[1] / args.steps, 3) for k, v in kernels.items()},
+        "kernels_mfma_frac": kernels_frac,
         "instrumented_ms_per_step": round(t_inst * 1e3 / args.steps, 3),
         "roofline": roof,
         "cpu_baseline": cpu,
