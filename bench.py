@@ -308,10 +308,14 @@ def alg_flops(kind, d, V, N, N_act):
     return None
 
 
-def cpu_baseline(w, inp, seconds=15.0, opts=None):
+def cpu_baseline(w, inp, seconds=15.0, opts=None, gpu=None):
     """The float64 oracle, as it stands, on a bounded sample: the first n
     flattened tokens of the batch, run through reference log-probs, loss forward
-    and loss backward, on all host threads BLAS uses."""
+    and loss backward, on all host threads BLAS uses.
+
+    With `gpu` (the last timed step's outputs: ref, lp, lse, kl, dH), the
+    sample's outputs are also compared with the GPU's for the same tokens; see
+    sample_parity."""
     import numpy as np
     import threadpoolctl
 
@@ -327,14 +331,17 @@ def cpu_baseline(w, inp, seconds=15.0, opts=None):
     # per-token advantages, so a sample may end inside a sequence (seq_len 1 below)
     adv_tok = np.repeat(oracle.group_advantages(r, w.G), w.L)
 
+    last = {}
+
     def run(n):
         Hs = H[:n].double().numpy()
         Hr = H_ref[:n].double().numpy()
         ys, ms, adv = y[:n], mask[:n], adv_tok[:n]
         t0 = time.perf_counter()
         ref, _ = oracle.token_logprobs(Hr, W64, ys, opts=opts)
-        oracle.loss_forward(Hs, W64, ys, ms, adv, ref, 1, 0.04, opts=opts)
-        oracle.loss_backward(Hs, W64, ys, ms, adv, ref, 1, 0.04, opts=opts)
+        fwd = oracle.loss_forward(Hs, W64, ys, ms, adv, ref, 1, 0.04, opts=opts)
+        dH, _ = oracle.loss_backward(Hs, W64, ys, ms, adv, ref, 1, 0.04, opts=opts)
+        last.update(n=n, ref=ref, lp=fwd["lp"], lse=fwd["lse"], kl=fwd["kl"], dH=dH)
         return time.perf_counter() - t0
 
     # size the sample to about `seconds` of work: small runs carry fixed costs, so
@@ -349,11 +356,37 @@ def cpu_baseline(w, inp, seconds=15.0, opts=None):
     n2, t2 = n, t
     info = threadpoolctl.threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] or [1])
-    return {"value": n2 / t2, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    parity = sample_parity(last, gpu, mask, opts) if gpu is not None else None
+    return parity, {"value": n2 / t2, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "cpu_model": cpu_model(),
             "sample": f"first {n2} flattened tokens of the batch (ref + fwd + bwd, float64 "
                       f"NumPy, full V={w.V}, d={w.d}); {t2:.1f} s on "
                       f"{len(os.sched_getaffinity(0))} visible host CPUs"}
+
+
+def sample_parity(orc, gpu, mask, opts):
+    """Errors of the GPU's outputs on the oracle's sample (the first n tokens).
+    ref_lp, lp, lse and kl of a token depend only on its own row, so they are
+    compared directly.  The GPU's dH rows carry the batch's 1 / sum(mask) where
+    the sample's carry its own; rescaled by the ratio of the two they are
+    compared by cosine and max |diff| / max |oracle|.  (Under the per-sequence
+    mean the sample's weights differ token by token, so dH is left out.)"""
+    import numpy as np
+    n = orc["n"]
+    out = {"tokens": n}
+    for k in ("ref", "lp", "lse", "kl"):
+        g = gpu[k][:n].double().cpu().numpy()
+        out[f"max_abs_{'ref_lp' if k == 'ref' else k}"] = float(np.abs(g - orc[k]).max())
+    if not (opts or {}).get("aggregation"):
+        m_all = max(float(mask.sum()), 1.0)
+        m_smp = max(float(mask[:n].sum()), 1.0)
+        g = gpu["dH"][:n].double().cpu().numpy() * (m_all / m_smp)
+        o = orc["dH"]
+        den = float(np.linalg.norm(g) * np.linalg.norm(o))
+        out["dH_cosine"] = float((g * o).sum() / den) if den > 0 else None
+        top = float(np.abs(o).max())
+        out["dH_max_abs_rel"] = float(np.abs(g - o).max() / top) if top > 0 else None
+    return out
 
 
 def main():
@@ -480,6 +513,8 @@ def main():
             ev[3].record(stream)
         return loss
 
+    last_out = {}   # the last bf16/f32 step's outputs, for the sampled parity check
+
     def step(ev=None):
         if args.fp8:
             return step_fp8(ev)
@@ -501,6 +536,7 @@ def main():
                          opts=xopts)
         if ev is not None:
             ev[3].record(stream)
+        last_out.update(ref=ref, lp=lp, lse=lse, kl=kl, dH=dH)
         return loss
 
     if args.traffic_probe:
@@ -575,10 +611,11 @@ def main():
             pk = PEAK_FLOPS["fp8"] if (args.fp8 and name == "lse_partials") else PEAK_FLOPS[w.dtype]
             kernels_frac[name] = round(fl * args.steps / (ms * 1e-3) / pk, 4)
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
         log("[bench] timing the float64 oracle on the host ...")
-        cpu = cpu_baseline(w, inp, args.cpu_seconds, xopts)
+        parity, cpu = cpu_baseline(w, inp, args.cpu_seconds, xopts,
+                                   None if args.fp8 else last_out)
         log(f"[bench] oracle {cpu['value']:.2f} tokens/s")
 
     out = {
@@ -613,6 +650,7 @@ def main():
         "instrumented_ms_per_step": round(t_inst * 1e3 / args.steps, 3),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "parity": parity,
     }
     print(json.dumps(out), flush=True)
 

@@ -128,3 +128,38 @@ def test_summarize_counters_derives_mfma_busy_and_clock(tmp_path, monkeypatch):
     text = open(tmp_path / "counters_wl.md").read()
     row = [l for l in text.splitlines() if l.startswith("| `k_lse_partials` | 0.0010")][0]
     assert "66.7%" in row and "1.80" in row and "0.250" in row
+
+
+def test_sampled_parity_rescales_the_batch_gradient():
+    """The bench's parity record compares the GPU's whole-batch outputs with the
+    oracle's run on the first tokens alone.  Fed the oracle's own whole-batch
+    outputs in place of the GPU's, it must report agreement to rounding: a
+    missing or wrong 1/sum(mask) rescale of dH would not."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import workloads
+
+    w = workloads.BY_NAME["tiny-f32"]
+    inp = workloads.generate(w, seed=3)
+    H = inp["H"].double().numpy()
+    Wt = inp["W"].double().numpy()
+    y = inp["y"].numpy().astype(np.int64)
+    mask = inp["mask"].numpy()
+    adv = oracle.group_advantages(inp["rewards"].numpy(), w.G)
+    ref, _ = oracle.token_logprobs(inp["H_ref"].double().numpy(), Wt, y)
+    fwd = oracle.loss_forward(H, Wt, y, mask, adv, ref, w.L, workloads.BETA)
+    dH, _ = oracle.loss_backward(H, Wt, y, mask, adv, ref, w.L, workloads.BETA, want_dW=False)
+    full = {k: torch.from_numpy(np.asarray(v)) for k, v in
+            dict(ref=ref, lp=fwd["lp"], lse=fwd["lse"], kl=fwd["kl"], dH=dH).items()}
+    parity, cpu = bench.cpu_baseline(w, inp, seconds=0.2, gpu=full)
+    assert cpu["kind"] == "oracle" and parity["tokens"] >= 16
+    for k in ("max_abs_ref_lp", "max_abs_lp", "max_abs_lse", "max_abs_kl"):
+        assert parity[k] < 1e-9, (k, parity[k])
+    assert parity["dH_cosine"] > 1 - 1e-12
+    assert parity["dH_max_abs_rel"] < 1e-9
+    # a dH off by a factor of two is reported as such
+    full["dH"] = full["dH"] * 2.0
+    bad, _ = bench.cpu_baseline(w, inp, seconds=0.2, gpu=full)
+    assert bad["dH_max_abs_rel"] > 0.5
