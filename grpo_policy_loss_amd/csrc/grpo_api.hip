@@ -85,13 +85,16 @@ FwdPlan plan_fwd(int64_t N, int64_t V, int64_t chunk) {
 // after the fixed part, then, among widths down to half of that, the one with
 // the fewest modelled GEMM waves.  grpo_workspace_bytes(GRPO_OP_BWD) sizes the
 // workspace for a slab of at most kSlabBytesDefault; GRPO_OP_BWD_MIN for one
-// 256-column slab.  Wider slabs mean fewer read-modify-write passes over the dH
-// partials: at the Qwen2.5-1.5B LM-head shape one full-vocabulary slab ran the
-// backward about 10 % faster than 256 MiB slabs.  Two hardware bounds cap the
-// width: the dW GEMM reads the slab K-major through one buffer resource
-// (cpad x vs elements) and the dH GEMM reads W the same way (vs x d elements),
-// and a resource spans less than 2^31 bytes.
-constexpr int64_t kSlabBytesDefault = 2048ll << 20;
+// 256-column slab.  Narrow slabs mean more read-modify-write passes over the dH
+// partials: at the Qwen2.5-1.5B LM-head shape one whole-vocabulary slab
+// (1.16 GiB) ran the backward 2 % faster than two, and 512 MiB slabs 6 %
+// slower.  Past that the width stops mattering: at Llama-3.1-8B and gpt-oss-20b
+// with 8192-token chunks, 1.25 GiB slabs ran within 0.5 % of 2 GiB ones (one
+// and two slabs per chunk) and keep 0.8 GB less workspace.  Two hardware
+// bounds cap the width: the dW GEMM reads the slab K-major through one buffer
+// resource (cpad x vs elements) and the dH GEMM reads W the same way
+// (vs x d elements), and a resource spans less than 2^31 bytes.
+constexpr int64_t kSlabBytesDefault = 1280ll << 20;
 constexpr int64_t kCUs = 256;  // MI355X compute units (one GEMM workgroup each: 160 KB LDS, 4 full-register waves)
 
 struct BwdPlan {

@@ -79,12 +79,30 @@ __device__ __forceinline__ void group_coords(int p, int tm, int tn, int& mt, int
 // Hardware dispatches workgroup b to XCD b % 8.  Remap so that XCD x
 // receives a contiguous range of logical tile ids, then order them in
 // groups of 4 M-tiles: the ~32 workgroups resident on one XCD share 4
-// A-panels and ~8 B-panels.
+// A-panels and ~8 B-panels.  (The dH GEMM's split launches use this form.)
 __device__ __forceinline__ void tile_coords(int bid, int nblocks, int tm, int tn, int& mt,
                                             int& nt) {
   const int xcd = bid & 7, slot = bid >> 3;
   const int q = nblocks >> 3, r = nblocks & 7;
   group_coords<4>(xcd * q + (xcd < r ? xcd : r) + slot, tm, tn, mt, nt);
+}
+
+// The same raster in whole blocks of 32 tiles, one wave of an XCD's 32 CUs:
+// XCD x takes a contiguous range of blocks, so the tiles resident on it at
+// one time are always one aligned block, which (with tn a multiple of 8) lies
+// inside one group: 4 A-panels and 8 B-panels.  A range that starts part-way
+// into a block would straddle two groups for some of its waves.  The grid is
+// xcd_grid(tm * tn) workgroups; false for the ones past this XCD's range.
+__device__ __forceinline__ bool tile_coords_blk(int bid, int tm, int tn, int& mt, int& nt) {
+  const int tiles = tm * tn;
+  const int xcd = bid & 7, slot = bid >> 3;
+  const int nb = (tiles + 31) >> 5;
+  const int q = nb >> 3, r = nb & 7;
+  const int nmine = (q + (xcd < r ? 1 : 0)) << 5;
+  const int p = ((xcd * q + (xcd < r ? xcd : r)) << 5) + slot;
+  if (slot >= nmine || p >= tiles) return false;
+  group_coords<4>(p, tm, tn, mt, nt);
+  return true;
 }
 
 template <typename T>
@@ -332,7 +350,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
   int mt, nt;
-  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  if (!tile_coords_blk(blockIdx.x, tm, tn, mt, nt)) return;
   const int64_t m0 = (int64_t)mt * kBM;  // first vocab row
   const int n0 = nt * kBN;               // first token (chunk-local)
   const uint32_t rowb = (uint32_t)(d * (int64_t)sizeof(T));
@@ -687,7 +705,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   int n_act = count[0] - (int)c0;
   n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
   int mt, nt;
-  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  if (!tile_coords_blk(blockIdx.x, tm, tn, mt, nt)) return;
   const int n0 = nt * kBN;
   if (n0 >= n_act) return;
   const int m0 = mt * kBM;
@@ -894,7 +912,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
   if (n_act <= 0) return;
   int mt, nt;
-  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  if (!tile_coords_blk(blockIdx.x, tm, tn, mt, nt)) return;
   const int m0 = mt * kBM;                  // first vocabulary row of the slab
   const int64_t n0 = (int64_t)nt * kBN;     // first hidden column
   const uint32_t kb = (uint32_t)(((int64_t)n_act * (int64_t)sizeof(T) + 15) & ~(int64_t)15);
@@ -945,7 +963,7 @@ __global__ void __launch_bounds__(kThreads, 1)
   __shared__ __attribute__((aligned(1024))) char smem[kLdsBytes];
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
   int mt, nt;
-  tile_coords(blockIdx.x, gridDim.x, tm, tn, mt, nt);
+  if (!tile_coords_blk(blockIdx.x, tm, tn, mt, nt)) return;
   const int64_t m0 = (int64_t)mt * kBM, n0 = (int64_t)nt * kBN;
   const uint32_t rowb = (uint32_t)(K * (int64_t)sizeof(T));
   const Operand Ao{(const char*)(A + m0 * K), rowb, (int)((M - m0) < kBM ? (M - m0) : kBM), rowb};
@@ -1084,6 +1102,9 @@ __global__ void __launch_bounds__(256)
 }
 
 inline int cdiv(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+// Workgroups for tile_coords_blk: whole 32-tile blocks, the same number on each
+// of the 8 XCDs (ceil(tiles / 256) waves, as for tiles workgroups).
+inline int xcd_grid(int tiles) { return 256 * cdiv(cdiv(tiles, 32), 8); }
 
 }  // namespace
 
@@ -1103,10 +1124,10 @@ hipError_t launch_lse_partials(const T* W, const T* H, const int32_t* y, int64_t
   ScopedKernelTimer timer_(KK_LSE_PARTIALS, s);
   const int tm = cdiv(V, kBM), tn = cdiv(n_tok, kBN);
   if (xf.softcap)
-    hipLaunchKernelGGL((k_lse_partials<T, true>), dim3(tm * tn), dim3(kThreads), 0, s, W, H, y, V,
+    hipLaunchKernelGGL((k_lse_partials<T, true>), dim3(xcd_grid(tm * tn)), dim3(kThreads), 0, s, W, H, y, V,
                        d, n_tok, cpad, tm, tn, xf, w_scale, h_scale, part_m, part_s, zy);
   else
-    hipLaunchKernelGGL((k_lse_partials<T, false>), dim3(tm * tn), dim3(kThreads), 0, s, W, H, y,
+    hipLaunchKernelGGL((k_lse_partials<T, false>), dim3(xcd_grid(tm * tn)), dim3(kThreads), 0, s, W, H, y,
                        V, d, n_tok, cpad, tm, tn, xf, w_scale, h_scale, part_m, part_s, zy);
   return hipGetLastError();
 }
@@ -1180,11 +1201,11 @@ hipError_t launch_dz(const T* W, const T* H_act, int64_t d, int64_t V, int64_t v
   (void)V;
   const int tm = cdiv(vs_valid, kBM), tn = cdiv(C, kBN);
   if (xf.softcap)
-    hipLaunchKernelGGL((k_dz<T, true>), dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0,
+    hipLaunchKernelGGL((k_dz<T, true>), dim3(xcd_grid(tm * tn)), dim3(kThreads), 0, s, W, H_act, d, v0,
                        vs_valid, vs, count, c0, C, cpad, tm, tn, xf, w_scale, hs_act, coef, lse_c,
                        y_c, tgt_c, dZ);
   else
-    hipLaunchKernelGGL((k_dz<T, false>), dim3(tm * tn), dim3(kThreads), 0, s, W, H_act, d, v0,
+    hipLaunchKernelGGL((k_dz<T, false>), dim3(xcd_grid(tm * tn)), dim3(kThreads), 0, s, W, H_act, d, v0,
                        vs_valid, vs, count, c0, C, cpad, tm, tn, xf, w_scale, hs_act, coef, lse_c,
                        y_c, tgt_c, dZ);
   return hipGetLastError();
@@ -1234,7 +1255,7 @@ hipError_t launch_dw_gemm(const T* HT, int cpad, const T* dZ, int vs, int64_t d,
                           hipStream_t s) {
   ScopedKernelTimer timer_(KK_DW_GEMM, s);
   const int tm = cdiv(vs_valid, kBM), tn = cdiv(d, kBN);
-  hipLaunchKernelGGL(k_dw_gemm<T>, dim3(tm * tn), dim3(kThreads), 0, s, HT, cpad, dZ, vs, d, v0,
+  hipLaunchKernelGGL(k_dw_gemm<T>, dim3(xcd_grid(tm * tn)), dim3(kThreads), 0, s, HT, cpad, dZ, vs, d, v0,
                      vs_valid, count, c0, C, tm, tn, dW);
   return hipGetLastError();
 }
@@ -1267,7 +1288,7 @@ hipError_t launch_gemm_nt(const T* A, const T* B, int64_t M, int64_t N, int64_t 
                           hipStream_t s) {
   ScopedKernelTimer timer_(KK_GEMM_NT, s);
   const int tm = cdiv(M, kBM), tn = cdiv(N, kBN);
-  hipLaunchKernelGGL(k_gemm_nt<T>, dim3(tm * tn), dim3(kThreads), 0, s, A, B, M, N, K, tm, tn, C);
+  hipLaunchKernelGGL(k_gemm_nt<T>, dim3(xcd_grid(tm * tn)), dim3(kThreads), 0, s, A, B, M, N, K, tm, tn, C);
   return hipGetLastError();
 }
 

@@ -88,8 +88,9 @@ typedef enum {
  * narrower one down to half of it where that wastes fewer waves of
  * workgroups, so a caller trades speed for memory by passing any size from
  * grpo_workspace_bytes(GRPO_OP_BWD_MIN, ...) (one 256-column slab) up.
- * GRPO_OP_BWD sizes a slab of at most 2 GiB (the whole vocabulary at the
- * usual LM-head shapes and chunks up to 8192 tokens).  The slab's bytes
+ * GRPO_OP_BWD sizes a slab of at most 1.25 GiB (the whole vocabulary of a
+ * 4096-token chunk at the usual LM-head shapes; a wider slab is not faster).
+ * The slab's bytes
  * (chunk x V_s) and V_s x d elements of W are each read through one buffer
  * resource, so V_s is also capped below 2^31 bytes for both.
  */

@@ -64,13 +64,16 @@ def test_workspace_bytes_bounded_and_independent_of_N_times_V(op):
         ws2 = L.grpo_workspace_bytes(op, 2 * N, d, V, 1, chunk)
         assert ws2 - ws <= 8 * N + 1024
     if op == 2:
-        # the whole vocabulary in one slab at this shape (8192 x 128256 x 2 B < 2 GiB)
-        assert ws >= chunk * V * 2
+        # the default slab budget, 1.25 GiB: 81920 of the 128256 vocabulary columns
+        # of an 8192-token chunk (two slabs per chunk)
+        least = L.grpo_workspace_bytes(3, N, d, V, 1, chunk)
+        assert ws - least == chunk * (81920 - 256) * 2
 
 
 def test_backward_workspace_plans_the_slab_from_its_size():
     # Qwen2.5-1.5B shape, bf16: the default holds the whole vocabulary in one slab
-    # (4096 x 151936 x 2 B = 1.24 GB); the minimum holds one 256-column slab
+    # (4096 x 151936 x 2 B = 1.16 GiB, within the 1.25 GiB budget); the minimum
+    # holds one 256-column slab
     N, d, V, chunk = 32768, 1536, 151936, 4096
     full = L.grpo_workspace_bytes(2, N, d, V, 1, chunk)
     least = L.grpo_workspace_bytes(3, N, d, V, 1, chunk)
