@@ -76,31 +76,28 @@ __device__ __forceinline__ void group_coords(int p, int tm, int tn, int& mt, int
   nt = rem / gm;
 }
 
-// Hardware dispatches workgroup b to XCD b % 8.  Remap so that XCD x
-// receives a contiguous range of logical tile ids, then order them in
-// groups of 4 M-tiles: the ~32 workgroups resident on one XCD share 4
-// A-panels and ~8 B-panels.  (The dH GEMM's split launches use this form.)
-__device__ __forceinline__ void tile_coords(int bid, int nblocks, int tm, int tn, int& mt,
-                                            int& nt) {
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int q = nblocks >> 3, r = nblocks & 7;
-  group_coords<4>(xcd * q + (xcd < r ? xcd : r) + slot, tm, tn, mt, nt);
-}
-
-// The same raster in whole blocks of 32 tiles, one wave of an XCD's 32 CUs:
+// Hardware dispatches workgroup b to XCD b % 8.  Deal the logical tile ids
+// [0, tiles) to the XCDs in whole blocks of 32, one wave of an XCD's 32 CUs:
 // XCD x takes a contiguous range of blocks, so the tiles resident on it at
-// one time are always one aligned block, which (with tn a multiple of 8) lies
-// inside one group: 4 A-panels and 8 B-panels.  A range that starts part-way
-// into a block would straddle two groups for some of its waves.  The grid is
-// xcd_grid(tm * tn) workgroups; false for the ones past this XCD's range.
-__device__ __forceinline__ bool tile_coords_blk(int bid, int tm, int tn, int& mt, int& nt) {
-  const int tiles = tm * tn;
+// one time are always one aligned block of the raster.  (A range starting
+// part-way into a block would straddle two groups of the raster for some of
+// its waves.)  The grid is xcd_grid(tiles) workgroups; false for those past
+// this XCD's range.
+__device__ __forceinline__ bool xcd_tile(int bid, int tiles, int& p) {
   const int xcd = bid & 7, slot = bid >> 3;
   const int nb = (tiles + 31) >> 5;
   const int q = nb >> 3, r = nb & 7;
   const int nmine = (q + (xcd < r ? 1 : 0)) << 5;
-  const int p = ((xcd * q + (xcd < r ? xcd : r)) << 5) + slot;
-  if (slot >= nmine || p >= tiles) return false;
+  p = ((xcd * q + (xcd < r ? xcd : r)) << 5) + slot;
+  return slot < nmine && p < tiles;
+}
+
+// Tile (mt, nt) of workgroup bid in a tm x tn grid: ids in groups of 4
+// M-tiles, so one 32-tile block (with tn a multiple of 8) lies inside one
+// group and its workgroups share 4 A-panels and 8 B-panels in the XCD's L2.
+__device__ __forceinline__ bool tile_coords_blk(int bid, int tm, int tn, int& mt, int& nt) {
+  int p;
+  if (!xcd_tile(bid, tm * tn, p)) return false;
   group_coords<4>(p, tm, tn, mt, nt);
   return true;
 }
@@ -862,11 +859,14 @@ __global__ void __launch_bounds__(kThreads, 1)
   char GRPO_LDS* lds = (char GRPO_LDS*)smem;
   int n_act = count[0] - (int)c0;
   n_act = n_act < 0 ? 0 : (n_act > C ? C : n_act);
-  // split index outermost, then the XCD-aware raster inside one split
+  // split index outermost, then the raster inside one split; the XCDs take
+  // whole blocks of the flattened order, so each holds few splits at a time
   const int per_split = tm * tn;
-  const int sp = blockIdx.x / per_split;
+  int p;
+  if (!xcd_tile(blockIdx.x, per_split * nsplit, p)) return;
+  const int sp = p / per_split;
   int mt, nt;
-  tile_coords(blockIdx.x - sp * per_split, per_split, tm, tn, mt, nt);
+  group_coords<4>(p - sp * per_split, tm, tn, mt, nt);
   const int n0 = nt * kBN;
   if (n0 >= n_act) return;
   const int64_t m0 = (int64_t)mt * kBM;
@@ -1244,7 +1244,7 @@ hipError_t launch_dh_gemm(const T* W, int64_t v0, int vs_valid, const T* dZ, int
   const int tm = cdiv(d, kBM), tn = cdiv(C, kBN);
   // K range per split: a whole number of the slab's 256-column strips
   const int kchunk = (int)(((int64_t)cdiv(vs_valid, nsplit) + 255) / 256 * 256);
-  hipLaunchKernelGGL(k_dh_gemm<T>, dim3(tm * tn * nsplit), dim3(kThreads), 0, s, W, v0, vs_valid,
+  hipLaunchKernelGGL(k_dh_gemm<T>, dim3(xcd_grid(tm * tn * nsplit)), dim3(kThreads), 0, s, W, v0, vs_valid,
                      dZ, vs, d, count, c0, C, cpad, tm, tn, nsplit, kchunk, first, dH_acc);
   return hipGetLastError();
 }
