@@ -90,9 +90,8 @@ typedef enum {
  * grpo_workspace_bytes(GRPO_OP_BWD_MIN, ...) (one 256-column slab) up.
  * GRPO_OP_BWD sizes a slab of at most 1.25 GiB (the whole vocabulary of a
  * 4096-token chunk at the usual LM-head shapes; a wider slab is not faster).
- * The slab's bytes
- * (chunk x V_s) and V_s x d elements of W are each read through one buffer
- * resource, so V_s is also capped below 2^31 bytes for both.
+ * The slab's bytes (chunk x V_s) and V_s x d elements of W are each read
+ * through one buffer resource, so V_s is also capped below 2^31 bytes for both.
  */
 size_t grpo_workspace_bytes(int op, int64_t N, int64_t d, int64_t V, int dtype, int64_t chunk);
 
