@@ -308,6 +308,17 @@ def alg_flops(kind, d, V, N, N_act):
     return None
 
 
+def slab_columns(w, dt):
+    """Vocabulary columns of the backward's dZ slab under the default workspace:
+    the two workspace sizes differ by exactly the slab beyond 256 columns."""
+    import grpo_policy_loss_amd as gp
+    full = gp.grpo_workspace_bytes(gp.GRPO_OP_BWD, w.N, w.d, w.V, dt, w.chunk)
+    least = gp.grpo_workspace_bytes(gp.GRPO_OP_BWD_MIN, w.N, w.d, w.V, dt, w.chunk)
+    cpad = -(-min(w.chunk, w.N) // 256) * 256
+    es = 4 if dt == gp.GRPO_F32 else 2        # the slab is bf16 for bf16 and fp8 inputs
+    return 256 + (full - least) // (cpad * es)
+
+
 def cpu_baseline(w, inp, seconds=15.0, opts=None, gpu=None):
     """The float64 oracle, as it stands, on a bounded sample: the first n
     flattened tokens of the batch, run through reference log-probs, loss forward
@@ -645,6 +656,8 @@ def main():
                                 "free_after": round(free_after / 1e9, 3),
                                 "total": round(total_hbm / 1e9, 3)},
         "full_fp32_logits_gb": round(N * V * 4 / 1e9, 2),
+        "workspace_gb": {"fwd": round(ws_f.numel() / 1e9, 3), "bwd": round(ws_b.numel() / 1e9, 3),
+                         "dz_slab_columns": slab_columns(w, dt)},
         "kernels_ms_per_step": {k: round(v[1] / args.steps, 3) for k, v in kernels.items()},
         "kernels_mfma_frac": kernels_frac,
         "instrumented_ms_per_step": round(t_inst * 1e3 / args.steps, 3),

@@ -163,3 +163,14 @@ def test_sampled_parity_rescales_the_batch_gradient():
     full["dH"] = full["dH"] * 2.0
     bad, _ = bench.cpu_baseline(w, inp, seconds=0.2, gpu=full)
     assert bad["dH_max_abs_rel"] > 0.5
+
+
+def test_slab_columns_of_the_default_workspace():
+    import workloads
+    import grpo_policy_loss_amd as gp
+    w = workloads.BY_NAME["llama3.1-8b-20k-bf16"]
+    assert bench.slab_columns(w, gp.GRPO_BF16) == 81920       # the 1.25 GiB budget
+    w = workloads.BY_NAME["qwen2.5-1.5b-bf16"]
+    assert bench.slab_columns(w, gp.GRPO_BF16) == 152064      # the whole padded vocabulary
+    w = workloads.BY_NAME["tiny-f32"]
+    assert bench.slab_columns(w, gp.GRPO_F32) == 1024
