@@ -34,3 +34,4 @@ from ._lib import (  # noqa: F401
     grpo_workspace_bytes,
     lib,
 )
+from .autograd import grpo_loss  # noqa: F401,E402

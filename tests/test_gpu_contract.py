@@ -9,7 +9,9 @@ binding would otherwise stand in between:
     on the loss and every lp;
   * a NaN reward stays inside its own group of advantages;
   * an out-of-range target (y < 0 or y >= V) gives lp = NaN at that token
-    and leaves every other token's lp, lse and ref bitwise unchanged."""
+    and leaves every other token's lp, lse and ref bitwise unchanged;
+  * the torch.autograd wrapper gives bitwise the direct calls' outputs and
+    gradients."""
 import ctypes
 
 import numpy as np
@@ -127,3 +129,33 @@ def test_out_of_range_target_gives_nan_lp_only_there(dtype):
     assert torch.all(torch.isnan(lp_b[bad])) and torch.all(torch.isnan(ref_b[bad]))
     assert torch.equal(lp_b[good], lp[good]) and torch.equal(ref_b[good], ref[good])
     assert torch.equal(lse_b, lse)           # the log-sum-exp does not involve the target
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_autograd_wrapper_gives_the_direct_calls_gradients(dtype):
+    """grpo_loss under torch.autograd: the loss, lp and kl of grpo_loss_fwd, and
+    (for an upstream gradient of 2) the dH and dW of grpo_loss_bwd with grad_loss 2,
+    bitwise; no gradient flows to the other arguments."""
+    _need_gpu()
+    w = workloads.WORKLOADS[0].scaled(name="ag", prompts=2, G=3, L=90, d=200, V=700,
+                                      dtype=dtype, chunk=256, len_lo=20, len_hi=90)
+    inp = workloads.generate(w, seed=13, device="cuda")
+    adv = gp.grpo_advantages(inp["rewards"], w.G, EPS)
+    ref = gp.grpo_ref_logprobs(inp["H_ref"], inp["W"], inp["y"], w.chunk)
+    H = inp["H"].clone().requires_grad_(True)
+    W = inp["W"].clone().requires_grad_(True)
+    loss, lp, kl = gp.grpo_loss(H, W, inp["y"], inp["mask"], adv, ref, w.B, w.L, BETA,
+                                w.chunk)
+    assert loss.shape == () and not lp.requires_grad and not kl.requires_grad
+    (2.0 * loss).backward()
+    loss2, lp2, kl2, lse2 = gp.grpo_loss_fwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv,
+                                             ref, w.B, w.L, BETA, w.chunk)
+    dH2, dW2 = gp.grpo_loss_bwd(inp["H"], inp["W"], inp["y"], inp["mask"], adv, ref, lp2,
+                                lse2, w.B, w.L, BETA, 2.0, w.chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(loss.detach(), loss2.reshape(()))
+    assert torch.equal(lp, lp2) and torch.equal(kl, kl2)
+    assert H.grad.dtype == H.dtype and W.grad.dtype == W.dtype
+    assert torch.equal(H.grad, dH2)
+    assert torch.equal(W.grad, dW2.to(W.dtype))
+    assert adv.grad is None and ref.grad is None
